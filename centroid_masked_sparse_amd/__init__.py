@@ -1,0 +1,241 @@
+"""Centroid-masked sparse LM head for MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``include/ce.h`` (``libce.so``).  It
+only marshals arguments: torch supplies device memory and streams, and every
+step of the computation runs in the library's HIP kernels.  If the library is
+missing, every call raises; there is no fallback implementation.
+
+The head is the one of Gemma4MTPMaskedEmbedder in the vLLM compare view
+"[Spec Decode] Add Gemma4 MTP speculative decoding with centroids masking"
+(diff of gemma4_mtp.py): ``top_tokens`` is get_top_tokens, ``masked_logits``
+is forward, and ``score_centroids`` / ``topk`` expose the first two steps of
+_select_and_score.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _ffi
+from ._ffi import (CE_BF16, CE_F32, CE_OP_MASKED_LOGITS, CE_OP_SCORE, CE_OP_TOP_TOKENS,
+                   CeError, check)
+
+__all__ = ["Head", "Graph", "CeError", "load_library"]
+
+
+def load_library():
+    """Load ``libce.so`` (raises when it has not been built)."""
+    return _ffi.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return CE_BF16
+    if t.dtype == torch.float32:
+        return CE_F32
+    raise TypeError(f"unsupported element type {t.dtype}; use float32 or bfloat16")
+
+
+def _stream_handle(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _host_i32(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+class Graph:
+    """An instantiated HIP graph of one ``top_tokens`` or ``masked_logits`` call."""
+
+    def __init__(self, lib, handle, keep):
+        self._lib = lib
+        self._handle = handle
+        self._keep = keep
+
+    def launch(self, stream=None) -> None:
+        s = stream if stream is not None else _stream_handle(self._keep[0].device)
+        check(self._lib.ce_graph_launch(self._handle, s), "ce_graph_launch")
+
+    def close(self) -> None:
+        if self._handle:
+            self._lib.ce_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Head:
+    """One prepared head: centroids ``[Nc, d]``, ordered embeddings ``[V, d]``.
+
+    ``token_of_slot`` (host, ``[V]``) gives the token id of each embedding row;
+    ``cluster_offsets`` (host, ``[Nc+1]``) gives each centroid's slot range, or
+    None for equal clusters.  ``max_B``/``max_K`` bound later calls.
+    """
+
+    def __init__(self, centroids, emb_ordered, token_of_slot, cluster_offsets=None,
+                 max_B: int = 64, max_K: int | None = None):
+        torch = _torch()
+        self._lib = _ffi.load()
+        for name, t in (("centroids", centroids), ("emb_ordered", emb_ordered)):
+            if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+                raise ValueError(f"{name} must be a contiguous 2-D GPU tensor")
+        if centroids.dtype != emb_ordered.dtype:
+            raise TypeError("centroids and emb_ordered must share one element type")
+        self.device = centroids.device
+        self.Nc, self.d = centroids.shape
+        self.V = emb_ordered.shape[0]
+        self.dtype = centroids.dtype
+        self.max_B = int(max_B)
+        self.max_K = int(max_K if max_K is not None else self.Nc)
+        self._tos = _host_i32(token_of_slot)
+        self._off = None if cluster_offsets is None else _host_i32(cluster_offsets)
+        self._keep = (centroids, emb_ordered)
+        desc = _ffi.HeadDesc(
+            d=self.d, V=self.V, Nc=self.Nc, max_B=self.max_B, max_K=self.max_K,
+            dtype=_dtype_code(centroids), centroids=centroids.data_ptr(),
+            emb_ordered=emb_ordered.data_ptr(),
+            cluster_offsets=None if self._off is None else
+            self._off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            token_of_slot=self._tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        handle = ctypes.c_void_p()
+        check(self._lib.ce_head_create(ctypes.byref(desc), ctypes.byref(handle)), "ce_head_create")
+        self._handle = handle
+        nbytes = ctypes.c_size_t()
+        check(self._lib.ce_head_persistent_bytes(handle, ctypes.byref(nbytes)),
+              "ce_head_persistent_bytes")
+        self._persist = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=self.device)
+        check(self._lib.ce_head_prepare(handle, self._persist.data_ptr(), nbytes.value,
+                                        _stream_handle(self.device)), "ce_head_prepare")
+        self._ws = {}
+
+    # ------------------------------------------------------------------ helpers
+    def workspace_bytes(self, B: int, K: int, op: int) -> int:
+        n = ctypes.c_size_t()
+        check(self._lib.ce_workspace_bytes(self._handle, B, K, op, ctypes.byref(n)),
+              "ce_workspace_bytes")
+        return n.value
+
+    def new_workspace(self, B: int, K: int, op: int):
+        torch = _torch()
+        return torch.empty(max(self.workspace_bytes(B, K, op), 256), dtype=torch.uint8,
+                           device=self.device)
+
+    def _workspace(self, B: int, K: int, op: int):
+        need = self.workspace_bytes(B, K, op)
+        ws = self._ws.get(op)
+        if ws is None or ws.numel() < need:
+            ws = self.new_workspace(B, K, op)
+            self._ws[op] = ws
+        return ws
+
+    def _check_h(self, h):
+        if not h.is_cuda or h.device != self.device or h.dtype != self.dtype:
+            raise ValueError("h must be on the head's device with the head's element type")
+        if h.dim() != 2 or h.shape[1] != self.d or not h.is_contiguous():
+            raise ValueError(f"h must be a contiguous [B, {self.d}] tensor")
+        return h.shape[0]
+
+    def _k(self, K):
+        return self.max_K if K is None else int(K)
+
+    # ------------------------------------------------------------------ calls
+    def score_centroids(self, h, out=None):
+        """``[B, Nc]`` fp32 canonical scores of every row against every centroid."""
+        torch = _torch()
+        B = self._check_h(h)
+        if out is None:
+            out = torch.empty((B, self.Nc), dtype=torch.float32, device=self.device)
+        ws = self._workspace(B, 1, CE_OP_SCORE)
+        check(self._lib.ce_score_centroids(self._handle, h.data_ptr(), B, out.data_ptr(),
+                                           ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
+              "ce_score_centroids")
+        return out
+
+    def topk(self, scores, K: int, out=None):
+        """``[B, K]`` int32 ascending ids of the K best centroids of each row."""
+        torch = _torch()
+        if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[1] != self.Nc \
+                or not scores.is_contiguous() or scores.device != self.device:
+            raise ValueError(f"scores must be a contiguous fp32 [B, {self.Nc}] tensor on the device")
+        B = scores.shape[0]
+        if out is None:
+            out = torch.empty((B, K), dtype=torch.int32, device=self.device)
+        check(self._lib.ce_topk(self._handle, scores.data_ptr(), B, K, out.data_ptr(),
+                                _stream_handle(self.device)), "ce_topk")
+        return out
+
+    def top_tokens(self, h, K: int | None = None, out=None, topk_out=None):
+        """``[B]`` int32 greedy token ids (get_top_tokens)."""
+        torch = _torch()
+        B = self._check_h(h)
+        K = self._k(K)
+        if out is None:
+            out = torch.empty((B,), dtype=torch.int32, device=self.device)
+        ws = self._workspace(B, K, CE_OP_TOP_TOKENS)
+        check(self._lib.ce_top_tokens(self._handle, h.data_ptr(), B, K, out.data_ptr(),
+                                      0 if topk_out is None else topk_out.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
+              "ce_top_tokens")
+        return out
+
+    def masked_logits(self, h, K: int | None = None, out=None, topk_out=None):
+        """``[B, V]`` fp32 logits, -inf outside the candidates (forward)."""
+        torch = _torch()
+        B = self._check_h(h)
+        K = self._k(K)
+        if out is None:
+            out = torch.empty((B, self.V), dtype=torch.float32, device=self.device)
+        ws = self._workspace(B, K, CE_OP_MASKED_LOGITS)
+        check(self._lib.ce_masked_logits(self._handle, h.data_ptr(), B, K, out.data_ptr(),
+                                         0 if topk_out is None else topk_out.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
+              "ce_masked_logits")
+        return out
+
+    def capture(self, op: int, h, K: int | None, out, topk_out=None, stream=None) -> Graph:
+        """Capture one call into a HIP graph with its own workspace.
+
+        ``op`` is ``CE_OP_TOP_TOKENS`` or ``CE_OP_MASKED_LOGITS``; ``h``, ``out``
+        and ``topk_out`` are read/written at the same addresses on every launch.
+        ``stream`` (a torch stream, not the null stream) is used for capture.
+        """
+        torch = _torch()
+        B = self._check_h(h)
+        K = self._k(K)
+        ws = self.new_workspace(B, K, op)
+        s = stream if stream is not None else torch.cuda.Stream(self.device)
+        g = ctypes.c_void_p()
+        check(self._lib.ce_graph_capture(self._handle, op, h.data_ptr(), B, K, out.data_ptr(),
+                                         0 if topk_out is None else topk_out.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), s.cuda_stream,
+                                         ctypes.byref(g)), "ce_graph_capture")
+        return Graph(self._lib, g, (h, out, topk_out, ws, self))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            self._lib.ce_head_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+OP_TOP_TOKENS = CE_OP_TOP_TOKENS
+OP_MASKED_LOGITS = CE_OP_MASKED_LOGITS

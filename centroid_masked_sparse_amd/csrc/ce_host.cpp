@@ -1,0 +1,487 @@
+// Host side of the centroid-masked sparse LM head: argument validation,
+// derived tables, workspace layout and the stream-ordered sequence of kernels
+// for each entry point of include/ce.h.
+//
+// The head follows Gemma4MTPMaskedEmbedder of the vLLM compare view "[Spec
+// Decode] Add Gemma4 MTP speculative decoding with centroids masking" (diff of
+// gemma4_mtp.py).  Its token_ordering buffer, read as slot -> token id and
+// viewed as [num_centroids, vocab_size_per_centroid], becomes token_of_slot
+// plus cluster offsets (equal clusters when no offsets are given).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/ce.h"
+#include "ce_internal.h"
+
+struct ce_head {
+  int32_t d = 0, V = 0, Nc = 0, max_B = 0, max_K = 0, dtype = 0;
+  const void* C = nullptr;
+  const void* E = nullptr;
+  std::vector<int32_t> offsets;       // [Nc+1]
+  std::vector<int32_t> tos;           // [V]
+  std::vector<int32_t> tok_cluster;   // [V]
+  std::vector<int32_t> tok_rank;      // [V]
+  std::vector<long long> cand_top;    // cand_top[K] = tokens owned by the K largest clusters
+  std::vector<long long> tiles_top;   // tiles_top[K] = tiles of the K clusters with most tiles
+  long long total_tiles = 0;
+  bool prepared = false;
+  ce::Tables tables{};
+};
+
+struct ce_graph {
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_probe_start = nullptr;
+thread_local hipEvent_t g_probe_stop = nullptr;
+
+ce_status fail(ce_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+ce_status fail_hip(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return CE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
+
+// Workspace regions of one pass (at most ce::kPassRows rows).
+struct Layout {
+  size_t state = 0, h64 = 0, scores = 0, topk = 0, cl_mask = 0, best = 0, items = 0,
+         rowpos = 0, logits = 0, total = 0;
+  int max_items = 0;
+  int ldL = 0;
+};
+
+Layout make_layout(const ce_head* h, int B, int K, int op) {
+  Layout L;
+  const size_t nb = (size_t)std::min(B, ce::kPassRows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.state = take(sizeof(ce::CallState));
+  L.h64 = take(nb * h->d * sizeof(double));
+  if (op == CE_OP_SCORE) {
+    L.total = off;
+    return L;
+  }
+  L.scores = take(nb * h->Nc * sizeof(float));
+  L.topk = take(nb * (size_t)K * sizeof(int32_t));
+  L.cl_mask = take((size_t)h->Nc * sizeof(unsigned long long));
+  L.best = take(ce::kPassRows * sizeof(unsigned long long));
+  const long long items = std::min<long long>(h->total_tiles, (long long)nb * h->tiles_top[K]);
+  L.max_items = (int)items;
+  L.items = take((size_t)std::max<long long>(items, 1) * sizeof(uint32_t));
+  if (op == CE_OP_MASKED_LOGITS) {
+    L.rowpos = take(nb * h->Nc * sizeof(int32_t));
+    L.ldL = (int)h->cand_top[K];
+    L.logits = take(nb * (size_t)std::max(L.ldL, 1) * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+// Offsets of the four device tables inside the persistent buffer.
+struct PersistLayout {
+  size_t offsets, tos, tok_cluster, tok_rank, total;
+};
+
+PersistLayout persist_layout(const ce_head* h) {
+  PersistLayout p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  p.offsets = take(((size_t)h->Nc + 1) * sizeof(int32_t));
+  p.tos = take((size_t)h->V * sizeof(int32_t));
+  p.tok_cluster = take((size_t)h->V * sizeof(int32_t));
+  p.tok_rank = take((size_t)h->V * sizeof(int32_t));
+  p.total = off;
+  return p;
+}
+
+ce_status check_call(const ce_head* h, const void* in, int B, int K, bool needs_k) {
+  if (!h) return fail(CE_ERR_NULL_POINTER, "head is NULL");
+  if (!h->prepared) return fail(CE_ERR_NOT_PREPARED, "ce_head_prepare has not been called");
+  if (B < 0 || B > h->max_B) return fail(CE_ERR_BAD_SHAPE, "B must lie in [0, max_B]");
+  if (needs_k && (K < 1 || K > h->max_K)) return fail(CE_ERR_BAD_SHAPE, "K must lie in [1, max_K]");
+  if (B > 0 && !in) return fail(CE_ERR_NULL_POINTER, "input pointer is NULL");
+  return CE_SUCCESS;
+}
+
+ce::PassArgs base_args(const ce_head* h, int K) {
+  ce::PassArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.dtype = h->dtype;
+  a.d = h->d;
+  a.V = h->V;
+  a.Nc = h->Nc;
+  a.K = K;
+  a.C = h->C;
+  a.E = h->E;
+  a.t = h->tables;
+  return a;
+}
+
+void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
+  a.state = reinterpret_cast<ce::CallState*>(ws + L.state);
+  a.H64 = reinterpret_cast<double*>(ws + L.h64);
+  a.S = reinterpret_cast<float*>(ws + L.scores);
+  a.ldS = a.Nc;
+  a.topk = reinterpret_cast<int32_t*>(ws + L.topk);
+  a.ldK = a.K;
+  a.cl_mask = reinterpret_cast<unsigned long long*>(ws + L.cl_mask);
+  a.best = reinterpret_cast<unsigned long long*>(ws + L.best);
+  a.items = reinterpret_cast<uint32_t*>(ws + L.items);
+  a.max_items = L.max_items;
+  a.rowpos = reinterpret_cast<int32_t*>(ws + L.rowpos);
+  a.L = reinterpret_cast<float*>(ws + L.logits);
+  a.ldL = L.ldL;
+}
+
+// The shared sequence of ce_top_tokens and ce_masked_logits, in passes of at
+// most kPassRows rows.
+ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* out,
+                     int32_t* topk_ids, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st = check_call(h, hin, B, K, true);
+  if (st != CE_SUCCESS) return st;
+  if (B > 0 && !out) return fail(CE_ERR_NULL_POINTER, "output pointer is NULL");
+  if (B == 0) return CE_SUCCESS;
+  if (!ws) return fail(CE_ERR_NULL_POINTER, "workspace is NULL");
+  if (!aligned(hin, 16) || !aligned(out, op == CE_OP_MASKED_LOGITS ? 16 : 4) || !aligned(ws, 256) ||
+      (topk_ids && !aligned(topk_ids, 4)))
+    return fail(CE_ERR_MISALIGNED, "h and logits need 16-byte, ws 256-byte alignment");
+  const Layout L = make_layout(h, B, K, op);
+  if (ws_bytes < L.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than ce_workspace_bytes");
+
+  hipEvent_t pstart = g_probe_start, pstop = g_probe_stop;
+  g_probe_start = g_probe_stop = nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (pstart && hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+    pstart = pstop = nullptr;
+
+  const size_t in_row = (size_t)h->d * elem_bytes(h->dtype);
+  for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
+    const int nb = std::min(ce::kPassRows, B - b0);
+    ce::PassArgs a = base_args(h, K);
+    a.B = nb;
+    a.h = static_cast<const char*>(hin) + (size_t)b0 * in_row;
+    bind_workspace(a, L, static_cast<char*>(ws));
+    if (topk_ids) {
+      a.topk = topk_ids + (size_t)b0 * K;
+      a.ldK = K;
+    }
+    if (op == CE_OP_TOP_TOKENS) a.tokens = static_cast<int32_t*>(out) + b0;
+    else a.logits = static_cast<float*>(out) + (size_t)b0 * h->V;
+    if (b0 == 0) {
+      a.probe_start = pstart;
+      a.probe_stop = pstop;
+    }
+    hipError_t e = ce::launch_prep(a, stream);
+    if (e == hipSuccess) e = ce::launch_scores(a, stream);
+    if (e == hipSuccess)
+      e = ce::launch_topk(a, op == CE_OP_MASKED_LOGITS ? ce::kTopkPlanRowpos : ce::kTopkPlan, stream);
+    if (e == hipSuccess)
+      e = ce::launch_gather(a, op == CE_OP_MASKED_LOGITS ? ce::kMasked : ce::kArgmax, stream);
+    if (e == hipSuccess && op == CE_OP_MASKED_LOGITS) e = ce::launch_writer(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  }
+  return CE_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
+  if (!desc || !out) return fail(CE_ERR_NULL_POINTER, "desc or out is NULL");
+  *out = nullptr;
+  if (!desc->centroids || !desc->emb_ordered || !desc->token_of_slot)
+    return fail(CE_ERR_NULL_POINTER, "centroids, emb_ordered and token_of_slot are required");
+  if (desc->dtype != CE_F32 && desc->dtype != CE_BF16) return fail(CE_ERR_BAD_DTYPE, "dtype must be CE_F32 or CE_BF16");
+  const int d = desc->d, V = desc->V, Nc = desc->Nc;
+  if (d < 64 || d > ce::kMaxD || d % 64) return fail(CE_ERR_BAD_SHAPE, "d must be a multiple of 64 in [64, 8192]");
+  if (V < 1) return fail(CE_ERR_BAD_SHAPE, "V must be >= 1");
+  if (Nc < 1 || Nc > ce::kMaxNc) return fail(CE_ERR_BAD_SHAPE, "Nc must lie in [1, 8192]");
+  if (desc->max_B < 1) return fail(CE_ERR_BAD_SHAPE, "max_B must be >= 1");
+  if (desc->max_K < 1 || desc->max_K > Nc) return fail(CE_ERR_BAD_SHAPE, "max_K must lie in [1, Nc]");
+  if (!aligned(desc->centroids, 16) || !aligned(desc->emb_ordered, 16))
+    return fail(CE_ERR_MISALIGNED, "centroids and emb_ordered need 16-byte alignment");
+
+  ce_head* h = new (std::nothrow) ce_head;
+  if (!h) return fail(CE_ERR_UNSUPPORTED, "out of host memory");
+  h->d = d;
+  h->V = V;
+  h->Nc = Nc;
+  h->max_B = desc->max_B;
+  h->max_K = desc->max_K;
+  h->dtype = desc->dtype;
+  h->C = desc->centroids;
+  h->E = desc->emb_ordered;
+  try {
+    h->offsets.resize((size_t)Nc + 1);
+    if (desc->cluster_offsets) {
+      std::memcpy(h->offsets.data(), desc->cluster_offsets, h->offsets.size() * sizeof(int32_t));
+      if (h->offsets[0] != 0 || h->offsets[Nc] != V) {
+        delete h;
+        return fail(CE_ERR_BAD_LAYOUT, "offsets must start at 0 and end at V");
+      }
+      for (int c = 0; c < Nc; ++c)
+        if (h->offsets[c + 1] < h->offsets[c]) {
+          delete h;
+          return fail(CE_ERR_BAD_LAYOUT, "offsets must be nondecreasing");
+        }
+    } else {
+      if (V % Nc) {
+        delete h;
+        return fail(CE_ERR_BAD_LAYOUT, "equal clusters need V % Nc == 0");
+      }
+      for (int c = 0; c <= Nc; ++c) h->offsets[c] = (int32_t)((long long)c * (V / Nc));
+    }
+    h->tos.assign(desc->token_of_slot, desc->token_of_slot + V);
+    h->tok_cluster.assign((size_t)V, -1);
+    h->tok_rank.assign((size_t)V, 0);
+    for (int c = 0; c < Nc; ++c) {
+      for (int j = h->offsets[c]; j < h->offsets[c + 1]; ++j) {
+        const int32_t t = h->tos[j];
+        if (t < 0 || t >= V || h->tok_cluster[t] != -1) {
+          delete h;
+          return fail(CE_ERR_BAD_LAYOUT, "token_of_slot must be a permutation of 0..V-1");
+        }
+        h->tok_cluster[t] = c;
+        h->tok_rank[t] = j - h->offsets[c];
+      }
+    }
+    std::vector<long long> sizes(Nc), tiles(Nc);
+    for (int c = 0; c < Nc; ++c) {
+      sizes[c] = h->offsets[c + 1] - h->offsets[c];
+      tiles[c] = (sizes[c] + ce::kTileTokens - 1) / ce::kTileTokens;
+      if (tiles[c] > ce::kMaxTilesPerCluster) {
+        delete h;
+        return fail(CE_ERR_UNSUPPORTED, "a cluster holds more than 2^19 * 64 tokens");
+      }
+    }
+    std::sort(sizes.begin(), sizes.end(), std::greater<long long>());
+    std::sort(tiles.begin(), tiles.end(), std::greater<long long>());
+    h->cand_top.assign((size_t)Nc + 1, 0);
+    h->tiles_top.assign((size_t)Nc + 1, 0);
+    for (int k = 0; k < Nc; ++k) {
+      h->cand_top[k + 1] = h->cand_top[k] + sizes[k];
+      h->tiles_top[k + 1] = h->tiles_top[k] + tiles[k];
+    }
+    h->total_tiles = h->tiles_top[Nc];
+  } catch (const std::bad_alloc&) {
+    delete h;
+    return fail(CE_ERR_UNSUPPORTED, "out of host memory");
+  }
+  *out = h;
+  return CE_SUCCESS;
+}
+
+ce_status ce_head_destroy(ce_head_t head) {
+  delete head;
+  return CE_SUCCESS;
+}
+
+ce_status ce_head_persistent_bytes(ce_head_t head, size_t* bytes) {
+  if (!head || !bytes) return fail(CE_ERR_NULL_POINTER, "head or bytes is NULL");
+  *bytes = persist_layout(head).total;
+  return CE_SUCCESS;
+}
+
+ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStream_t stream) {
+  if (!head || !persistent) return fail(CE_ERR_NULL_POINTER, "head or persistent buffer is NULL");
+  if (!aligned(persistent, 256)) return fail(CE_ERR_MISALIGNED, "persistent buffer needs 256-byte alignment");
+  const PersistLayout p = persist_layout(head);
+  if (bytes < p.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "persistent buffer too small");
+  char* base = static_cast<char*>(persistent);
+  struct Copy {
+    size_t at;
+    const std::vector<int32_t>* v;
+  } copies[] = {{p.offsets, &head->offsets}, {p.tos, &head->tos},
+                {p.tok_cluster, &head->tok_cluster}, {p.tok_rank, &head->tok_rank}};
+  for (const Copy& c : copies) {
+    hipError_t e = hipMemcpyAsync(base + c.at, c.v->data(), c.v->size() * sizeof(int32_t),
+                                  hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
+  }
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+  head->tables.offsets = reinterpret_cast<const int32_t*>(base + p.offsets);
+  head->tables.tos = reinterpret_cast<const int32_t*>(base + p.tos);
+  head->tables.tok_cluster = reinterpret_cast<const int32_t*>(base + p.tok_cluster);
+  head->tables.tok_rank = reinterpret_cast<const int32_t*>(base + p.tok_rank);
+  head->prepared = true;
+  return CE_SUCCESS;
+}
+
+ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op, size_t* bytes) {
+  if (!head || !bytes) return fail(CE_ERR_NULL_POINTER, "head or bytes is NULL");
+  if (op < CE_OP_SCORE || op > CE_OP_MASKED_LOGITS) return fail(CE_ERR_UNSUPPORTED, "unknown op");
+  if (B < 0 || B > head->max_B) return fail(CE_ERR_BAD_SHAPE, "B must lie in [0, max_B]");
+  if (op == CE_OP_TOPK) {
+    *bytes = 0;
+    return CE_SUCCESS;
+  }
+  if (op != CE_OP_SCORE && (K < 1 || K > head->max_K)) return fail(CE_ERR_BAD_SHAPE, "K must lie in [1, max_K]");
+  *bytes = make_layout(head, B, op == CE_OP_SCORE ? 1 : K, op).total;
+  return CE_SUCCESS;
+}
+
+ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* scores, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  ce_status st = check_call(head, h, B, 1, false);
+  if (st != CE_SUCCESS) return st;
+  if (B == 0) return CE_SUCCESS;
+  if (!scores || !ws) return fail(CE_ERR_NULL_POINTER, "scores or workspace is NULL");
+  if (!aligned(h, 16) || !aligned(scores, 4) || !aligned(ws, 256))
+    return fail(CE_ERR_MISALIGNED, "h needs 16-byte, ws 256-byte alignment");
+  const Layout L = make_layout(head, B, 1, CE_OP_SCORE);
+  if (ws_bytes < L.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than ce_workspace_bytes");
+  const size_t in_row = (size_t)head->d * elem_bytes(head->dtype);
+  for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
+    ce::PassArgs a = base_args(head, 1);
+    a.B = std::min(ce::kPassRows, B - b0);
+    a.h = static_cast<const char*>(h) + (size_t)b0 * in_row;
+    char* w = static_cast<char*>(ws);
+    a.state = reinterpret_cast<ce::CallState*>(w + L.state);
+    a.H64 = reinterpret_cast<double*>(w + L.h64);
+    a.cl_mask = nullptr;  // prep then clears only the call state
+    a.best = nullptr;
+    a.S = scores + (size_t)b0 * head->Nc;
+    a.ldS = head->Nc;
+    hipError_t e = ce::launch_prep(a, stream);
+    if (e == hipSuccess) e = ce::launch_scores(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  }
+  return CE_SUCCESS;
+}
+
+ce_status ce_topk(ce_head_t head, const float* scores, int32_t B, int32_t K, int32_t* topk_ids,
+                  hipStream_t stream) {
+  ce_status st = check_call(head, scores, B, K, true);
+  if (st != CE_SUCCESS) return st;
+  if (B == 0) return CE_SUCCESS;
+  if (!topk_ids) return fail(CE_ERR_NULL_POINTER, "topk_ids is NULL");
+  if (!aligned(scores, 4) || !aligned(topk_ids, 4)) return fail(CE_ERR_MISALIGNED, "scores and ids need 4-byte alignment");
+  for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
+    ce::PassArgs a = base_args(head, K);
+    a.B = std::min(ce::kPassRows, B - b0);
+    a.S = const_cast<float*>(scores) + (size_t)b0 * head->Nc;
+    a.ldS = head->Nc;
+    a.topk = topk_ids + (size_t)b0 * K;
+    a.ldK = K;
+    hipError_t e = ce::launch_topk(a, ce::kTopkOnly, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  }
+  return CE_SUCCESS;
+}
+
+ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t* tokens,
+                        int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_sparse(head, CE_OP_TOP_TOKENS, h, B, K, tokens, topk_ids_or_null, ws, ws_bytes, stream);
+}
+
+ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K, float* logits,
+                           int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_sparse(head, CE_OP_MASKED_LOGITS, h, B, K, logits, topk_ids_or_null, ws, ws_bytes, stream);
+}
+
+ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B, int32_t K, void* out,
+                           int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream,
+                           ce_graph_t* graph) {
+  if (!graph) return fail(CE_ERR_NULL_POINTER, "graph is NULL");
+  *graph = nullptr;
+  if (op != CE_OP_TOP_TOKENS && op != CE_OP_MASKED_LOGITS)
+    return fail(CE_ERR_UNSUPPORTED, "only CE_OP_TOP_TOKENS and CE_OP_MASKED_LOGITS are captured");
+  if (!stream) return fail(CE_ERR_UNSUPPORTED, "capture needs a non-null stream");
+  // validate before capturing so that a bad call leaves no capture behind
+  ce_status st = check_call(head, h, B, K, true);
+  if (st != CE_SUCCESS) return st;
+  hipError_t e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamBeginCapture");
+  st = run_sparse(head, op, h, B, K, out, topk_ids_or_null, ws, ws_bytes, stream);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(stream, &g);
+  if (st != CE_SUCCESS) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return fail_hip(e, "hipStreamEndCapture");
+  ce_graph* out_g = new (std::nothrow) ce_graph;
+  if (!out_g) {
+    (void)hipGraphDestroy(g);
+    return fail(CE_ERR_UNSUPPORTED, "out of host memory");
+  }
+  e = hipGraphInstantiate(&out_g->exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) {
+    delete out_g;
+    return fail_hip(e, "hipGraphInstantiate");
+  }
+  *graph = out_g;
+  return CE_SUCCESS;
+}
+
+ce_status ce_graph_launch(ce_graph_t graph, hipStream_t stream) {
+  if (!graph || !graph->exec) return fail(CE_ERR_NULL_POINTER, "graph is NULL");
+  hipError_t e = hipGraphLaunch(graph->exec, stream);
+  if (e != hipSuccess) return fail_hip(e, "hipGraphLaunch");
+  return CE_SUCCESS;
+}
+
+ce_status ce_graph_destroy(ce_graph_t graph) {
+  if (!graph) return CE_SUCCESS;
+  if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return CE_SUCCESS;
+}
+
+ce_status ce_probe_gather_events(hipEvent_t start, hipEvent_t stop) {
+  if (!start || !stop) return fail(CE_ERR_NULL_POINTER, "events are NULL");
+  g_probe_start = start;
+  g_probe_stop = stop;
+  return CE_SUCCESS;
+}
+
+const char* ce_status_string(ce_status status) {
+  switch (status) {
+    case CE_SUCCESS: return "CE_SUCCESS";
+    case CE_ERR_NULL_POINTER: return "CE_ERR_NULL_POINTER";
+    case CE_ERR_BAD_SHAPE: return "CE_ERR_BAD_SHAPE";
+    case CE_ERR_BAD_DTYPE: return "CE_ERR_BAD_DTYPE";
+    case CE_ERR_MISALIGNED: return "CE_ERR_MISALIGNED";
+    case CE_ERR_BAD_LAYOUT: return "CE_ERR_BAD_LAYOUT";
+    case CE_ERR_WORKSPACE_TOO_SMALL: return "CE_ERR_WORKSPACE_TOO_SMALL";
+    case CE_ERR_NOT_PREPARED: return "CE_ERR_NOT_PREPARED";
+    case CE_ERR_HIP: return "CE_ERR_HIP";
+    case CE_ERR_UNSUPPORTED: return "CE_ERR_UNSUPPORTED";
+  }
+  return "CE_UNKNOWN_STATUS";
+}
+
+const char* ce_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

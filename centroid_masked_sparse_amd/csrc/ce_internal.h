@@ -1,0 +1,73 @@
+// Internal interface between the host library (ce_host.cpp) and the HIP
+// kernels (ce_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ce {
+
+constexpr int kPassRows = 64;     // rows per internal pass: row sets are 64-bit masks
+constexpr int kTileTokens = 64;   // candidate tokens per gather work item (one per lane)
+constexpr int kMaxNc = 8192;      // centroid id fits the low 13 bits of a work item
+constexpr int kItemShift = 13;
+constexpr int kMaxTilesPerCluster = 1 << (32 - kItemShift);
+constexpr int kMaxD = 8192;
+
+// Per-call counters, cleared by the first kernel of every pass.
+struct CallState {
+  uint32_t n_items;      // gather work items appended by the top-K kernel
+  uint32_t done_items;   // gather work items finished (argmax completion ticket)
+  uint32_t pad[62];      // 256 bytes
+};
+
+// Device tables uploaded at prepare time.
+struct Tables {
+  const int32_t* offsets;      // [Nc+1] cluster c owns slots [offsets[c], offsets[c+1])
+  const int32_t* tos;          // [V] token id of each slot
+  const int32_t* tok_cluster;  // [V] cluster owning each token
+  const int32_t* tok_rank;     // [V] slot of each token minus its cluster's first slot
+};
+
+enum GatherMode { kArgmax = 0, kMasked = 1 };
+enum TopkMode { kTopkOnly = 0, kTopkPlan = 1, kTopkPlanRowpos = 2 };
+
+// Everything one pass (at most kPassRows rows) needs.
+struct PassArgs {
+  int dtype;              // CE_F32 or CE_BF16
+  int d, V, Nc, K;
+  int B;                  // rows in this pass, 1..kPassRows
+  const void* C;          // [Nc][d]
+  const void* E;          // [V][d] ordered layout
+  Tables t;
+  const void* h;          // [B][d] rows of this pass
+  // workspace regions
+  CallState* state;
+  double* H64;            // [B][d] hidden rows widened to float64
+  float* S;               // [B][ldS] centroid scores
+  int ldS;
+  int32_t* topk;          // [B][ldK] selected centroids
+  int ldK;
+  unsigned long long* cl_mask;  // [Nc] rows that selected each centroid
+  unsigned long long* best;     // [kPassRows] packed (ordered logit, ~token)
+  uint32_t* items;              // [max_items] (tile << 13) | centroid
+  int max_items;
+  int32_t* rowpos;        // [B][Nc] first candidate position of a centroid in a row, or -1
+  float* L;               // [B][ldL] candidate logits in row order
+  int ldL;
+  // outputs
+  int32_t* tokens;        // [B]
+  float* logits;          // [B][V]
+  // measurement hook (HIP extended launch around the gather kernel)
+  hipEvent_t probe_start;
+  hipEvent_t probe_stop;
+};
+
+hipError_t launch_prep(const PassArgs& a, hipStream_t s);
+hipError_t launch_scores(const PassArgs& a, hipStream_t s);
+hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);
+hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
+hipError_t launch_writer(const PassArgs& a, hipStream_t s);
+
+}  // namespace ce

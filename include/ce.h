@@ -1,0 +1,222 @@
+/*
+ * ce.h - C ABI of the centroid-masked sparse LM head for MI355X (gfx950).
+ *
+ * The operation is the one of Gemma4MTPMaskedEmbedder in the vLLM compare view
+ * "[Spec Decode] Add Gemma4 MTP speculative decoding with centroids masking"
+ * (diff of gemma4_mtp.py):
+ *   _select_and_score  project each hidden row onto Nc centroid vectors, keep
+ *                      the K best centroids, gather the embeddings of the
+ *                      tokens those centroids own and dot them with the row;
+ *   forward            a full-vocabulary logit row: those scores at the
+ *                      candidate token ids, the fill value everywhere else;
+ *   get_top_tokens     the token id of the largest candidate score.
+ *
+ * Numerics (fixed where the page leaves them open):
+ *   - Every dot product is the canonical key: elements widened exactly to
+ *     float64, summed in hidden-dimension order from +0.0 with one rounding
+ *     per step (s = fma(x_k, w_k, s)), then rounded to fp32 nearest-even and
+ *     -0 turned into +0.  All scores and logits returned are these values.
+ *   - Top-K ties go to the lowest centroid id; argmax ties to the lowest token
+ *     id.  Top-K ids are returned as an ascending set.
+ *   - The fill value of the full-vocabulary row is -inf (fp32 0xFF800000).
+ *   - NaN inputs are not supported.
+ *
+ * Layout: the embedding table is in the ordered layout: row j holds the
+ * embedding of token token_of_slot[j], and cluster c owns the contiguous slots
+ * [cluster_offsets[c], cluster_offsets[c+1]).  With equal clusters (offsets
+ * NULL) cluster c owns slots [c*V/Nc, (c+1)*V/Nc), which is the page's
+ * token_ordering.view(num_centroids, vocab_size_per_centroid).
+ *
+ * Memory and streams: the library never allocates device memory.  The caller
+ * passes a persistent buffer at prepare time and a workspace on every call,
+ * sized by ce_head_persistent_bytes / ce_workspace_bytes.  Every compute call
+ * is enqueued on the caller's stream, never synchronises, reads no device
+ * memory on the host and may be captured into a HIP graph.  Calls that share
+ * one workspace must be ordered on one stream.  A head handle is read-only
+ * after ce_head_prepare, so calls on several streams with separate
+ * workspaces may run concurrently.
+ *
+ * Errors: every entry point returns a ce_status; nothing is thrown across
+ * the ABI.  ce_last_error() gives a thread-local message for the last failure
+ * of the calling thread.  Argument checks happen before any device work; on a
+ * check failure nothing is enqueued and no output is written.
+ */
+#ifndef CE_H_
+#define CE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ce_status {
+  CE_SUCCESS = 0,
+  CE_ERR_NULL_POINTER = 1,     /* a required pointer is NULL */
+  CE_ERR_BAD_SHAPE = 2,        /* a size is out of range (see each call) */
+  CE_ERR_BAD_DTYPE = 3,        /* element type is not CE_F32 or CE_BF16 */
+  CE_ERR_MISALIGNED = 4,       /* a device pointer is not 16-byte aligned */
+  CE_ERR_BAD_LAYOUT = 5,       /* token_of_slot not a permutation, or bad offsets */
+  CE_ERR_WORKSPACE_TOO_SMALL = 6,
+  CE_ERR_NOT_PREPARED = 7,     /* compute call before ce_head_prepare */
+  CE_ERR_HIP = 8,              /* the HIP runtime reported an error */
+  CE_ERR_UNSUPPORTED = 9       /* valid request this library does not serve */
+} ce_status;
+
+typedef enum ce_dtype {
+  CE_F32 = 0,   /* IEEE binary32 */
+  CE_BF16 = 1   /* bfloat16 (upper half of a binary32) */
+} ce_dtype;
+
+typedef enum ce_op {
+  CE_OP_SCORE = 0,          /* ce_score_centroids */
+  CE_OP_TOPK = 1,           /* ce_topk */
+  CE_OP_TOP_TOKENS = 2,     /* ce_top_tokens */
+  CE_OP_MASKED_LOGITS = 3   /* ce_masked_logits */
+} ce_op;
+
+typedef struct ce_head* ce_head_t;
+typedef struct ce_graph* ce_graph_t;
+
+/* Shape and weights of one head (the constructor arguments of the page's
+ * Gemma4MTPMaskedEmbedder: hidden_size, vocab_size, num_centroids,
+ * centroid_intermediate_top_k, plus the centroid weight, token_ordering and
+ * the lm_head weight that _select_and_score receives).
+ *
+ *   d        hidden size; a multiple of 64 in [64, 8192]
+ *   V        vocabulary size, in [1, 2^31 - 1]
+ *   Nc       number of centroids, in [1, 8192] and <= V when offsets is NULL
+ *   max_B    largest batch any call will pass, >= 1
+ *   max_K    largest K any call will pass, in [1, Nc]
+ *   dtype    element type of h, centroids and embeddings (ce_dtype)
+ *   centroids       DEVICE [Nc][d] row-major, 16-byte aligned; borrowed
+ *   emb_ordered     DEVICE [V][d] row-major, 16-byte aligned; borrowed; row j
+ *                   is the embedding of token token_of_slot[j]
+ *   cluster_offsets HOST [Nc+1] nondecreasing, offsets[0] = 0,
+ *                   offsets[Nc] = V; or NULL for equal clusters (V % Nc == 0).
+ *                   Empty clusters are allowed.  Copied at create.
+ *   token_of_slot   HOST [V], a permutation of 0..V-1.  Copied at create.
+ * The device arrays must stay valid and unchanged while the head is used. */
+typedef struct ce_head_desc {
+  int32_t d;
+  int32_t V;
+  int32_t Nc;
+  int32_t max_B;
+  int32_t max_K;
+  int32_t dtype;
+  const void* centroids;
+  const void* emb_ordered;
+  const int32_t* cluster_offsets;
+  const int32_t* token_of_slot;
+} ce_head_desc;
+
+/* Validate desc on the host and create a head.  Makes no HIP call.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, BAD_LAYOUT. */
+ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out);
+
+/* Release a head (host memory only; the caller owns every device buffer).
+ * NULL is accepted. */
+ce_status ce_head_destroy(ce_head_t head);
+
+/* Bytes of the persistent device buffer ce_head_prepare needs. Host only. */
+ce_status ce_head_persistent_bytes(ce_head_t head, size_t* bytes);
+
+/* Upload the derived tables (offsets, slot->token and token->(cluster, rank)
+ * maps) into the caller's persistent device buffer (256-byte aligned, at
+ * least ce_head_persistent_bytes).  Set-up only: copies on `stream` and
+ * synchronises it.  The buffer must live as long as the head is used.
+ * Errors: NULL_POINTER, MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
+ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes,
+                          hipStream_t stream);
+
+/* Workspace bytes one call of `op` with batch B and top-K K needs (the
+ * worst case over inputs).  Host only.  CE_OP_TOPK needs none (returns 0).
+ * Errors: NULL_POINTER, BAD_SHAPE. */
+ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op,
+                             size_t* bytes);
+
+/* The centroid projection (the page's self.centroids(hidden_states)):
+ *   scores[b][c] = canonical dot(h[b], centroids[c]),  b < B, c < Nc.
+ *   h       DEVICE [B][d] of the head's dtype, 16-byte aligned
+ *   scores  DEVICE [B][Nc] fp32, written entirely
+ *   ws      DEVICE workspace, 256-byte aligned, >= ce_workspace_bytes(SCORE)
+ * B = 0 is a no-op.  Errors: NOT_PREPARED, NULL_POINTER, BAD_SHAPE
+ * (B outside [0, max_B]), MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
+ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B,
+                             float* scores, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Top-K selection (the page's torch.topk over the centroid scores) on a
+ * caller-given fp32 array, bit-exact: topk_ids[b] holds, in ascending order,
+ * the K centroid ids that rank first under (score descending, id ascending),
+ * with -0 equal to +0.
+ *   scores    DEVICE [B][Nc] fp32 (no NaN)
+ *   topk_ids  DEVICE [B][K] int32
+ * No workspace.  B = 0 is a no-op.  Errors: NOT_PREPARED, NULL_POINTER,
+ * BAD_SHAPE (B outside [0, max_B], K outside [1, max_K]), HIP. */
+ce_status ce_topk(ce_head_t head, const float* scores, int32_t B, int32_t K,
+                  int32_t* topk_ids, hipStream_t stream);
+
+/* get_top_tokens: for every row b < B, the token id t with the largest
+ * canonical logit among the tokens owned by the row's K selected centroids,
+ * ties to the lowest id; -1 when those centroids own no token (possible only
+ * with empty clusters).
+ *   h                DEVICE [B][d] of the head's dtype, 16-byte aligned
+ *   tokens           DEVICE [B] int32
+ *   topk_ids_or_null DEVICE [B][K] int32 (the selected centroids, ascending)
+ *                    or NULL
+ *   ws               DEVICE workspace, 256-byte aligned
+ * B = 0 is a no-op.  Rows are independent: row b's outputs do not depend on
+ * B or on the other rows.  Errors: as ce_score_centroids, plus BAD_SHAPE for
+ * K outside [1, max_K]. */
+ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K,
+                        int32_t* tokens, int32_t* topk_ids_or_null, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* forward: logits[b][t] = canonical logit of token t if t is owned by one of
+ * row b's K selected centroids, else -inf.  Every entry of [B][V] is written.
+ *   logits  DEVICE [B][V] fp32, 16-byte aligned
+ * Other arguments and errors as ce_top_tokens. */
+ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K,
+                           float* logits, int32_t* topk_ids_or_null, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Capture one call of ce_top_tokens (op CE_OP_TOP_TOKENS, out = tokens) or
+ * ce_masked_logits (op CE_OP_MASKED_LOGITS, out = logits) into an
+ * instantiated HIP graph, the counterpart of the page's per-batch-size CUDA
+ * graphs.  The graph reads h and writes out/topk_ids/ws at the addresses given
+ * here on every launch.  `stream` must not be the null stream; it is used only
+ * for capture.  Errors: as the captured call, plus UNSUPPORTED for another
+ * op, HIP for a capture failure. */
+ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B,
+                           int32_t K, void* out, int32_t* topk_ids_or_null,
+                           void* ws, size_t ws_bytes, hipStream_t stream,
+                           ce_graph_t* graph);
+
+/* Launch a captured graph on `stream`.  Errors: NULL_POINTER, HIP. */
+ce_status ce_graph_launch(ce_graph_t graph, hipStream_t stream);
+
+/* Destroy a captured graph.  NULL is accepted. */
+ce_status ce_graph_destroy(ce_graph_t graph);
+
+/* Measurement hook: the next ce_top_tokens or ce_masked_logits call made by
+ * this thread (not under capture) records `start` and `stop` on its stream
+ * immediately around the candidate gather kernel, through the HIP extended
+ * launch so that the pair brackets that kernel alone.  Consumed by that call.
+ * Errors: NULL_POINTER. */
+ce_status ce_probe_gather_events(hipEvent_t start, hipEvent_t stop);
+
+/* Short name of a status code.  Never NULL. */
+const char* ce_status_string(ce_status status);
+
+/* Message for the calling thread's last failure ("" if none).  Never NULL. */
+const char* ce_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CE_H_ */

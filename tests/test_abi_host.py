@@ -1,0 +1,177 @@
+"""Host-side checks of the C ABI (no GPU): symbols, validation, sizing.
+
+ce_head_create, ce_workspace_bytes, ce_head_persistent_bytes and the error
+paths of the compute calls make no HIP call, so they run here with fake
+(aligned, never dereferenced) device addresses.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from centroid_masked_sparse_amd import _ffi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ce.h")
+FAKE = 0x10000          # aligned fake device address (never dereferenced here)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_ffi.LIB_PATH):
+        from centroid_masked_sparse_amd import build_lib
+        build_lib.build()
+    return _ffi.load()
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ce_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared_symbols()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", _ffi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(names) == set(_ffi.SIGNATURES), "binding and header disagree"
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def _desc(d=64, V=256, Nc=4, max_B=8, max_K=4, dtype=_ffi.CE_BF16, tos=None, off=None,
+          c_ptr=FAKE, e_ptr=FAKE):
+    tos = np.arange(V, dtype=np.int32) if tos is None else np.asarray(tos, dtype=np.int32)
+    keep = [tos]
+    desc = _ffi.HeadDesc(d=d, V=V, Nc=Nc, max_B=max_B, max_K=max_K, dtype=dtype,
+                         centroids=c_ptr, emb_ordered=e_ptr,
+                         token_of_slot=tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if off is not None:
+        off = np.asarray(off, dtype=np.int32)
+        keep.append(off)
+        desc.cluster_offsets = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return desc, keep
+
+
+def _create(lib, desc):
+    h = ctypes.c_void_p()
+    st = lib.ce_head_create(ctypes.byref(desc), ctypes.byref(h))
+    return st, h
+
+
+ERR = {v: k for k, v in _ffi.STATUS_NAMES.items()}
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=7), "CE_ERR_BAD_DTYPE"),
+    (dict(d=96), "CE_ERR_BAD_SHAPE"),
+    (dict(d=0), "CE_ERR_BAD_SHAPE"),
+    (dict(Nc=0), "CE_ERR_BAD_SHAPE"),
+    (dict(Nc=9000, V=9000 * 2, max_K=4), "CE_ERR_BAD_SHAPE"),
+    (dict(max_K=5), "CE_ERR_BAD_SHAPE"),
+    (dict(max_B=0), "CE_ERR_BAD_SHAPE"),
+    (dict(c_ptr=FAKE + 8), "CE_ERR_MISALIGNED"),
+    (dict(e_ptr=FAKE + 2), "CE_ERR_MISALIGNED"),
+    (dict(V=250), "CE_ERR_BAD_LAYOUT"),                       # V % Nc with equal clusters
+    (dict(tos=[0] * 256), "CE_ERR_BAD_LAYOUT"),               # not a permutation
+    (dict(tos=np.arange(1, 257)), "CE_ERR_BAD_LAYOUT"),       # out of range
+    (dict(off=[0, 10, 5, 200, 256]), "CE_ERR_BAD_LAYOUT"),    # decreasing
+    (dict(off=[0, 10, 20, 30, 255]), "CE_ERR_BAD_LAYOUT"),    # does not end at V
+    (dict(off=[1, 10, 20, 30, 256]), "CE_ERR_BAD_LAYOUT"),    # does not start at 0
+    (dict(c_ptr=0), "CE_ERR_NULL_POINTER"),
+])
+def test_create_rejects(lib, kw, want):
+    desc, _keep = _desc(**kw)
+    st, h = _create(lib, desc)
+    assert _ffi.STATUS_NAMES[st] == want
+    assert not h.value
+    assert lib.ce_last_error().decode()
+
+
+def test_create_null_args(lib):
+    h = ctypes.c_void_p()
+    assert lib.ce_head_create(None, ctypes.byref(h)) == ERR["CE_ERR_NULL_POINTER"]
+    desc, _keep = _desc()
+    assert lib.ce_head_create(ctypes.byref(desc), None) == ERR["CE_ERR_NULL_POINTER"]
+
+
+def test_create_ragged_and_sizes(lib):
+    off = [0, 0, 100, 130, 256]              # an empty cluster and a 100-token one
+    tos = np.random.default_rng(0).permutation(256)
+    desc, _keep = _desc(tos=tos, off=off, max_B=100, max_K=4)
+    st, h = _create(lib, desc)
+    assert st == 0
+    try:
+        n = ctypes.c_size_t()
+        assert lib.ce_head_persistent_bytes(h, ctypes.byref(n)) == 0
+        # offsets (5 ints) + 3 tables of V ints, each rounded up to 256 bytes
+        assert n.value == 256 + 3 * 1024
+        assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOPK, ctypes.byref(n)) == 0
+        assert n.value == 0
+        sizes = {}
+        for op in (_ffi.CE_OP_SCORE, _ffi.CE_OP_TOP_TOKENS, _ffi.CE_OP_MASKED_LOGITS):
+            assert lib.ce_workspace_bytes(h, 8, 2, op, ctypes.byref(n)) == 0
+            sizes[op] = n.value
+            assert n.value % 256 == 0
+        assert sizes[_ffi.CE_OP_SCORE] < sizes[_ffi.CE_OP_TOP_TOKENS] < sizes[_ffi.CE_OP_MASKED_LOGITS]
+        # more than one pass of rows needs no more workspace than one full pass
+        assert lib.ce_workspace_bytes(h, 64, 2, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == 0
+        one = n.value
+        assert lib.ce_workspace_bytes(h, 100, 2, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == 0
+        assert n.value == one
+        assert lib.ce_workspace_bytes(h, 101, 2, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
+        assert lib.ce_workspace_bytes(h, 8, 5, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
+        assert lib.ce_workspace_bytes(h, 8, 0, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
+        assert lib.ce_workspace_bytes(h, 8, 1, 9, ctypes.byref(n)) == ERR["CE_ERR_UNSUPPORTED"]
+    finally:
+        lib.ce_head_destroy(h)
+
+
+def test_compute_calls_before_prepare_fail_on_host(lib):
+    desc, _keep = _desc()
+    st, h = _create(lib, desc)
+    assert st == 0
+    try:
+        NP = ERR["CE_ERR_NOT_PREPARED"]
+        assert lib.ce_top_tokens(h, FAKE, 1, 2, FAKE, None, FAKE, 1 << 20, None) == NP
+        assert lib.ce_masked_logits(h, FAKE, 1, 2, FAKE, None, FAKE, 1 << 20, None) == NP
+        assert lib.ce_score_centroids(h, FAKE, 1, FAKE, FAKE, 1 << 20, None) == NP
+        assert lib.ce_topk(h, FAKE, 1, 2, FAKE, None) == NP
+        assert "prepare" in lib.ce_last_error().decode()
+        assert lib.ce_top_tokens(None, FAKE, 1, 2, FAKE, None, FAKE, 1, None) == ERR["CE_ERR_NULL_POINTER"]
+        g = ctypes.c_void_p()
+        assert lib.ce_graph_capture(h, 0, FAKE, 1, 2, FAKE, None, FAKE, 1, FAKE,
+                                    ctypes.byref(g)) == ERR["CE_ERR_UNSUPPORTED"]
+        assert lib.ce_graph_launch(None, None) == ERR["CE_ERR_NULL_POINTER"]
+        assert lib.ce_graph_destroy(None) == 0
+        assert lib.ce_head_prepare(h, None, 0, None) == ERR["CE_ERR_NULL_POINTER"]
+        assert lib.ce_head_prepare(h, FAKE + 16, 1 << 20, None) == ERR["CE_ERR_MISALIGNED"]
+        assert lib.ce_head_prepare(h, FAKE, 16, None) == ERR["CE_ERR_WORKSPACE_TOO_SMALL"]
+        assert lib.ce_probe_gather_events(None, None) == ERR["CE_ERR_NULL_POINTER"]
+    finally:
+        assert lib.ce_head_destroy(h) == 0
+    assert lib.ce_head_destroy(None) == 0
+
+
+def test_status_strings(lib):
+    for code, name in _ffi.STATUS_NAMES.items():
+        assert lib.ce_status_string(code).decode() == name
+    assert lib.ce_status_string(99).decode() == "CE_UNKNOWN_STATUS"
+
+
+def test_product_path_never_imports_oracle():
+    pkg = os.path.join(ROOT, "centroid_masked_sparse_amd")
+    for dirpath, _dirs, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "workloads" not in text, f
