@@ -19,8 +19,7 @@ import ctypes
 import numpy as np
 
 from . import _ffi
-from ._ffi import (CE_BF16, CE_F32, CE_OP_MASKED_LOGITS, CE_OP_SCORE, CE_OP_TOP_TOKENS,
-                   CeError, check)
+from ._ffi import CE_BF16, CE_F32, CE_OP_MASKED_LOGITS, CE_OP_TOP_TOKENS, CeError, check
 
 __all__ = ["Head", "Graph", "CeError", "load_library"]
 
@@ -159,10 +158,8 @@ class Head:
         B = self._check_h(h)
         if out is None:
             out = torch.empty((B, self.Nc), dtype=torch.float32, device=self.device)
-        ws = self._workspace(B, 1, CE_OP_SCORE)
         check(self._lib.ce_score_centroids(self._handle, h.data_ptr(), B, out.data_ptr(),
-                                           ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
-              "ce_score_centroids")
+                                           _stream_handle(self.device)), "ce_score_centroids")
         return out
 
     def topk(self, scores, K: int, out=None):

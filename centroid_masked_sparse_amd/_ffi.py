@@ -36,7 +36,7 @@ SIGNATURES = {
     "ce_head_persistent_bytes": (_i32, [_vp, ctypes.POINTER(_sz)]),
     "ce_head_prepare": (_i32, [_vp, _vp, _sz, _vp]),
     "ce_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
-    "ce_score_centroids": (_i32, [_vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "ce_score_centroids": (_i32, [_vp, _vp, _i32, _vp, _vp]),
     "ce_topk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "ce_top_tokens": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "ce_masked_logits": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),

@@ -29,9 +29,8 @@ struct ce_head {
   std::vector<int32_t> tos;           // [V]
   std::vector<int32_t> tok_cluster;   // [V]
   std::vector<int32_t> tok_rank;      // [V]
+  std::vector<uint32_t> tiles;        // every 64-slot tile: (index in cluster << 13) | cluster
   std::vector<long long> cand_top;    // cand_top[K] = tokens owned by the K largest clusters
-  std::vector<long long> tiles_top;   // tiles_top[K] = tiles of the K clusters with most tiles
-  long long total_tiles = 0;
   bool prepared = false;
   ce::Tables tables{};
 };
@@ -64,9 +63,7 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
-  size_t state = 0, h64 = 0, scores = 0, topk = 0, cl_mask = 0, best = 0, items = 0,
-         rowpos = 0, logits = 0, total = 0;
-  int max_items = 0;
+  size_t scores = 0, topk = 0, cl_mask = 0, best = 0, rowpos = 0, logits = 0, total = 0;
   int ldL = 0;
 };
 
@@ -79,19 +76,14 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
     off = round_up(off + bytes, 256);
     return at;
   };
-  L.state = take(sizeof(ce::CallState));
-  L.h64 = take(nb * h->d * sizeof(double));
   if (op == CE_OP_SCORE) {
-    L.total = off;
+    L.total = 0;
     return L;
   }
   L.scores = take(nb * h->Nc * sizeof(float));
   L.topk = take(nb * (size_t)K * sizeof(int32_t));
   L.cl_mask = take((size_t)h->Nc * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
-  const long long items = std::min<long long>(h->total_tiles, (long long)nb * h->tiles_top[K]);
-  L.max_items = (int)items;
-  L.items = take((size_t)std::max<long long>(items, 1) * sizeof(uint32_t));
   if (op == CE_OP_MASKED_LOGITS) {
     L.rowpos = take(nb * h->Nc * sizeof(int32_t));
     L.ldL = (int)h->cand_top[K];
@@ -103,7 +95,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
 
 // Offsets of the four device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t offsets, tos, tok_cluster, tok_rank, total;
+  size_t offsets, tos, tok_cluster, tok_rank, tiles, et, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -118,6 +110,10 @@ PersistLayout persist_layout(const ce_head* h) {
   p.tos = take((size_t)h->V * sizeof(int32_t));
   p.tok_cluster = take((size_t)h->V * sizeof(int32_t));
   p.tok_rank = take((size_t)h->V * sizeof(int32_t));
+  p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
+  const size_t tile_bytes = (size_t)ce::kTileTokens * h->d * elem_bytes(h->dtype);
+  p.et = take(h->tiles.size() * tile_bytes);
+  p.ct = take((((size_t)h->Nc + ce::kTileTokens - 1) / ce::kTileTokens) * tile_bytes);
   p.total = off;
   return p;
 }
@@ -146,16 +142,12 @@ ce::PassArgs base_args(const ce_head* h, int K) {
 }
 
 void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
-  a.state = reinterpret_cast<ce::CallState*>(ws + L.state);
-  a.H64 = reinterpret_cast<double*>(ws + L.h64);
   a.S = reinterpret_cast<float*>(ws + L.scores);
   a.ldS = a.Nc;
   a.topk = reinterpret_cast<int32_t*>(ws + L.topk);
   a.ldK = a.K;
   a.cl_mask = reinterpret_cast<unsigned long long*>(ws + L.cl_mask);
   a.best = reinterpret_cast<unsigned long long*>(ws + L.best);
-  a.items = reinterpret_cast<uint32_t*>(ws + L.items);
-  a.max_items = L.max_items;
   a.rowpos = reinterpret_cast<int32_t*>(ws + L.rowpos);
   a.L = reinterpret_cast<float*>(ws + L.logits);
   a.ldL = L.ldL;
@@ -199,13 +191,11 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.probe_start = pstart;
       a.probe_stop = pstop;
     }
-    hipError_t e = ce::launch_prep(a, stream);
-    if (e == hipSuccess) e = ce::launch_scores(a, stream);
-    if (e == hipSuccess)
-      e = ce::launch_topk(a, op == CE_OP_MASKED_LOGITS ? ce::kTopkPlanRowpos : ce::kTopkPlan, stream);
-    if (e == hipSuccess)
-      e = ce::launch_gather(a, op == CE_OP_MASKED_LOGITS ? ce::kMasked : ce::kArgmax, stream);
-    if (e == hipSuccess && op == CE_OP_MASKED_LOGITS) e = ce::launch_writer(a, stream);
+    const bool masked = op == CE_OP_MASKED_LOGITS;
+    hipError_t e = ce::launch_scores(a, stream);
+    if (e == hipSuccess) e = ce::launch_topk(a, masked ? ce::kTopkMarkRowpos : ce::kTopkMark, stream);
+    if (e == hipSuccess) e = ce::launch_gather(a, masked ? ce::kMasked : ce::kArgmax, stream);
+    if (e == hipSuccess) e = masked ? ce::launch_writer(a, stream) : ce::launch_finalize(a, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
   }
   return CE_SUCCESS;
@@ -274,24 +264,20 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
         h->tok_rank[t] = j - h->offsets[c];
       }
     }
-    std::vector<long long> sizes(Nc), tiles(Nc);
+    std::vector<long long> sizes(Nc);
     for (int c = 0; c < Nc; ++c) {
       sizes[c] = h->offsets[c + 1] - h->offsets[c];
-      tiles[c] = (sizes[c] + ce::kTileTokens - 1) / ce::kTileTokens;
-      if (tiles[c] > ce::kMaxTilesPerCluster) {
+      const long long nt = (sizes[c] + ce::kTileTokens - 1) / ce::kTileTokens;
+      if (nt > ce::kMaxTilesPerCluster) {
         delete h;
         return fail(CE_ERR_UNSUPPORTED, "a cluster holds more than 2^19 * 64 tokens");
       }
+      for (long long q = 0; q < nt; ++q)
+        h->tiles.push_back(((uint32_t)q << ce::kTileShift) | (uint32_t)c);
     }
     std::sort(sizes.begin(), sizes.end(), std::greater<long long>());
-    std::sort(tiles.begin(), tiles.end(), std::greater<long long>());
     h->cand_top.assign((size_t)Nc + 1, 0);
-    h->tiles_top.assign((size_t)Nc + 1, 0);
-    for (int k = 0; k < Nc; ++k) {
-      h->cand_top[k + 1] = h->cand_top[k] + sizes[k];
-      h->tiles_top[k + 1] = h->tiles_top[k] + tiles[k];
-    }
-    h->total_tiles = h->tiles_top[Nc];
+    for (int k = 0; k < Nc; ++k) h->cand_top[k + 1] = h->cand_top[k] + sizes[k];
   } catch (const std::bad_alloc&) {
     delete h;
     return fail(CE_ERR_UNSUPPORTED, "out of host memory");
@@ -327,12 +313,30 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
                                   hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
   }
-  hipError_t e = hipStreamSynchronize(stream);
+  if (!head->tiles.empty()) {
+    hipError_t e = hipMemcpyAsync(base + p.tiles, head->tiles.data(), head->tiles.size() * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
+  }
+  hipError_t e = ce::launch_pack(head->E, head->dtype, head->d, (long)head->tiles.size(),
+                                 reinterpret_cast<const uint32_t*>(base + p.tiles),
+                                 reinterpret_cast<const int32_t*>(base + p.offsets), head->V,
+                                 base + p.et, stream);
+  if (e == hipSuccess)
+    e = ce::launch_pack(head->C, head->dtype, head->d,
+                        ((long)head->Nc + ce::kTileTokens - 1) / ce::kTileTokens, nullptr, nullptr,
+                        head->Nc, base + p.ct, stream);
+  if (e != hipSuccess) return fail_hip(e, "pack kernel launch");
+  e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
   head->tables.offsets = reinterpret_cast<const int32_t*>(base + p.offsets);
   head->tables.tos = reinterpret_cast<const int32_t*>(base + p.tos);
   head->tables.tok_cluster = reinterpret_cast<const int32_t*>(base + p.tok_cluster);
   head->tables.tok_rank = reinterpret_cast<const int32_t*>(base + p.tok_rank);
+  head->tables.tiles = reinterpret_cast<const uint32_t*>(base + p.tiles);
+  head->tables.n_tiles = (int)head->tiles.size();
+  head->tables.ET = base + p.et;
+  head->tables.CT = base + p.ct;
   head->prepared = true;
   return CE_SUCCESS;
 }
@@ -350,30 +354,22 @@ ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op, s
   return CE_SUCCESS;
 }
 
-ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* scores, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* scores,
+                             hipStream_t stream) {
   ce_status st = check_call(head, h, B, 1, false);
   if (st != CE_SUCCESS) return st;
   if (B == 0) return CE_SUCCESS;
-  if (!scores || !ws) return fail(CE_ERR_NULL_POINTER, "scores or workspace is NULL");
-  if (!aligned(h, 16) || !aligned(scores, 4) || !aligned(ws, 256))
-    return fail(CE_ERR_MISALIGNED, "h needs 16-byte, ws 256-byte alignment");
-  const Layout L = make_layout(head, B, 1, CE_OP_SCORE);
-  if (ws_bytes < L.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than ce_workspace_bytes");
-  const size_t in_row = (size_t)head->d * elem_bytes(head->dtype);
+  if (!scores) return fail(CE_ERR_NULL_POINTER, "scores is NULL");
+  if (!aligned(h, 16) || !aligned(scores, 4)) return fail(CE_ERR_MISALIGNED, "h needs 16-byte alignment");
   for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
     ce::PassArgs a = base_args(head, 1);
     a.B = std::min(ce::kPassRows, B - b0);
-    a.h = static_cast<const char*>(h) + (size_t)b0 * in_row;
-    char* w = static_cast<char*>(ws);
-    a.state = reinterpret_cast<ce::CallState*>(w + L.state);
-    a.H64 = reinterpret_cast<double*>(w + L.h64);
-    a.cl_mask = nullptr;  // prep then clears only the call state
+    a.h = static_cast<const char*>(h) + (size_t)b0 * (size_t)head->d * elem_bytes(head->dtype);
+    a.cl_mask = nullptr;  // no selection follows: nothing to clear
     a.best = nullptr;
     a.S = scores + (size_t)b0 * head->Nc;
     a.ldS = head->Nc;
-    hipError_t e = ce::launch_prep(a, stream);
-    if (e == hipSuccess) e = ce::launch_scores(a, stream);
+    hipError_t e = ce::launch_scores(a, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
   }
   return CE_SUCCESS;

@@ -11,16 +11,9 @@ namespace ce {
 constexpr int kPassRows = 64;     // rows per internal pass: row sets are 64-bit masks
 constexpr int kTileTokens = 64;   // candidate tokens per gather work item (one per lane)
 constexpr int kMaxNc = 8192;      // centroid id fits the low 13 bits of a work item
-constexpr int kItemShift = 13;
-constexpr int kMaxTilesPerCluster = 1 << (32 - kItemShift);
+constexpr int kTileShift = 13;     // tile word: (tile index in cluster << 13) | cluster
+constexpr int kMaxTilesPerCluster = 1 << (32 - kTileShift);
 constexpr int kMaxD = 8192;
-
-// Per-call counters, cleared by the first kernel of every pass.
-struct CallState {
-  uint32_t n_items;      // gather work items appended by the top-K kernel
-  uint32_t done_items;   // gather work items finished (argmax completion ticket)
-  uint32_t pad[62];      // 256 bytes
-};
 
 // Device tables uploaded at prepare time.
 struct Tables {
@@ -28,10 +21,14 @@ struct Tables {
   const int32_t* tos;          // [V] token id of each slot
   const int32_t* tok_cluster;  // [V] cluster owning each token
   const int32_t* tok_rank;     // [V] slot of each token minus its cluster's first slot
+  const uint32_t* tiles;       // [n_tiles] every 64-slot tile of every cluster, cluster-major
+  int n_tiles;
+  const void* ET;              // packed embeddings: [n_tiles][d/vec][64] 16-byte vectors
+  const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
 };
 
 enum GatherMode { kArgmax = 0, kMasked = 1 };
-enum TopkMode { kTopkOnly = 0, kTopkPlan = 1, kTopkPlanRowpos = 2 };
+enum TopkMode { kTopkOnly = 0, kTopkMark = 1, kTopkMarkRowpos = 2 };
 
 // Everything one pass (at most kPassRows rows) needs.
 struct PassArgs {
@@ -43,16 +40,12 @@ struct PassArgs {
   Tables t;
   const void* h;          // [B][d] rows of this pass
   // workspace regions
-  CallState* state;
-  double* H64;            // [B][d] hidden rows widened to float64
   float* S;               // [B][ldS] centroid scores
   int ldS;
   int32_t* topk;          // [B][ldK] selected centroids
   int ldK;
   unsigned long long* cl_mask;  // [Nc] rows that selected each centroid
   unsigned long long* best;     // [kPassRows] packed (ordered logit, ~token)
-  uint32_t* items;              // [max_items] (tile << 13) | centroid
-  int max_items;
   int32_t* rowpos;        // [B][Nc] first candidate position of a centroid in a row, or -1
   float* L;               // [B][ldL] candidate logits in row order
   int ldL;
@@ -64,10 +57,13 @@ struct PassArgs {
   hipEvent_t probe_stop;
 };
 
-hipError_t launch_prep(const PassArgs& a, hipStream_t s);
+// Pack rows of W into 64-row tiles [t][v][lane] (see ce_kernels.hip).
+hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint32_t* tiles,
+                       const int32_t* offsets, int nrows_total, void* out, hipStream_t s);
 hipError_t launch_scores(const PassArgs& a, hipStream_t s);
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
+hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
 hipError_t launch_writer(const PassArgs& a, hipStream_t s);
 
 }  // namespace ce

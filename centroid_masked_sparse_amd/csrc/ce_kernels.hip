@@ -7,26 +7,40 @@
 // then a greedy argmax (get_top_tokens) or a full-vocabulary row filled with
 // -inf outside the candidates (forward).
 //
+// Packed weights.  At prepare time the centroid rows and the ordered
+// embedding rows are packed in tiles of 64 rows (a cluster's slots never
+// share a tile with another cluster): tile t stores, for every 16-byte vector
+// v of a row, the vectors of its 64 rows side by side, [t][v][lane].  Lane l
+// of a wave then reads its own row's next 8 bf16 (or 4 fp32) elements while
+// the wave reads 1 KiB of contiguous memory, so slabs stream from HBM straight
+// into registers, fully coalesced, and LDS only carries the hidden rows.
+//
 // One pass handles at most 64 rows and runs these kernels in stream order:
-//   prep     widen h to float64, clear the per-call counters and row masks
-//   scores   centroid projection S[b][c] (canonical dot, see below)
+//   scores   centroid projection S[b][c] (canonical dot, see below); also
+//            clears the per-centroid row masks and the argmax slots
 //   topk     one workgroup per row: radix select of the K best centroids; the
-//            first row to claim a centroid appends its 64-token tiles to the
-//            gather work list (cross-row dedup: each tile is read once)
-//   gather   one wave per 64-token tile: stage the tile through LDS once, dot
-//            every row that selected its centroid, then either reduce to a
-//            per-row packed argmax with a 64-bit atomicMax (the last tile to
-//            finish writes the token ids) or store the candidate logits
-//   writer   (forward only) one coalesced pass over [B][V]: -inf or the
-//            candidate logit of each token
+//            row's bit is or-ed into the mask of every centroid it selected
+//   gather   one wave per 64-token tile of the static tile list; a tile whose
+//            centroid no row selected exits at once, so each selected slab is
+//            read exactly once however many rows share it (cross-row dedup).
+//            The tile is dotted with every row in its mask, then reduced to a
+//            per-row packed argmax (64-bit atomicMax) or stored as candidate
+//            logits
+//   finalize (get_top_tokens) decode the packed argmax into token ids
+//   writer   (forward) one coalesced pass over [B][V]: -inf or the candidate
+//            logit of each token
+//
+// No kernel waits on another workgroup and none uses a device-scope fence:
+// on a multi-XCD part such a fence writes back the L2, so results travel
+// between steps only through kernel boundaries and fire-and-forget atomics.
 //
 // Canonical dot: every product is formed exactly in float64 and summed in
 // hidden-dimension order from +0.0 by a chain of v_fmac_f64 (one rounding per
 // step), then rounded to fp32 nearest-even with -0 mapped to +0.  Each lane
 // owns whole chains (one per output), so no reduction tree reorders a sum and
 // the results equal a sequential float64 loop bit for bit.  The hidden rows are
-// wave-uniform operands: they are read as float64 through the scalar cache
-// (address space 4) and fed to v_fmac_f64 as SGPR pairs.
+// wave-uniform operands: each 64-dim chunk is widened to float64 into LDS and
+// read back as broadcasts.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -34,21 +48,21 @@
 
 #include "ce_internal.h"
 
+// Wavefront reductions of the ROCm device library (DPP based).
+extern "C" __device__ unsigned int __ockl_wfred_add_u32(unsigned int);
+extern "C" __device__ unsigned long long __ockl_wfred_max_u64(unsigned long long);
+
 namespace ce {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kChunk = 64;   // hidden dims staged through LDS per step
-
-typedef const __attribute__((address_space(4))) double cdouble_t;
+constexpr int kChunk = 64;       // hidden dims per LDS step
+constexpr int kGatherRows = 4;   // hidden rows dotted per pass over a gather tile
 
 // 16 bytes as a native vector (HIP's uint4 wraps a union, which keeps arrays
 // of it out of registers).
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-// View of read-only float64 data as the constant address space, so that
-// wave-uniform reads become scalar loads.
-__device__ __forceinline__ cdouble_t* as_const(const double* p) { return (cdouble_t*)p; }
+typedef double v2d __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Elem;
 template <> struct Elem<float> { static constexpr int kPerVec = 4; };      // fp32
@@ -67,11 +81,6 @@ __device__ __forceinline__ void widen(const v4u v, double (&x)[8], uint16_t) {
   }
 }
 
-__device__ __forceinline__ double widen1(float v) { return (double)v; }
-__device__ __forceinline__ double widen1(uint16_t v) {
-  return (double)__uint_as_float((uint32_t)v << 16);
-}
-
 // float64 sum -> fp32 nearest-even, -0 -> +0.
 __device__ __forceinline__ float canon(double s) {
   uint32_t u = __float_as_uint((float)s);
@@ -85,118 +94,180 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <typename T>
-struct TileGeom {
+// ------------------------------------------------------------------ packing
+
+// Pack rows of W ([rows][d] row-major) into 64-row tiles [t][v][lane].
+// With `tiles` (the cluster tile list) tile t covers the slots of one
+// cluster's 64-slot tile; without it, tile t covers rows [64t, 64t+64) of
+// `nrows_total`.  Lanes past a tile's last row are zero.
+__global__ __launch_bounds__(256) void pack_kernel(const v4u* __restrict__ W, int nvec, long n_out,
+                                                   const uint32_t* __restrict__ tiles,
+                                                   const int32_t* __restrict__ offsets,
+                                                   int nrows_total, v4u* __restrict__ out) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < n_out; o += stride) {
+    const int lane = (int)(o % kTileTokens);
+    const long tv = o / kTileTokens;
+    const int v = (int)(tv % nvec);
+    const long t = tv / nvec;
+    long start, end;
+    if (tiles) {
+      const uint32_t w = tiles[t];
+      const int c = (int)(w & ((1u << kTileShift) - 1u));
+      start = (long)offsets[c] + (long)(w >> kTileShift) * kTileTokens;
+      end = offsets[c + 1];
+    } else {
+      start = t * kTileTokens;
+      end = nrows_total;
+    }
+    const long row = start + lane;
+    v4u val = {0u, 0u, 0u, 0u};
+    if (row < end) val = W[row * nvec + v];
+    out[o] = val;
+  }
+}
+
+// ------------------------------------------------------------------ dot tile
+
+template <typename T, int RB>
+struct HStage {
   static constexpr int kPerVec = Elem<T>::kPerVec;
-  static constexpr int kVecPerTok = kChunk / kPerVec;      // 16-byte vectors per token per chunk
-  static constexpr int kTokStep = kWave / kVecPerTok;      // tokens covered by one wave load
-  static constexpr int kLoads = kVecPerTok;                // loads per lane per chunk
-  static constexpr int kPitch = kVecPerTok + 1;            // LDS row pitch in 16-byte units (+16 B pad)
-  static constexpr int kLdsVecs = kTileTokens * kPitch;
+  static constexpr int kVecPerRow = kChunk / kPerVec;                 // raw 16-B vectors per row chunk
+  static constexpr int kLoads = (RB * kVecPerRow + kWave - 1) / kWave;
+  static constexpr int kV2PerRow = kChunk / 2;                        // v2d per row chunk in LDS
 };
 
-// Dot 64 consecutive rows of W ([*, d] row-major) starting at row j0 (rows
-// >= nvalid are clamped to nvalid-1 and their results must be ignored) with
-// up to RB hidden rows hrow[0..nrows) (float64, scalar-cache reads).  Lane t
-// ends with acc[r] = the float64 chain for (row j0+t, hidden row r).
+// Dot one packed 64-row tile `wt` ([d/kPerVec][64] vectors; rows >= nvalid
+// are not read and their results must be ignored) with the hidden rows
+// h[rows[r]] for r < nrows ([*][d] of T).  Lane t ends with acc[r] = the
+// float64 chain of (tile row t, hidden row rows[r]).
 //
-// Each chunk of 64 dims is read from HBM with fully coalesced 16-byte loads
-// (8 tokens x 128 B per wave instruction for bf16), written to LDS with a
-// 16-byte pad per token row so that the per-lane row reads are bank-conflict
-// free, and the next chunk's loads are in flight while this one is consumed.
+// Per chunk of 64 dims each lane loads its row's vectors (one 1 KiB
+// coalesced wave load per vector) one chunk ahead of use, and the wave widens
+// the chunk of its hidden rows to float64 into a double-buffered LDS slot.
 template <typename T, int RB>
-__device__ __forceinline__ void dot_tile(const T* __restrict__ W, long j0, int nvalid, int d,
-                                         cdouble_t* const (&hrow)[RB], int nrows,
-                                         double (&acc)[RB], v4u* lds) {
-  using G = TileGeom<T>;
+__device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid, int d,
+                                         const T* __restrict__ h, const int (&rows)[RB], int nrows,
+                                         double (&acc)[RB], v2d (&lds)[2][RB * kChunk / 2]) {
+  constexpr int PV = Elem<T>::kPerVec;
+  constexpr int VPC = kChunk / PV;              // weight vectors per chunk
+  using HS = HStage<T, RB>;
   const int lane = threadIdx.x;
-  const int part = lane % G::kVecPerTok;
-  const int tok0 = lane / G::kVecPerTok;
+  const bool wvalid = lane < nvalid;
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = 0.0;
 
-  const v4u* src[G::kLoads];
+  // hidden-row raw loads: vector hv = lane + 64 i covers row hv / kVecPerRow
+  const char* hbase = reinterpret_cast<const char*>(h);
+  uint32_t hoff[HS::kLoads];
+  bool hval[HS::kLoads];
+  int hslot[HS::kLoads];
 #pragma unroll
-  for (int i = 0; i < G::kLoads; ++i) {
-    int tok = tok0 + i * G::kTokStep;
-    tok = tok < nvalid ? tok : nvalid - 1;
-    src[i] = reinterpret_cast<const v4u*>(W + (j0 + tok) * (long)d) + part;
+  for (int i = 0; i < HS::kLoads; ++i) {
+    const int hv = lane + kWave * i;
+    const int r = hv / HS::kVecPerRow;
+    const int part = hv % HS::kVecPerRow;
+    int row = rows[0];
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+      if (q == r) row = rows[q];
+    hval[i] = r < nrows;
+    hoff[i] = ((uint32_t)row * (uint32_t)d + (uint32_t)part * PV) * sizeof(T);
+    hslot[i] = r * HS::kV2PerRow + part * (PV / 2);
   }
-  v4u buf[G::kLoads];
-#pragma unroll
-  for (int i = 0; i < G::kLoads; ++i) buf[i] = src[i][0];
 
-  // consume the chunk staged in LDS: dims [kc, kc + kChunk)
-  auto consume = [&](int kc) {
+  struct Stage {
+    v4u e[VPC];
+    v4u h[HS::kLoads];
+  };
+  auto load = [&](Stage& st, int ch) {
 #pragma unroll
-    for (int p = 0; p < G::kVecPerTok; ++p) {
-      const v4u v = lds[lane * G::kPitch + p];
-      double x[G::kPerVec];
-      widen(v, x, T());
+    for (int p = 0; p < VPC; ++p)
+      if (wvalid) st.e[p] = wt[(ch * VPC + p) * kWave + lane];
+    const uint32_t hadv = (uint32_t)ch * (kChunk * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < HS::kLoads; ++i)
+      if (hval[i]) st.h[i] = *reinterpret_cast<const v4u*>(hbase + hoff[i] + hadv);
+  };
+  auto park = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < HS::kLoads; ++i)
+      if (hval[i]) {
+        double x[PV];
+        widen(st.h[i], x, T());
+#pragma unroll
+        for (int j = 0; j < PV / 2; ++j) lds[buf][hslot[i] + j] = v2d{x[2 * j], x[2 * j + 1]};
+      }
+  };
+  auto consume = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int p = 0; p < VPC; ++p) {
+      double x[PV];
+      widen(st.e[p], x, T());
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         if (r < nrows) {
-          cdouble_t* hp = hrow[r] + kc + p * G::kPerVec;
 #pragma unroll
-          for (int i = 0; i < G::kPerVec; ++i) acc[r] = __builtin_fma(x[i], hp[i], acc[r]);
+          for (int q = 0; q < PV / 2; ++q) {
+            const v2d hv = lds[buf][r * HS::kV2PerRow + p * (PV / 2) + q];
+            acc[r] = __builtin_fma(x[2 * q], hv.x, acc[r]);
+            acc[r] = __builtin_fma(x[2 * q + 1], hv.y, acc[r]);
+          }
         }
       }
     }
   };
 
-  const int last = d / kChunk - 1;
-  for (int ch = 0; ch < last; ++ch) {
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) lds[(tok0 + i * G::kTokStep) * G::kPitch + part] = buf[i];
+  // Two register stages: while one chunk is consumed the other is in flight;
+  // a stage is reloaded only after its weights have been consumed.  One wave
+  // per workgroup: the barrier orders this wave's LDS writes before its
+  // reads; the other LDS buffer is rewritten only after a later barrier.
+  const int nch = d / kChunk;
+  Stage s0, s1;
+  load(s0, 0);
+  if (nch > 1) load(s1, 1);
+  for (int ch = 0; ch < nch; ch += 2) {
+    park(s0, 0);
     __syncthreads();
-    const int adv = (ch + 1) * (kChunk / G::kPerVec);
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) buf[i] = src[i][adv];   // next chunk in flight
-    consume(ch * kChunk);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < G::kLoads; ++i) lds[(tok0 + i * G::kTokStep) * G::kPitch + part] = buf[i];
-  __syncthreads();
-  consume(last * kChunk);
-  __syncthreads();
-}
-
-// ------------------------------------------------------------------ prep
-
-template <typename T>
-__global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ h, int n, double* H64,
-                                                   int Nc, unsigned long long* cl_mask,
-                                                   unsigned long long* best, CallState* st) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int stride = gridDim.x * blockDim.x;
-  for (int k = i; k < n; k += stride) H64[k] = widen1(h[k]);
-  if (cl_mask)
-    for (int k = i; k < Nc; k += stride) cl_mask[k] = 0ull;
-  if (i < kPassRows) {
-    if (best) best[i] = 0ull;
-    reinterpret_cast<uint32_t*>(st)[i] = 0u;
+    consume(s0, 0);
+    if (ch + 2 < nch) load(s0, ch + 2);
+    if (ch + 1 < nch) {
+      park(s1, 1);
+      __syncthreads();
+      consume(s1, 1);
+      if (ch + 3 < nch) load(s1, ch + 3);
+    }
   }
 }
 
 // ------------------------------------------------------------------ scores
 
+// One wave per (64-centroid tile, RB rows).  Also clears the row masks and
+// argmax slots of the pass (when given), before the top-K kernel runs.
 template <typename T, int RB>
-__global__ __launch_bounds__(64) void scores_kernel(const T* __restrict__ C, int Nc, int d,
-                                                    const double* __restrict__ H64, int B,
-                                                    float* __restrict__ S, int ldS) {
-  __shared__ v4u lds[TileGeom<T>::kLdsVecs];
+__global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, int Nc, int d,
+                                                    const T* __restrict__ h, int B,
+                                                    float* __restrict__ S, int ldS,
+                                                    unsigned long long* __restrict__ cl_mask,
+                                                    unsigned long long* __restrict__ best) {
+  __shared__ v2d lds[2][RB * kChunk / 2];
+  const int lane = threadIdx.x;
+  if (cl_mask) {
+    const int w = blockIdx.y * gridDim.x + blockIdx.x;
+    const int nw = gridDim.x * gridDim.y;
+    for (int k = w * kWave + lane; k < Nc; k += nw * kWave) cl_mask[k] = 0ull;
+    if (w == 0) best[lane] = 0ull;
+  }
   const int c0 = blockIdx.x * kTileTokens;
   const int r0 = blockIdx.y * RB;
   const int nvalid = min(kTileTokens, Nc - c0);
   const int nrows = min(RB, B - r0);
-  cdouble_t* hrow[RB];
+  int rows[RB];
 #pragma unroll
-  for (int r = 0; r < RB; ++r)
-    hrow[r] = as_const(H64 + (long)(r0 + (r < nrows ? r : nrows - 1)) * d);
+  for (int r = 0; r < RB; ++r) rows[r] = r0 + (r < nrows ? r : nrows - 1);
   double acc[RB];
-  dot_tile<T, RB>(C, c0, nvalid, d, hrow, nrows, acc, lds);
-  const int lane = threadIdx.x;
+  const long tile_vecs = (long)(d / Elem<T>::kPerVec) * kWave;
+  dot_tile<T, RB>(CT + blockIdx.x * tile_vecs, nvalid, d, h, rows, nrows, acc, lds);
   if (lane < nvalid) {
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -237,114 +308,96 @@ struct TopkArgs {
   int ldS, Nc, K;
   int32_t* out;
   int ldK;
-  int b_base;                      // row index offset into cl_mask bit positions (0)
   const int32_t* offsets;
   unsigned long long* cl_mask;
-  uint32_t* items;
-  CallState* st;
   int32_t* rowpos;
 };
 
 // One workgroup per row.  Thread t holds centroids [t*EPT, t*EPT+EPT), so
-// thread order is id order.  MSB-first radix select over 8-bit digits finds
-// the exact K-th largest key tau and how many keys equal to tau to keep; the
-// kept ties are the lowest ids.  The result is written in ascending id order.
+// thread order is id order.  Bit-serial radix select, most significant bit
+// first, over order-preserving keys: `alive` marks keys still tied with the
+// K-th largest on the bits seen so far; at each bit, if the alive keys with a
+// 1 there number at most kk they are all kept (and kk shrinks), else the
+// search continues among them.  Counting needs no atomics: a per-lane
+// popcount, a DPP wave reduction and one barrier per bit (partial sums are
+// double-buffered by bit parity).  The loop stops as soon as exactly K keys
+// are kept; keys still alive after 32 bits are equal, and the lowest ids
+// among them are kept.
 template <int EPT, int MODE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   static_assert(EPT <= 32, "selection mask is 32 bits");
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t part[2][kTopkThreads / kWave];
   __shared__ uint32_t scan_sh[kTopkThreads / kWave];
-  __shared__ uint32_t sel_digit, sel_kk;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
   const int Nc = a.Nc;
   const float* row = a.S + (long)b * a.ldS;
 
   uint32_t key[EPT];
+  uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const int c = tid * EPT + i;
     key[i] = c < Nc ? order_key(row[c]) : 0u;
+    valid |= (c < Nc ? 1u : 0u) << i;
   }
 
-  uint32_t prefix = 0, pmask = 0, kk = (uint32_t)a.K;
-  const bool take_all = a.K >= Nc;
-  if (!take_all) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0u;
-      __syncthreads();
+  uint32_t sel = 0, alive = valid, kk = (uint32_t)a.K;
+  if (a.K >= Nc) {
+    sel = valid;
+    alive = 0;
+    kk = 0;
+  }
+  for (int bit = 31; bit >= 0 && kk > 0; --bit) {
+    uint32_t ones = 0;
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const int c = tid * EPT + i;
-        if (c < Nc && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // thread t looks at digit 255-t: excl = keys with a larger digit
-      const uint32_t v = hist[255 - tid];
-      uint32_t tot;
-      const uint32_t excl = block_excl_scan(v, scan_sh, &tot);
-      if (excl < kk && excl + v >= kk) {
-        sel_digit = 255u - (uint32_t)tid;
-        sel_kk = kk - excl;
-      }
-      __syncthreads();
-      prefix |= sel_digit << shift;
-      pmask |= 0xFFu << shift;
-      kk = sel_kk;
+    for (int i = 0; i < EPT; ++i) ones |= ((key[i] >> bit) & 1u) << i;
+    ones &= alive;
+    const uint32_t wsum = __ockl_wfred_add_u32((uint32_t)__popc(ones));
+    if (lane == 0) part[bit & 1][wv] = wsum;
+    __syncthreads();
+    uint32_t total = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkThreads / kWave; ++i) total += part[bit & 1][i];
+    if (total <= kk) {
+      sel |= ones;
+      alive &= ~ones;
+      kk -= total;
+    } else {
+      alive = ones;
     }
   }
-  const uint32_t tau = prefix;
-
-  // tie ranks in id order
-  uint32_t n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int c = tid * EPT + i;
-    n_eq += (c < Nc && key[i] == tau) ? 1u : 0u;
-  }
+  // keys still alive are all equal: keep the kk lowest ids among them
   uint32_t tot;
-  uint32_t eq_seen = block_excl_scan(n_eq, scan_sh, &tot);
-  uint32_t selmask = 0;
+  const uint32_t eq_before = block_excl_scan((uint32_t)__popc(alive), scan_sh, &tot);
+  if (kk > 0) {
+    uint32_t seen = eq_before;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int c = tid * EPT + i;
-    bool s = false;
-    if (c < Nc) {
-      if (take_all || key[i] > tau) {
-        s = true;
-      } else if (key[i] == tau) {
-        s = eq_seen < kk;
-        ++eq_seen;
+    for (int i = 0; i < EPT; ++i)
+      if (alive & (1u << i)) {
+        if (seen < kk) sel |= 1u << i;
+        ++seen;
       }
-    }
-    selmask |= (s ? 1u : 0u) << i;
   }
+  const uint32_t selmask = sel;
   uint32_t pos = block_excl_scan((uint32_t)__popc(selmask), scan_sh, &tot);
   int32_t* out = a.out + (long)b * a.ldK;
 #pragma unroll
   for (int i = 0; i < EPT; ++i)
     if (selmask & (1u << i)) out[pos++] = tid * EPT + i;
 
-  if (MODE >= kTopkPlan) {
+  if (MODE >= kTopkMark) {
+    // no return value is used, so these atomics do not stall the wave
     const unsigned long long bit = 1ull << b;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      if (selmask & (1u << i)) {
-        const int c = tid * EPT + i;
-        const unsigned long long old = atomicOr(&a.cl_mask[c], bit);
-        if (old == 0ull) {
-          const int n = a.offsets[c + 1] - a.offsets[c];
-          const uint32_t nt = (uint32_t)((n + kTileTokens - 1) / kTileTokens);
-          if (nt) {
-            const uint32_t base = atomicAdd(&a.st->n_items, nt);
-            for (uint32_t q = 0; q < nt; ++q)
-              a.items[base + q] = (q << kItemShift) | (uint32_t)c;
-          }
-        }
-      }
-    }
+    for (int i = 0; i < EPT; ++i)
+      if (selmask & (1u << i))
+        __hip_atomic_fetch_or(&a.cl_mask[tid * EPT + i], bit, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (MODE == kTopkPlanRowpos) {
+  if (MODE == kTopkMarkRowpos) {
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
@@ -372,51 +425,38 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 // ------------------------------------------------------------------ gather
 
 struct GatherArgs {
-  const void* E;
-  int d, Nc, B;
+  const v4u* ET;
+  const void* h;
+  int d, Nc;
   const int32_t* offsets;
   const int32_t* tos;
-  const double* H64;
   const unsigned long long* cl_mask;
-  const uint32_t* items;
-  CallState* st;
+  const uint32_t* tiles;
   unsigned long long* best;
-  int32_t* tokens;
   const int32_t* rowpos;
   float* L;
   int ldL;
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const unsigned long long w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  return __ockl_wfred_max_u64(v);
 }
 
 template <typename T, int RB, int MODE>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
-  __shared__ v4u lds[TileGeom<T>::kLdsVecs];
+  __shared__ v2d lds[2][RB * kChunk / 2];
   const int lane = threadIdx.x;
-  const uint32_t n_items = a.st->n_items;
-  const uint32_t it = blockIdx.x;
-  if (it >= n_items) {
-    if (MODE == kArgmax && it == 0) {
-      // no work at all: every row's selected centroids are empty
-      for (int b = lane; b < a.B; b += kWave) a.tokens[b] = -1;
-    }
-    return;
-  }
-  const uint32_t item = a.items[it];
-  const int c = (int)(item & ((1u << kItemShift) - 1u));
-  const int q = (int)(item >> kItemShift);
+  const uint32_t tile = a.tiles[blockIdx.x];
+  const int c = (int)(tile & ((1u << kTileShift) - 1u));
+  unsigned long long mask = a.cl_mask[c];
+  if (!mask) return;   // no row selected this centroid
+  const int q = (int)(tile >> kTileShift);
   const long j0 = (long)a.offsets[c] + (long)q * kTileTokens;
   const int nvalid = (int)min((long)kTileTokens, (long)a.offsets[c + 1] - j0);
-  const int tok = lane < nvalid ? a.tos[j0 + lane] : 0;
-  unsigned long long mask = a.cl_mask[c];
-  const T* E = reinterpret_cast<const T*>(a.E);
+  const int tok = (MODE == kArgmax && lane < nvalid) ? a.tos[j0 + lane] : 0;
+  const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
+  const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
+  const T* h = reinterpret_cast<const T*>(a.h);
 
   while (mask) {
     int rows[RB];
@@ -431,11 +471,8 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
         rows[r] = rows[0];
       }
     }
-    cdouble_t* hrow[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) hrow[r] = as_const(a.H64 + (long)rows[r] * a.d);
     double acc[RB];
-    dot_tile<T, RB>(E, j0, nvalid, a.d, hrow, nrows, acc, lds);
+    dot_tile<T, RB>(wt, nvalid, a.d, h, rows, nrows, acc, lds);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (r < nrows) {
@@ -445,7 +482,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
           if (lane < nvalid)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           k = wave_max_u64(k);
-          if (lane == 0) atomicMax(&a.best[rows[r]], k);
+          if (lane == 0) atomicMax(&a.best[rows[r]], k);   // result unused: no stall
         } else {
           if (lane < nvalid) {
             const int p = a.rowpos[(long)rows[r] * a.Nc + c];
@@ -454,22 +491,18 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
         }
       }
     }
+    __syncthreads();   // the next pass reuses the LDS buffers
   }
+}
 
-  if (MODE == kArgmax) {
-    // completion ticket: the last item to finish decodes every row's winner
-    __threadfence();
-    uint32_t ticket = 0;
-    if (lane == 0) ticket = atomicAdd(&a.st->done_items, 1u);
-    ticket = __shfl(ticket, 0, kWave);
-    if (ticket == n_items - 1u) {
-      __threadfence();
-      for (int b = lane; b < a.B; b += kWave) {
-        const unsigned long long v =
-            __hip_atomic_load(&a.best[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.tokens[b] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
-      }
-    }
+// Decode each row's packed (ordered logit, ~token) maximum; 0 means no
+// candidate at all.
+__global__ __launch_bounds__(64) void finalize_kernel(const unsigned long long* __restrict__ best,
+                                                      int B, int32_t* __restrict__ tokens) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    const unsigned long long v = best[b];
+    tokens[b] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
   }
 }
 
@@ -518,33 +551,33 @@ __global__ __launch_bounds__(256) void writer_kernel(float* __restrict__ out, in
   }
 }
 
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_prep(const PassArgs& a, hipStream_t s) {
-  const int n = a.B * a.d;
-  const int work = n > a.Nc ? n : a.Nc;
-  int blocks = (work + 255) / 256;
-  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(prep_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.h), n, a.H64, a.Nc, a.cl_mask, a.best, a.state);
-  else
-    hipLaunchKernelGGL(prep_kernel<float>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const float*>(a.h), n, a.H64, a.Nc, a.cl_mask, a.best, a.state);
+hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint32_t* tiles,
+                       const int32_t* offsets, int nrows_total, void* out, hipStream_t s) {
+  const int nvec = d / (dtype == 1 ? Elem<uint16_t>::kPerVec : Elem<float>::kPerVec);
+  const long n_out = n_tiles * nvec * kTileTokens;
+  if (n_out == 0) return hipSuccess;
+  long blocks = (n_out + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const v4u*>(W), nvec, n_out, tiles, offsets, nrows_total,
+                     static_cast<v4u*>(out));
   return hipGetLastError();
 }
 
 template <typename T, int RB>
 static void launch_scores_t(const PassArgs& a, hipStream_t s) {
   const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
-  hipLaunchKernelGGL((scores_kernel<T, RB>), grid, dim3(64), 0, s, static_cast<const T*>(a.C),
-                     a.Nc, a.d, a.H64, a.B, a.S, a.ldS);
+  hipLaunchKernelGGL((scores_kernel<T, RB>), grid, dim3(64), 0, s,
+                     static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
+                     a.S, a.ldS, a.cl_mask, a.best);
 }
 
 hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
-  // two rows per wave once there are enough rows to keep the chip busy
   const bool two = a.B >= 2;
   if (a.dtype == 1) {
     if (two) launch_scores_t<uint16_t, 2>(a, s); else launch_scores_t<uint16_t, 1>(a, s);
@@ -558,10 +591,10 @@ template <int EPT>
 static void launch_topk_ept(const TopkArgs& t, int B, int mode, hipStream_t s) {
   if (mode == kTopkOnly)
     hipLaunchKernelGGL((topk_kernel<EPT, kTopkOnly>), dim3(B), dim3(kTopkThreads), 0, s, t);
-  else if (mode == kTopkPlan)
-    hipLaunchKernelGGL((topk_kernel<EPT, kTopkPlan>), dim3(B), dim3(kTopkThreads), 0, s, t);
+  else if (mode == kTopkMark)
+    hipLaunchKernelGGL((topk_kernel<EPT, kTopkMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
   else
-    hipLaunchKernelGGL((topk_kernel<EPT, kTopkPlanRowpos>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kTopkMarkRowpos>), dim3(B), dim3(kTopkThreads), 0, s, t);
 }
 
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
@@ -572,11 +605,8 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.K = a.K;
   t.out = a.topk;
   t.ldK = a.ldK;
-  t.b_base = 0;
   t.offsets = a.t.offsets;
   t.cl_mask = a.cl_mask;
-  t.items = a.items;
-  t.st = a.state;
   t.rowpos = a.rowpos;
   const int ept = (a.Nc + kTopkThreads - 1) / kTopkThreads;
   if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, s);
@@ -591,23 +621,20 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
 template <typename T, int MODE>
 static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   GatherArgs g;
-  g.E = a.E;
+  g.ET = static_cast<const v4u*>(a.t.ET);
+  g.h = a.h;
   g.d = a.d;
   g.Nc = a.Nc;
-  g.B = a.B;
   g.offsets = a.t.offsets;
   g.tos = a.t.tos;
-  g.H64 = a.H64;
   g.cl_mask = a.cl_mask;
-  g.items = a.items;
-  g.st = a.state;
+  g.tiles = a.t.tiles;
   g.best = a.best;
-  g.tokens = a.tokens;
   g.rowpos = a.rowpos;
   g.L = a.L;
   g.ldL = a.ldL;
-  const dim3 grid(a.max_items > 0 ? a.max_items : 1);
-  auto kern = gather_kernel<T, 8, MODE>;
+  const dim3 grid(a.t.n_tiles > 0 ? a.t.n_tiles : 1);
+  auto kern = gather_kernel<T, kGatherRows, MODE>;
   if (a.probe_start && a.probe_stop) {
     hipExtLaunchKernelGGL(kern, grid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);
   } else {
@@ -617,11 +644,17 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s) {
+  if (a.t.n_tiles == 0) return hipSuccess;   // every cluster is empty
   if (a.dtype == 1)
     return mode == kArgmax ? launch_gather_t<uint16_t, kArgmax>(a, s)
                            : launch_gather_t<uint16_t, kMasked>(a, s);
   return mode == kArgmax ? launch_gather_t<float, kArgmax>(a, s)
                          : launch_gather_t<float, kMasked>(a, s);
+}
+
+hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(finalize_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.best, a.B, a.tokens);
+  return hipGetLastError();
 }
 
 hipError_t launch_writer(const PassArgs& a, hipStream_t s) {

@@ -92,14 +92,15 @@ typedef struct ce_graph* ce_graph_t;
  *   max_B    largest batch any call will pass, >= 1
  *   max_K    largest K any call will pass, in [1, Nc]
  *   dtype    element type of h, centroids and embeddings (ce_dtype)
- *   centroids       DEVICE [Nc][d] row-major, 16-byte aligned; borrowed
- *   emb_ordered     DEVICE [V][d] row-major, 16-byte aligned; borrowed; row j
- *                   is the embedding of token token_of_slot[j]
+ *   centroids       DEVICE [Nc][d] row-major, 16-byte aligned
+ *   emb_ordered     DEVICE [V][d] row-major, 16-byte aligned; row j is the
+ *                   embedding of token token_of_slot[j]
  *   cluster_offsets HOST [Nc+1] nondecreasing, offsets[0] = 0,
  *                   offsets[Nc] = V; or NULL for equal clusters (V % Nc == 0).
  *                   Empty clusters are allowed.  Copied at create.
  *   token_of_slot   HOST [V], a permutation of 0..V-1.  Copied at create.
- * The device arrays must stay valid and unchanged while the head is used. */
+ * The two device arrays are read only by ce_head_prepare, which packs them
+ * into the persistent buffer; they may be freed or changed afterwards. */
 typedef struct ce_head_desc {
   int32_t d;
   int32_t V;
@@ -124,16 +125,21 @@ ce_status ce_head_destroy(ce_head_t head);
 /* Bytes of the persistent device buffer ce_head_prepare needs. Host only. */
 ce_status ce_head_persistent_bytes(ce_head_t head, size_t* bytes);
 
-/* Upload the derived tables (offsets, slot->token and token->(cluster, rank)
- * maps) into the caller's persistent device buffer (256-byte aligned, at
- * least ce_head_persistent_bytes).  Set-up only: copies on `stream` and
- * synchronises it.  The buffer must live as long as the head is used.
+/* Fill the caller's persistent device buffer (256-byte aligned, at least
+ * ce_head_persistent_bytes): the derived tables (offsets, slot->token and
+ * token->(cluster, rank) maps, the list of 64-slot cluster tiles) and packed
+ * copies of the centroids and embeddings in 64-row tiles whose 16-byte
+ * vectors are interleaved across rows, so that the hot kernels stream them
+ * with fully coalesced loads (one more copy of the weights in HBM).  Set-up
+ * only: copies and packs on `stream` and synchronises it.  The buffer must
+ * live as long as the head is used.
  * Errors: NULL_POINTER, MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
 ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes,
                           hipStream_t stream);
 
 /* Workspace bytes one call of `op` with batch B and top-K K needs (the
- * worst case over inputs).  Host only.  CE_OP_TOPK needs none (returns 0).
+ * worst case over inputs).  Host only.  CE_OP_SCORE and CE_OP_TOPK need none
+ * (0 bytes).
  * Errors: NULL_POINTER, BAD_SHAPE. */
 ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op,
                              size_t* bytes);
@@ -142,12 +148,10 @@ ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op,
  *   scores[b][c] = canonical dot(h[b], centroids[c]),  b < B, c < Nc.
  *   h       DEVICE [B][d] of the head's dtype, 16-byte aligned
  *   scores  DEVICE [B][Nc] fp32, written entirely
- *   ws      DEVICE workspace, 256-byte aligned, >= ce_workspace_bytes(SCORE)
- * B = 0 is a no-op.  Errors: NOT_PREPARED, NULL_POINTER, BAD_SHAPE
- * (B outside [0, max_B]), MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
+ * No workspace.  B = 0 is a no-op.  Errors: NOT_PREPARED, NULL_POINTER,
+ * BAD_SHAPE (B outside [0, max_B]), MISALIGNED, HIP. */
 ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B,
-                             float* scores, void* ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             float* scores, hipStream_t stream);
 
 /* Top-K selection (the page's torch.topk over the centroid scores) on a
  * caller-given fp32 array, bit-exact: topk_ids[b] holds, in ascending order,
