@@ -32,6 +32,27 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 METRIC = "sparse-head draft rows/sec at B=1..64 + achieved HBM GB/s vs peak (1 MI355X)"
 
+# HBM bytes per launch of the dominant kernel (gather, top_tokens, B=64) from
+# two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each
+# scaled by what the counter reads for a plain 128 MiB copy (fetch x2.00,
+# write x1.00); see profiles/gather_kernel_sweep_B64.md.  Valid only for the
+# kernel source it was measured on: any other source reports null.
+TRAFFIC_RECORD = {
+    "kernels_sha256_prefix": "22113ba4837c30bc",
+    "fetch_kib": 41715, "fetch_scale": 2.00, "write_kib": 128, "write_scale": 1.00,
+}
+
+
+def _traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "centroid_masked_sparse_amd", "csrc", "ce_kernels.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    r = TRAFFIC_RECORD
+    if not digest.startswith(r["kernels_sha256_prefix"]):
+        return None
+    return int((r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"]) * 1024)
+
 
 def _to_device(a, dtype, torch):
     if dtype == "bf16":
@@ -257,7 +278,7 @@ def main() -> int:
         "hbm_frac_peak": head_row["frac_peak"],
         "roofline": {"bound": "hbm", "kernel": "gather_kernel<bf16,argmax>",
                      "achieved": round(gather_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gather_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gather_gbs / PEAK_HBM_GBS, 4), "traffic": _traffic_bytes(),
                      "bytes_per_launch": int(head_slab), "us_per_launch": round(gather_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "sweep": sweep,

@@ -153,14 +153,14 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid,
   constexpr int VPC = kChunk / PV;              // weight vectors per chunk
   using HS = HStage<T, RB>;
   const int lane = threadIdx.x;
-  const bool wvalid = lane < nvalid;
+  (void)nvalid;
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = 0.0;
 
   // hidden-row raw loads: vector hv = lane + 64 i covers row hv / kVecPerRow
+  // (slots of rows >= nrows load a valid row and are never read back)
   const char* hbase = reinterpret_cast<const char*>(h);
   uint32_t hoff[HS::kLoads];
-  bool hval[HS::kLoads];
   int hslot[HS::kLoads];
 #pragma unroll
   for (int i = 0; i < HS::kLoads; ++i) {
@@ -171,33 +171,34 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid,
 #pragma unroll
     for (int q = 0; q < RB; ++q)
       if (q == r) row = rows[q];
-    hval[i] = r < nrows;
     hoff[i] = ((uint32_t)row * (uint32_t)d + (uint32_t)part * PV) * sizeof(T);
-    hslot[i] = r * HS::kV2PerRow + part * (PV / 2);
+    hslot[i] = (r < RB ? r : 0) * HS::kV2PerRow + part * (PV / 2);
   }
 
+  // Every load is unconditional (packed tiles are zero-padded to 64 rows and
+  // hidden-row slots are clamped to valid rows): a load under a branch makes
+  // the compiler wait for all outstanding loads at the join, which would
+  // serialise the two stages in flight.
   struct Stage {
     v4u e[VPC];
     v4u h[HS::kLoads];
   };
   auto load = [&](Stage& st, int ch) {
 #pragma unroll
-    for (int p = 0; p < VPC; ++p)
-      if (wvalid) st.e[p] = wt[(ch * VPC + p) * kWave + lane];
+    for (int p = 0; p < VPC; ++p) st.e[p] = wt[(ch * VPC + p) * kWave + lane];
     const uint32_t hadv = (uint32_t)ch * (kChunk * sizeof(T));
 #pragma unroll
     for (int i = 0; i < HS::kLoads; ++i)
-      if (hval[i]) st.h[i] = *reinterpret_cast<const v4u*>(hbase + hoff[i] + hadv);
+      st.h[i] = *reinterpret_cast<const v4u*>(hbase + hoff[i] + hadv);
   };
   auto park = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int i = 0; i < HS::kLoads; ++i)
-      if (hval[i]) {
-        double x[PV];
-        widen(st.h[i], x, T());
+    for (int i = 0; i < HS::kLoads; ++i) {
+      double x[PV];
+      widen(st.h[i], x, T());
 #pragma unroll
-        for (int j = 0; j < PV / 2; ++j) lds[buf][hslot[i] + j] = v2d{x[2 * j], x[2 * j + 1]};
-      }
+      for (int j = 0; j < PV / 2; ++j) lds[buf][hslot[i] + j] = v2d{x[2 * j], x[2 * j + 1]};
+    }
   };
   auto consume = [&](const Stage& st, int buf) {
 #pragma unroll
@@ -222,20 +223,48 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid,
   // a stage is reloaded only after its weights have been consumed.  One wave
   // per workgroup: the barrier orders this wave's LDS writes before its
   // reads; the other LDS buffer is rewritten only after a later barrier.
+  // The steady-state loop (even chunk counts) reloads unconditionally and
+  // the last two chunks are peeled, so no load sits under a branch.
   const int nch = d / kChunk;
   Stage s0, s1;
-  load(s0, 0);
-  if (nch > 1) load(s1, 1);
-  for (int ch = 0; ch < nch; ch += 2) {
+  if (nch == 1) {
+    load(s0, 0);
     park(s0, 0);
     __syncthreads();
     consume(s0, 0);
-    if (ch + 2 < nch) load(s0, ch + 2);
-    if (ch + 1 < nch) {
+  } else if ((nch & 1) == 0) {
+    load(s0, 0);
+    load(s1, 1);
+    for (int ch = 0; ch < nch - 2; ch += 2) {
+      park(s0, 0);
+      __syncthreads();
+      consume(s0, 0);
+      load(s0, ch + 2);
       park(s1, 1);
       __syncthreads();
       consume(s1, 1);
-      if (ch + 3 < nch) load(s1, ch + 3);
+      load(s1, ch + 3);
+    }
+    park(s0, 0);
+    __syncthreads();
+    consume(s0, 0);
+    park(s1, 1);
+    __syncthreads();
+    consume(s1, 1);
+  } else {
+    load(s0, 0);
+    load(s1, 1);
+    for (int ch = 0; ch < nch; ch += 2) {
+      park(s0, 0);
+      __syncthreads();
+      consume(s0, 0);
+      if (ch + 2 < nch) load(s0, ch + 2);
+      if (ch + 1 < nch) {
+        park(s1, 1);
+        __syncthreads();
+        consume(s1, 1);
+        if (ch + 3 < nch) load(s1, ch + 3);
+      }
     }
   }
 }
@@ -453,7 +482,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int q = (int)(tile >> kTileShift);
   const long j0 = (long)a.offsets[c] + (long)q * kTileTokens;
   const int nvalid = (int)min((long)kTileTokens, (long)a.offsets[c + 1] - j0);
-  const int tok = (MODE == kArgmax && lane < nvalid) ? a.tos[j0 + lane] : 0;
+  const int tok = MODE == kArgmax ? a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)] : 0;
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
   const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
   const T* h = reinterpret_cast<const T*>(a.h);
