@@ -87,6 +87,14 @@ __device__ __forceinline__ float canon(double s) {
   return __uint_as_float(u == 0x80000000u ? 0u : u);
 }
 
+// Keep a loaded value live on every path.  Without it the compiler sinks a
+// load whose result is only used under a condition into that branch, and a
+// load under a branch is waited for on its own (no overlap with the others).
+template <typename V>
+__device__ __forceinline__ void pin(V& v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Order-preserving map of a (non-NaN) fp32 to u32; -0 and +0 map alike.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -364,12 +372,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const int Nc = a.Nc;
   const float* row = a.S + (long)b * a.ldS;
 
+  float v[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int c = tid * EPT + i;
+    v[i] = row[c < Nc ? c : Nc - 1];   // unconditional (clamped) loads
+  }
   uint32_t key[EPT];
   uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const int c = tid * EPT + i;
-    key[i] = c < Nc ? order_key(row[c]) : 0u;
+    pin(v[i]);
+    key[i] = c < Nc ? order_key(v[i]) : 0u;
     valid |= (c < Nc ? 1u : 0u) << i;
   }
 
@@ -482,7 +497,11 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int q = (int)(tile >> kTileShift);
   const long j0 = (long)a.offsets[c] + (long)q * kTileTokens;
   const int nvalid = (int)min((long)kTileTokens, (long)a.offsets[c + 1] - j0);
-  const int tok = MODE == kArgmax ? a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)] : 0;
+  int tok = 0;
+  if (MODE == kArgmax) {
+    tok = a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)];
+    pin(tok);
+  }
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
   const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
   const T* h = reinterpret_cast<const T*>(a.h);
