@@ -63,7 +63,7 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
-  size_t scores = 0, topk = 0, cl_mask = 0, best = 0, rowpos = 0, logits = 0, total = 0;
+  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, rowpos = 0, logits = 0, total = 0;
   int ldL = 0;
 };
 
@@ -82,7 +82,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   }
   L.scores = take(nb * h->Nc * sizeof(float));
   L.topk = take(nb * (size_t)K * sizeof(int32_t));
-  L.cl_mask = take((size_t)h->Nc * sizeof(unsigned long long));
+  L.cl_sel = take(((size_t)h->Nc + 63) / 64 * ce::kPassRows * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
   if (op == CE_OP_MASKED_LOGITS) {
     L.rowpos = take(nb * h->Nc * sizeof(int32_t));
@@ -146,7 +146,7 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.ldS = a.Nc;
   a.topk = reinterpret_cast<int32_t*>(ws + L.topk);
   a.ldK = a.K;
-  a.cl_mask = reinterpret_cast<unsigned long long*>(ws + L.cl_mask);
+  a.cl_sel = reinterpret_cast<unsigned long long*>(ws + L.cl_sel);
   a.best = reinterpret_cast<unsigned long long*>(ws + L.best);
   a.rowpos = reinterpret_cast<int32_t*>(ws + L.rowpos);
   a.L = reinterpret_cast<float*>(ws + L.logits);
@@ -365,8 +365,6 @@ ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* sc
     ce::PassArgs a = base_args(head, 1);
     a.B = std::min(ce::kPassRows, B - b0);
     a.h = static_cast<const char*>(h) + (size_t)b0 * (size_t)head->d * elem_bytes(head->dtype);
-    a.cl_mask = nullptr;  // no selection follows: nothing to clear
-    a.best = nullptr;
     a.S = scores + (size_t)b0 * head->Nc;
     a.ldS = head->Nc;
     hipError_t e = ce::launch_scores(a, stream);

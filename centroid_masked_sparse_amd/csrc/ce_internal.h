@@ -28,7 +28,10 @@ struct Tables {
 };
 
 enum GatherMode { kArgmax = 0, kMasked = 1 };
-enum TopkMode { kTopkOnly = 0, kTopkMark = 1, kTopkMarkRowpos = 2 };
+// What the top-K kernel writes besides the ids: nothing, the rows' selection
+// words and cleared argmax slots (get_top_tokens), or the selection words and
+// candidate positions (forward).
+enum TopkMode { kTopkOnly = 1, kTopkMark = 2, kTopkMarkRowpos = 3 };
 
 // Everything one pass (at most kPassRows rows) needs.
 struct PassArgs {
@@ -44,7 +47,7 @@ struct PassArgs {
   int ldS;
   int32_t* topk;          // [B][ldK] selected centroids
   int ldK;
-  unsigned long long* cl_mask;  // [Nc] rows that selected each centroid
+  unsigned long long* cl_sel;   // [ceil(Nc/64)][kPassRows] bit i of word (w, b): row b selected 64w+i
   unsigned long long* best;     // [kPassRows] packed (ordered logit, ~token)
   int32_t* rowpos;        // [B][Nc] first candidate position of a centroid in a row, or -1
   float* L;               // [B][ldL] candidate logits in row order
@@ -61,7 +64,7 @@ struct PassArgs {
 hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint32_t* tiles,
                        const int32_t* offsets, int nrows_total, void* out, hipStream_t s);
 hipError_t launch_scores(const PassArgs& a, hipStream_t s);
-hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);
+hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: TopkMode
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
 hipError_t launch_writer(const PassArgs& a, hipStream_t s);

@@ -48,8 +48,9 @@
 
 #include "ce_internal.h"
 
-// Wavefront reductions of the ROCm device library (DPP based).
+// Wavefront reductions and scans of the ROCm device library (DPP based).
 extern "C" __device__ unsigned int __ockl_wfred_add_u32(unsigned int);
+extern "C" __device__ unsigned int __ockl_wfscan_add_u32(unsigned int, bool inclusive);
 extern "C" __device__ unsigned long long __ockl_wfred_max_u64(unsigned long long);
 
 namespace ce {
@@ -279,22 +280,13 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid,
 
 // ------------------------------------------------------------------ scores
 
-// One wave per (64-centroid tile, RB rows).  Also clears the row masks and
-// argmax slots of the pass (when given), before the top-K kernel runs.
+// One wave per (64-centroid tile, RB rows): S[b][c] for the tile's centroids.
 template <typename T, int RB>
 __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, int Nc, int d,
                                                     const T* __restrict__ h, int B,
-                                                    float* __restrict__ S, int ldS,
-                                                    unsigned long long* __restrict__ cl_mask,
-                                                    unsigned long long* __restrict__ best) {
+                                                    float* __restrict__ S, int ldS) {
   __shared__ v2d lds[2][RB * kChunk / 2];
   const int lane = threadIdx.x;
-  if (cl_mask) {
-    const int w = blockIdx.y * gridDim.x + blockIdx.x;
-    const int nw = gridDim.x * gridDim.y;
-    for (int k = w * kWave + lane; k < Nc; k += nw * kWave) cl_mask[k] = 0ull;
-    if (w == 0) best[lane] = 0ull;
-  }
   const int c0 = blockIdx.x * kTileTokens;
   const int r0 = blockIdx.y * RB;
   const int nvalid = min(kTileTokens, Nc - c0);
@@ -315,147 +307,317 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
 // ------------------------------------------------------------------ top-K
 
 constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kCandCap = 1024;   // candidate keys kept for the exact select
+
+// Lanes of the wave below this one whose bit is set in `m`.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint32_t popc64(unsigned long long m) { return (uint32_t)__popcll(m); }
 
 // Exclusive prefix sum over the 256 threads of the block; *total gets the sum.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) sh[w] = x;
+  const uint32_t x = __ockl_wfscan_add_u32(v, false);   // exclusive, within the wave
+  if (lane == kWave - 1) sh[w] = x + v;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkThreads / kWave; ++i) {
+  for (int i = 0; i < kTopkWaves; ++i) {
     const uint32_t s = sh[i];
     base += (i < w) ? s : 0u;
     tot += s;
   }
   __syncthreads();
   *total = tot;
-  return base + x - v;
+  return base + x;
 }
+
+// K-th largest, counting repeats, of the values r[0..NV) of every lane of
+// the wave (0 marks an absent value; K must not exceed the present ones), by
+// radix select from the top bit: at each bit the values that agree with the
+// answer on the bits above and have a 1 at this bit are counted; if they are
+// at least kk the answer has a 1 there, else they all rank above it and kk
+// drops by their number.  *quota gets kk at the end: how many copies of the
+// answer the K largest hold.  All 32 steps are unrolled and branch-free (one
+// wave alone runs this, so every taken branch would be paid in full).
+template <int NV>
+__device__ __forceinline__ uint32_t radix_kth(const uint32_t (&r)[NV], uint32_t K, uint32_t* quota) {
+  uint32_t prefix = 0, kk = K;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t want = (prefix >> bit) | 1u;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) c += popc64(__ballot((r[j] >> bit) == want));
+    const bool one = c >= kk;
+    prefix |= one ? (1u << bit) : 0u;
+    kk -= one ? 0u : c;
+  }
+  *quota = kk;
+  return prefix;
+}
+
+// The K-th largest T of cand[0..n) (LDS, nonzero, K <= n), the number of
+// copies of T the K largest hold (*quota) and the number of copies in all
+// (*copies); one wave.
+template <int NV>
+__device__ __forceinline__ uint32_t cand_kth(const uint32_t* cand, int n, uint32_t K,
+                                             uint32_t* quota, uint32_t* copies) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t r[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int idx = j * kWave + lane;
+    r[j] = idx < n ? cand[idx] : 0u;
+  }
+  const uint32_t T = radix_kth<NV>(r, K, quota);
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) c += popc64(__ballot(r[j] == T));
+  *copies = c;
+  return T;
+}
+
+enum SelectMode { kSelIds = 1, kSelMark = 2, kSelRowpos = 3 };
 
 struct TopkArgs {
   const float* S;
   int ldS, Nc, K;
-  int32_t* out;
+  int32_t* out;                    // [rows][ldK] ascending ids
   int ldK;
-  const int32_t* offsets;
-  unsigned long long* cl_mask;
-  int32_t* rowpos;
+  unsigned long long* cl_sel;      // [ceil(Nc/64)][64]: bit i of word (w, b) = row b selected 64w+i
+  int32_t* rowpos;                 // [rows][Nc]
+  const int32_t* offsets;          // [Nc+1]
+  unsigned long long* best;        // [64] argmax slots, cleared per row
 };
 
-// One workgroup per row.  Thread t holds centroids [t*EPT, t*EPT+EPT), so
-// thread order is id order.  Bit-serial radix select, most significant bit
-// first, over order-preserving keys: `alive` marks keys still tied with the
-// K-th largest on the bits seen so far; at each bit, if the alive keys with a
-// 1 there number at most kk they are all kept (and kk shrinks), else the
-// search continues among them.  Counting needs no atomics: a per-lane
-// popcount, a DPP wave reduction and one barrier per bit (partial sums are
-// double-buffered by bit parity).  The loop stops as soon as exactly K keys
-// are kept; keys still alive after 32 bits are equal, and the lowest ids
-// among them are kept.
+// Number of the values vals[0..n) (LDS, read as broadcasts; n a multiple
+// of kCountBlock, zero-padded) that are greater than x.  Each block of reads
+// is issued before the first compare.
+constexpr int kCountBlock = 32;
+__device__ __forceinline__ uint32_t count_above(const uint32_t* vals, int n, uint32_t x) {
+  uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  for (int j = 0; j < n; j += kCountBlock) {
+    v4u q[kCountBlock / 4];
+#pragma unroll
+    for (int u = 0; u < kCountBlock / 4; ++u) q[u] = *reinterpret_cast<const v4u*>(vals + j + 4 * u);
+#pragma unroll
+    for (int u = 0; u < kCountBlock / 4; ++u) {
+      c0 += q[u].x > x ? 1u : 0u;
+      c1 += q[u].y > x ? 1u : 0u;
+      c2 += q[u].z > x ? 1u : 0u;
+      c3 += q[u].w > x ? 1u : 0u;
+    }
+  }
+  return (c0 + c1) + (c2 + c3);
+}
+
+// One workgroup of 256 threads per row; thread t holds centroids
+// [t*EPT, t*EPT+EPT), so thread order is id order.  The K-th largest value
+// of a set is the smallest of its values with fewer than K values strictly
+// above it, so it can be found by counting in parallel, without a serial
+// chain of steps:
+//  1. Threshold: each wave finds the K-th largest mu_w of its 64 thread
+//     maxima (K <= 64) by such counts.  Those are K distinct keys >= mu_w,
+//     so the K-th largest key T of the row is >= mu = max_w mu_w, and the
+//     top K lies among the keys >= mu (about a hundred on random rows).
+//  2. The keys >= mu are gathered into LDS and T is found among them: one
+//     candidate per thread counted against all (up to 256 candidates), else
+//     by a radix select in each wave.
+//  3. One block scan of the per-thread counts of keys > T and keys == T
+//     gives the number of copies of T to keep (K minus the keys above T,
+//     lowest ids first), and every thread's position in the ascending id
+//     list; the kept bits are assembled into the row's 64-centroid
+//     selection words.
+// Rows with more than kCandCap keys >= mu (K > 64 on large rows, or masses
+// of equal scores) fall back to a bit-serial select over all keys with one
+// barrier per bit.  K >= Nc keeps every centroid.
 template <int EPT, int MODE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  static_assert(EPT <= 32, "selection mask is 32 bits");
-  __shared__ uint32_t part[2][kTopkThreads / kWave];
-  __shared__ uint32_t scan_sh[kTopkThreads / kWave];
+  static_assert(EPT >= 1 && EPT <= 32 && kWave % EPT == 0, "per-thread keys");
+  __shared__ __attribute__((aligned(16))) uint32_t cand[kCandCap + kCountBlock];
+  __shared__ __attribute__((aligned(16))) uint32_t wmax[kTopkThreads];
+  __shared__ unsigned long long words[kMaxNc / kWave];
+  __shared__ uint32_t wred[kTopkWaves];
+  __shared__ uint32_t part[2][kTopkWaves];
+  __shared__ uint32_t scan_sh[kTopkWaves];
+  __shared__ uint32_t ncand;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int Nc = a.Nc;
+  const uint32_t K = (uint32_t)a.K;
+  const int first = tid * EPT;
   const float* row = a.S + (long)b * a.ldS;
 
   float v[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int c = tid * EPT + i;
+    const int c = first + i;
     v[i] = row[c < Nc ? c : Nc - 1];   // unconditional (clamped) loads
   }
+  const int nwords = (Nc + kWave - 1) / kWave;
+  if (MODE >= kSelMark)
+    for (int w = tid; w < nwords; w += kTopkThreads) words[w] = 0ull;
+  if (tid == 0) ncand = 0;
+
   uint32_t key[EPT];
-  uint32_t valid = 0;
+  uint32_t valid = 0, m = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int c = tid * EPT + i;
+    const int c = first + i;
     pin(v[i]);
     key[i] = c < Nc ? order_key(v[i]) : 0u;
     valid |= (c < Nc ? 1u : 0u) << i;
+    m = max(m, key[i]);
   }
 
-  uint32_t sel = 0, alive = valid, kk = (uint32_t)a.K;
-  if (a.K >= Nc) {
-    sel = valid;
-    alive = 0;
-    kk = 0;
+  const bool take_all = K >= (uint32_t)Nc;
+  wmax[tid] = m;
+  __syncthreads();
+  uint32_t mu = 0;
+  if (!take_all && K <= (uint32_t)kWave) {
+    // smallest wave maximum with fewer than K wave maxima above it (0, a
+    // valid bound, when the wave holds fewer than K keys)
+    const uint32_t above = count_above(wmax + wv * kWave, kWave, m);
+    mu = __ockl_wfred_min_u32(above < K ? m : 0xFFFFFFFFu);
   }
-  for (int bit = 31; bit >= 0 && kk > 0; --bit) {
-    uint32_t ones = 0;
+  if (lane == 0) wred[wv] = mu;
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) ones |= ((key[i] >> bit) & 1u) << i;
-    ones &= alive;
-    const uint32_t wsum = __ockl_wfred_add_u32((uint32_t)__popc(ones));
-    if (lane == 0) part[bit & 1][wv] = wsum;
+  for (int i = 0; i < kTopkWaves; ++i) mu = max(mu, wred[i]);
+
+  uint32_t sel = valid, pos = 0, tot;
+  bool placed = false;   // pos already known
+  if (!take_all) {
+    // 2. candidates: the keys >= mu, in any order
+    uint32_t wtotal = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) wtotal += popc64(__ballot(key[i] != 0u && key[i] >= mu));
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&ncand, wtotal);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const bool p = key[i] != 0u && key[i] >= mu;
+      const unsigned long long pm = __ballot(p);
+      const uint32_t at = base + lanes_below(pm);
+      if (p && at < (uint32_t)kCandCap) cand[at] = key[i];
+      base += popc64(pm);
+    }
     __syncthreads();
-    uint32_t total = 0;
+    const int n = (int)ncand;
+    if (n <= kCandCap) {
+      uint32_t T;
+      if (n <= kTopkThreads) {
+        // zero the tail to a whole block (zeros are never above a key)
+        if (tid < kCountBlock) cand[n + tid] = 0u;
+        __syncthreads();
+        const uint32_t x = tid < n ? cand[tid] : 0u;
+        const uint32_t above =
+            count_above(cand, (n + kCountBlock - 1) / kCountBlock * kCountBlock, x);
+        const uint32_t wmin = __ockl_wfred_min_u32(x && above < K ? x : 0xFFFFFFFFu);
+        if (lane == 0) wred[wv] = wmin;
+        __syncthreads();
+        T = wred[0];
 #pragma unroll
-    for (int i = 0; i < kTopkThreads / kWave; ++i) total += part[bit & 1][i];
-    if (total <= kk) {
-      sel |= ones;
-      alive &= ~ones;
-      kk -= total;
+        for (int i = 1; i < kTopkWaves; ++i) T = min(T, wred[i]);
+      } else {
+        uint32_t quota, copies;
+        if (n <= 8 * kWave) T = cand_kth<8>(cand, n, K, &quota, &copies);
+        else T = cand_kth<16>(cand, n, K, &quota, &copies);
+      }
+      // 3. keys > T, then copies of T up to K in id order
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        gt |= (key[i] > T ? 1u : 0u) << i;
+        eq |= (key[i] == T ? 1u : 0u) << i;
+      }
+      const uint32_t ex =
+          block_excl_scan(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(eq), scan_sh, &tot);
+      const uint32_t quota = K - (tot >> 16);
+      uint32_t eq_rank = ex & 0xFFFFu;
+      pos = (ex >> 16) + min(eq_rank, quota);
+      uint32_t keep = 0;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if (eq & (1u << i)) {
+          if (eq_rank < quota) keep |= 1u << i;
+          ++eq_rank;
+        }
+      sel = gt | keep;
+      placed = true;
     } else {
-      alive = ones;
+      // bit-serial over all keys: `alive` marks keys still tied with the
+      // K-th largest on the bits seen so far
+      uint32_t s = 0, alive = valid, kk = K;
+      for (int bit = 31; bit >= 0 && kk > 0; --bit) {
+        uint32_t ones = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) ones |= ((key[i] >> bit) & 1u) << i;
+        ones &= alive;
+        const uint32_t wsum = __ockl_wfred_add_u32((uint32_t)__popc(ones));
+        if (lane == 0) part[bit & 1][wv] = wsum;
+        __syncthreads();
+        uint32_t total = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkWaves; ++i) total += part[bit & 1][i];
+        if (total <= kk) {
+          s |= ones;
+          alive &= ~ones;
+          kk -= total;
+        } else {
+          alive = ones;
+        }
+      }
+      // keys still alive are equal: keep the kk lowest ids among them
+      uint32_t seen = block_excl_scan((uint32_t)__popc(alive), scan_sh, &tot);
+      if (kk > 0) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+          if (alive & (1u << i)) {
+            if (seen < kk) s |= 1u << i;
+            ++seen;
+          }
+      }
+      sel = s;
     }
   }
-  // keys still alive are all equal: keep the kk lowest ids among them
-  uint32_t tot;
-  const uint32_t eq_before = block_excl_scan((uint32_t)__popc(alive), scan_sh, &tot);
-  if (kk > 0) {
-    uint32_t seen = eq_before;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-      if (alive & (1u << i)) {
-        if (seen < kk) sel |= 1u << i;
-        ++seen;
-      }
-  }
-  const uint32_t selmask = sel;
-  uint32_t pos = block_excl_scan((uint32_t)__popc(selmask), scan_sh, &tot);
+  if (!placed) pos = block_excl_scan((uint32_t)__popc(sel), scan_sh, &tot);
+
+  // outputs
   int32_t* out = a.out + (long)b * a.ldK;
 #pragma unroll
   for (int i = 0; i < EPT; ++i)
-    if (selmask & (1u << i)) out[pos++] = tid * EPT + i;
+    if (sel & (1u << i)) out[pos++] = first + i;
 
-  if (MODE >= kTopkMark) {
-    // no return value is used, so these atomics do not stall the wave
-    const unsigned long long bit = 1ull << b;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-      if (selmask & (1u << i))
-        __hip_atomic_fetch_or(&a.cl_mask[tid * EPT + i], bit, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+  if (MODE >= kSelMark) {
+    if (sel) atomicOr(&words[first / kWave], (unsigned long long)sel << (first % kWave));
+    __syncthreads();
+    for (int w = tid; w < nwords; w += kTopkThreads) a.cl_sel[(long)w * kWave + b] = words[w];
   }
-  if (MODE == kTopkMarkRowpos) {
+  if (MODE == kSelMark && tid == 0) a.best[b] = 0ull;
+  if (MODE == kSelRowpos) {
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
-      if (selmask & (1u << i)) {
-        const int c = tid * EPT + i;
+      if (sel & (1u << i)) {
+        const int c = first + i;
         local += (uint32_t)(a.offsets[c + 1] - a.offsets[c]);
       }
     uint32_t run = block_excl_scan(local, scan_sh, &tot);
     int32_t* rp = a.rowpos + (long)b * Nc;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
-      const int c = tid * EPT + i;
+      const int c = first + i;
       if (c < Nc) {
-        if (selmask & (1u << i)) {
+        if (sel & (1u << i)) {
           rp[c] = (int32_t)run;
           run += (uint32_t)(a.offsets[c + 1] - a.offsets[c]);
         } else {
@@ -474,7 +636,8 @@ struct GatherArgs {
   int d, Nc;
   const int32_t* offsets;
   const int32_t* tos;
-  const unsigned long long* cl_mask;
+  const unsigned long long* cl_sel;
+  int B;
   const uint32_t* tiles;
   unsigned long long* best;
   const int32_t* rowpos;
@@ -492,7 +655,9 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
   const uint32_t tile = a.tiles[blockIdx.x];
   const int c = (int)(tile & ((1u << kTileShift) - 1u));
-  unsigned long long mask = a.cl_mask[c];
+  // lane b reads row b's selection word of c's 64-centroid block
+  const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
+  unsigned long long mask = __ballot((word >> (c % kWave)) & 1ull);
   if (!mask) return;   // no row selected this centroid
   const int q = (int)(tile >> kTileShift);
   const long j0 = (long)a.offsets[c] + (long)q * kTileTokens;
@@ -622,7 +787,7 @@ static void launch_scores_t(const PassArgs& a, hipStream_t s) {
   const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
   hipLaunchKernelGGL((scores_kernel<T, RB>), grid, dim3(64), 0, s,
                      static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
-                     a.S, a.ldS, a.cl_mask, a.best);
+                     a.S, a.ldS);
 }
 
 hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
@@ -638,11 +803,11 @@ hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
 template <int EPT>
 static void launch_topk_ept(const TopkArgs& t, int B, int mode, hipStream_t s) {
   if (mode == kTopkOnly)
-    hipLaunchKernelGGL((topk_kernel<EPT, kTopkOnly>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelIds>), dim3(B), dim3(kTopkThreads), 0, s, t);
   else if (mode == kTopkMark)
-    hipLaunchKernelGGL((topk_kernel<EPT, kTopkMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
   else
-    hipLaunchKernelGGL((topk_kernel<EPT, kTopkMarkRowpos>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelRowpos>), dim3(B), dim3(kTopkThreads), 0, s, t);
 }
 
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
@@ -653,9 +818,10 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.K = a.K;
   t.out = a.topk;
   t.ldK = a.ldK;
-  t.offsets = a.t.offsets;
-  t.cl_mask = a.cl_mask;
+  t.cl_sel = a.cl_sel;
   t.rowpos = a.rowpos;
+  t.offsets = a.t.offsets;
+  t.best = a.best;
   const int ept = (a.Nc + kTopkThreads - 1) / kTopkThreads;
   if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, s);
   else if (ept <= 2) launch_topk_ept<2>(t, a.B, mode, s);
@@ -675,7 +841,8 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.Nc = a.Nc;
   g.offsets = a.t.offsets;
   g.tos = a.t.tos;
-  g.cl_mask = a.cl_mask;
+  g.cl_sel = a.cl_sel;
+  g.B = a.B;
   g.tiles = a.t.tiles;
   g.best = a.best;
   g.rowpos = a.rowpos;
