@@ -39,8 +39,9 @@
 // step), then rounded to fp32 nearest-even with -0 mapped to +0.  Each lane
 // owns whole chains (one per output), so no reduction tree reorders a sum and
 // the results equal a sequential float64 loop bit for bit.  The hidden rows are
-// wave-uniform operands: each 64-dim chunk is widened to float64 into LDS and
-// read back as broadcasts.
+// wave-uniform operands: each lane widens four elements of a 64-dim chunk to
+// float64 and a 64-bit DPP row broadcast hands element k to every lane, so
+// the hidden rows take no LDS traffic and no barriers.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -138,51 +139,107 @@ __global__ __launch_bounds__(256) void pack_kernel(const v4u* __restrict__ W, in
 
 // ------------------------------------------------------------------ dot tile
 
-template <typename T, int RB>
-struct HStage {
-  static constexpr int kPerVec = Elem<T>::kPerVec;
-  static constexpr int kVecPerRow = kChunk / kPerVec;                 // raw 16-B vectors per row chunk
-  static constexpr int kLoads = (RB * kVecPerRow + kWave - 1) / kWave;
-  static constexpr int kV2PerRow = kChunk / 2;                        // v2d per row chunk in LDS
-};
+// acc = fma(h_k, x_k, acc) for the elements k of one weight vector, in
+// order, with h_k taken from lane k/4 of this lane's 16-lane row by a 64-bit
+// DPP row broadcast fused into v_fmac_f64 (src0), so the hidden value costs
+// neither LDS traffic nor an extra instruction.  hq holds this lane's four
+// elements.  A DPP read needs two wait states after a VALU write of its
+// source; the compiler cannot see inside the asm, so each block starts with
+// them.
+template <int J>
+__device__ __forceinline__ void fmac_vec(double& acc, const double (&hq)[4], const double (&x)[8]) {
+  // bf16: elements 8p..8p+7 sit in lanes J = 2p (first four) and J+1
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f64_dpp %0, %1, %5 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %6 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %7 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %8 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %1, %9 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %11 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(hq[0]), "v"(hq[1]), "v"(hq[2]), "v"(hq[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]),
+        "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "n"(J), "n"(J + 1));
+}
+template <int J>
+__device__ __forceinline__ void fmac_vec(double& acc, const double (&hq)[4], const double (&x)[4]) {
+  // fp32: elements 4p..4p+3 sit in lane J = p
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f64_dpp %0, %1, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %6 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %7 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(hq[0]), "v"(hq[1]), "v"(hq[2]), "v"(hq[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]),
+        "v"(x[3]), "n"(J));
+}
+// Weight vector p of a chunk (p is a constant once the loops are unrolled).
+template <int PV>
+__device__ __forceinline__ void fmac_vec_p(int p, double& acc, const double (&hq)[4],
+                                           const double (&x)[PV]) {
+  constexpr int S = PV / 4;   // lanes per vector: 2 (bf16) or 1 (fp32)
+  switch (p) {
+    case 0: fmac_vec<0 * S>(acc, hq, x); break;
+    case 1: fmac_vec<1 * S>(acc, hq, x); break;
+    case 2: fmac_vec<2 * S>(acc, hq, x); break;
+    case 3: fmac_vec<3 * S>(acc, hq, x); break;
+    case 4: fmac_vec<4 * S>(acc, hq, x); break;
+    case 5: fmac_vec<5 * S>(acc, hq, x); break;
+    case 6: fmac_vec<6 * S>(acc, hq, x); break;
+    case 7: fmac_vec<7 * S>(acc, hq, x); break;
+    case 8: fmac_vec<(8 * S) & 15>(acc, hq, x); break;
+    case 9: fmac_vec<(9 * S) & 15>(acc, hq, x); break;
+    case 10: fmac_vec<(10 * S) & 15>(acc, hq, x); break;
+    case 11: fmac_vec<(11 * S) & 15>(acc, hq, x); break;
+    case 12: fmac_vec<(12 * S) & 15>(acc, hq, x); break;
+    case 13: fmac_vec<(13 * S) & 15>(acc, hq, x); break;
+    case 14: fmac_vec<(14 * S) & 15>(acc, hq, x); break;
+    default: fmac_vec<(15 * S) & 15>(acc, hq, x); break;
+  }
+}
 
-// Dot one packed 64-row tile `wt` ([d/kPerVec][64] vectors; rows >= nvalid
-// are not read and their results must be ignored) with the hidden rows
-// h[rows[r]] for r < nrows ([*][d] of T).  Lane t ends with acc[r] = the
-// float64 chain of (tile row t, hidden row rows[r]).
+// Four consecutive hidden-row elements as loaded by one lane.
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+template <typename T> struct HQuad;
+template <> struct HQuad<uint16_t> { typedef v2u raw; };   // 4 bf16
+template <> struct HQuad<float> { typedef v4u raw; };      // 4 fp32
+
+__device__ __forceinline__ void widen4(const v2u r, double (&x)[4]) {
+  x[0] = (double)__uint_as_float(r[0] << 16);
+  x[1] = (double)__uint_as_float(r[0] & 0xffff0000u);
+  x[2] = (double)__uint_as_float(r[1] << 16);
+  x[3] = (double)__uint_as_float(r[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void widen4(const v4u r, double (&x)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (double)__uint_as_float(r[i]);
+}
+
+// Dot one packed 64-row tile `wt` ([d/kPerVec][64] vectors, zero-padded)
+// with the hidden rows h[rows[r]] for r < nrows ([*][d] of T).  Lane t ends
+// with acc[r] = the float64 chain of (tile row t, hidden row rows[r]).
 //
-// Per chunk of 64 dims each lane loads its row's vectors (one 1 KiB
-// coalesced wave load per vector) one chunk ahead of use, and the wave widens
-// the chunk of its hidden rows to float64 into a double-buffered LDS slot.
+// Per chunk of 64 dims each lane loads its tile row's vectors (one 1 KiB
+// coalesced wave load per vector) one chunk ahead of use, and four
+// consecutive elements of each hidden row: lane l of every 16-lane row holds
+// elements 4l..4l+3 of the chunk, widened to float64, and element k reaches
+// every lane by a 64-bit DPP broadcast from lane k/4 of its row.
 template <typename T, int RB>
-__device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid, int d,
+__device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
                                          const T* __restrict__ h, const int (&rows)[RB], int nrows,
-                                         double (&acc)[RB], v2d (&lds)[2][RB * kChunk / 2]) {
+                                         double (&acc)[RB]) {
   constexpr int PV = Elem<T>::kPerVec;
   constexpr int VPC = kChunk / PV;              // weight vectors per chunk
-  using HS = HStage<T, RB>;
+  using HR = typename HQuad<T>::raw;
   const int lane = threadIdx.x;
-  (void)nvalid;
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = 0.0;
-
-  // hidden-row raw loads: vector hv = lane + 64 i covers row hv / kVecPerRow
-  // (slots of rows >= nrows load a valid row and are never read back)
-  const char* hbase = reinterpret_cast<const char*>(h);
-  uint32_t hoff[HS::kLoads];
-  int hslot[HS::kLoads];
+  const T* hp[RB];
 #pragma unroll
-  for (int i = 0; i < HS::kLoads; ++i) {
-    const int hv = lane + kWave * i;
-    const int r = hv / HS::kVecPerRow;
-    const int part = hv % HS::kVecPerRow;
-    int row = rows[0];
-#pragma unroll
-    for (int q = 0; q < RB; ++q)
-      if (q == r) row = rows[q];
-    hoff[i] = ((uint32_t)row * (uint32_t)d + (uint32_t)part * PV) * sizeof(T);
-    hslot[i] = (r < RB ? r : 0) * HS::kV2PerRow + part * (PV / 2);
-  }
+  for (int r = 0; r < RB; ++r) hp[r] = h + (long)rows[r] * d + 4 * (lane & 15);
 
   // Every load is unconditional (packed tiles are zero-padded to 64 rows and
   // hidden-row slots are clamped to valid rows): a load under a branch makes
@@ -190,88 +247,59 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int nvalid,
   // serialise the two stages in flight.
   struct Stage {
     v4u e[VPC];
-    v4u h[HS::kLoads];
+    HR h[RB];
   };
   auto load = [&](Stage& st, int ch) {
 #pragma unroll
     for (int p = 0; p < VPC; ++p) st.e[p] = wt[(ch * VPC + p) * kWave + lane];
-    const uint32_t hadv = (uint32_t)ch * (kChunk * sizeof(T));
 #pragma unroll
-    for (int i = 0; i < HS::kLoads; ++i)
-      st.h[i] = *reinterpret_cast<const v4u*>(hbase + hoff[i] + hadv);
+    for (int r = 0; r < RB; ++r) st.h[r] = *reinterpret_cast<const HR*>(hp[r] + ch * kChunk);
   };
-  auto park = [&](const Stage& st, int buf) {
+  auto consume = [&](const Stage& st) {
+    double hd[RB][4];
 #pragma unroll
-    for (int i = 0; i < HS::kLoads; ++i) {
-      double x[PV];
-      widen(st.h[i], x, T());
-#pragma unroll
-      for (int j = 0; j < PV / 2; ++j) lds[buf][hslot[i] + j] = v2d{x[2 * j], x[2 * j + 1]};
-    }
-  };
-  auto consume = [&](const Stage& st, int buf) {
+    for (int r = 0; r < RB; ++r) widen4(st.h[r], hd[r]);
 #pragma unroll
     for (int p = 0; p < VPC; ++p) {
       double x[PV];
       widen(st.e[p], x, T());
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (r < nrows) {
-#pragma unroll
-          for (int q = 0; q < PV / 2; ++q) {
-            const v2d hv = lds[buf][r * HS::kV2PerRow + p * (PV / 2) + q];
-            acc[r] = __builtin_fma(x[2 * q], hv.x, acc[r]);
-            acc[r] = __builtin_fma(x[2 * q + 1], hv.y, acc[r]);
-          }
-        }
-      }
+      for (int r = 0; r < RB; ++r)
+        if (r < nrows) fmac_vec_p<PV>(p, acc[r], hd[r], x);
+      // widen each vector right before its use (hoisting them all would
+      // hold a whole chunk of float64 weights in registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Two register stages: while one chunk is consumed the other is in flight;
-  // a stage is reloaded only after its weights have been consumed.  One wave
-  // per workgroup: the barrier orders this wave's LDS writes before its
-  // reads; the other LDS buffer is rewritten only after a later barrier.
-  // The steady-state loop (even chunk counts) reloads unconditionally and
-  // the last two chunks are peeled, so no load sits under a branch.
+  // Two register stages: while one chunk is consumed the other is in
+  // flight; a stage is reloaded only after it has been consumed.  The
+  // steady-state loop (even chunk counts) reloads unconditionally and the
+  // last two chunks are peeled, so no load sits under a branch.
   const int nch = d / kChunk;
   Stage s0, s1;
   if (nch == 1) {
     load(s0, 0);
-    park(s0, 0);
-    __syncthreads();
-    consume(s0, 0);
+    consume(s0);
   } else if ((nch & 1) == 0) {
     load(s0, 0);
     load(s1, 1);
     for (int ch = 0; ch < nch - 2; ch += 2) {
-      park(s0, 0);
-      __syncthreads();
-      consume(s0, 0);
+      consume(s0);
       load(s0, ch + 2);
-      park(s1, 1);
-      __syncthreads();
-      consume(s1, 1);
+      consume(s1);
       load(s1, ch + 3);
     }
-    park(s0, 0);
-    __syncthreads();
-    consume(s0, 0);
-    park(s1, 1);
-    __syncthreads();
-    consume(s1, 1);
+    consume(s0);
+    consume(s1);
   } else {
     load(s0, 0);
     load(s1, 1);
     for (int ch = 0; ch < nch; ch += 2) {
-      park(s0, 0);
-      __syncthreads();
-      consume(s0, 0);
+      consume(s0);
       if (ch + 2 < nch) load(s0, ch + 2);
       if (ch + 1 < nch) {
-        park(s1, 1);
-        __syncthreads();
-        consume(s1, 1);
+        consume(s1);
         if (ch + 3 < nch) load(s1, ch + 3);
       }
     }
@@ -285,7 +313,6 @@ template <typename T, int RB>
 __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, int Nc, int d,
                                                     const T* __restrict__ h, int B,
                                                     float* __restrict__ S, int ldS) {
-  __shared__ v2d lds[2][RB * kChunk / 2];
   const int lane = threadIdx.x;
   const int c0 = blockIdx.x * kTileTokens;
   const int r0 = blockIdx.y * RB;
@@ -296,7 +323,7 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   for (int r = 0; r < RB; ++r) rows[r] = r0 + (r < nrows ? r : nrows - 1);
   double acc[RB];
   const long tile_vecs = (long)(d / Elem<T>::kPerVec) * kWave;
-  dot_tile<T, RB>(CT + blockIdx.x * tile_vecs, nvalid, d, h, rows, nrows, acc, lds);
+  dot_tile<T, RB>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
   if (lane < nvalid) {
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -651,7 +678,6 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 
 template <typename T, int RB, int MODE>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
-  __shared__ v2d lds[2][RB * kChunk / 2];
   const int lane = threadIdx.x;
   const uint32_t tile = a.tiles[blockIdx.x];
   const int c = (int)(tile & ((1u << kTileShift) - 1u));
@@ -685,7 +711,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
       }
     }
     double acc[RB];
-    dot_tile<T, RB>(wt, nvalid, a.d, h, rows, nrows, acc, lds);
+    dot_tile<T, RB>(wt, a.d, h, rows, nrows, acc);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (r < nrows) {
@@ -704,7 +730,6 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
         }
       }
     }
-    __syncthreads();   // the next pass reuses the LDS buffers
   }
 }
 
