@@ -227,7 +227,7 @@ __device__ __forceinline__ void widen4(const v4u r, double (&x)[4]) {
 // consecutive elements of each hidden row: lane l of every 16-lane row holds
 // elements 4l..4l+3 of the chunk, widened to float64, and element k reaches
 // every lane by a 64-bit DPP broadcast from lane k/4 of its row.
-template <typename T, int RB>
+template <typename T, int RB, int NCH>
 __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
                                          const T* __restrict__ h, const int (&rows)[RB], int nrows,
                                          double (&acc)[RB]) {
@@ -273,11 +273,27 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
   };
 
   // Two register stages: while one chunk is consumed the other is in
-  // flight; a stage is reloaded only after it has been consumed.  The
-  // steady-state loop (even chunk counts) reloads unconditionally and the
-  // last two chunks are peeled, so no load sits under a branch.
-  const int nch = d / kChunk;
+  // flight; a stage is reloaded only after it has been consumed.  With the
+  // chunk count NCH known at compile time the pipeline is straight-line
+  // code; otherwise the steady-state loop (even chunk counts) reloads
+  // unconditionally and the last two chunks are peeled, so no load sits
+  // under a branch.
   Stage s0, s1;
+  if constexpr (NCH > 0) {
+    load(s0, 0);
+    if constexpr (NCH > 1) load(s1, 1);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ch += 2) {
+      consume(s0);
+      if (ch + 2 < NCH) load(s0, ch + 2);
+      if (ch + 1 < NCH) {
+        consume(s1);
+        if (ch + 3 < NCH) load(s1, ch + 3);
+      }
+    }
+    return;
+  }
+  const int nch = d / kChunk;
   if (nch == 1) {
     load(s0, 0);
     consume(s0);
@@ -309,7 +325,7 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
 // ------------------------------------------------------------------ scores
 
 // One wave per (64-centroid tile, RB rows): S[b][c] for the tile's centroids.
-template <typename T, int RB>
+template <typename T, int RB, int NCH>
 __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, int Nc, int d,
                                                     const T* __restrict__ h, int B,
                                                     float* __restrict__ S, int ldS) {
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   for (int r = 0; r < RB; ++r) rows[r] = r0 + (r < nrows ? r : nrows - 1);
   double acc[RB];
   const long tile_vecs = (long)(d / Elem<T>::kPerVec) * kWave;
-  dot_tile<T, RB>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
+  dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
   if (lane < nvalid) {
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -676,7 +692,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return __ockl_wfred_max_u64(v);
 }
 
-template <typename T, int RB, int MODE>
+template <typename T, int RB, int MODE, int NCH>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
   const uint32_t tile = a.tiles[blockIdx.x];
@@ -711,7 +727,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
       }
     }
     double acc[RB];
-    dot_tile<T, RB>(wt, a.d, h, rows, nrows, acc);
+    dot_tile<T, RB, NCH>(wt, a.d, h, rows, nrows, acc);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (r < nrows) {
@@ -807,12 +823,28 @@ hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint
   return hipGetLastError();
 }
 
-template <typename T, int RB>
-static void launch_scores_t(const PassArgs& a, hipStream_t s) {
+template <typename T, int RB, int NCH>
+static void launch_scores_n(const PassArgs& a, hipStream_t s) {
   const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
-  hipLaunchKernelGGL((scores_kernel<T, RB>), grid, dim3(64), 0, s,
+  hipLaunchKernelGGL((scores_kernel<T, RB, NCH>), grid, dim3(64), 0, s,
                      static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
                      a.S, a.ldS);
+}
+
+// Hidden sizes with a straight-line chunk pipeline; others take the generic one.
+#define CE_DISPATCH_NCH(d, CALL)          \
+  switch ((d) / kChunk) {                 \
+    case 4: CALL(4); break;               \
+    case 8: CALL(8); break;               \
+    case 16: CALL(16); break;             \
+    default: CALL(0); break;              \
+  }
+
+template <typename T, int RB>
+static void launch_scores_t(const PassArgs& a, hipStream_t s) {
+#define CE_SCORES(N) launch_scores_n<T, RB, N>(a, s)
+  CE_DISPATCH_NCH(a.d, CE_SCORES)
+#undef CE_SCORES
 }
 
 hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
@@ -874,12 +906,16 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.L = a.L;
   g.ldL = a.ldL;
   const dim3 grid(a.t.n_tiles > 0 ? a.t.n_tiles : 1);
-  auto kern = gather_kernel<T, kGatherRows, MODE>;
-  if (a.probe_start && a.probe_stop) {
-    hipExtLaunchKernelGGL(kern, grid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);
-  } else {
-    hipLaunchKernelGGL(kern, grid, dim3(64), 0, s, g);
-  }
+  auto go = [&](auto kern) {
+    if (a.probe_start && a.probe_stop) {
+      hipExtLaunchKernelGGL(kern, grid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);
+    } else {
+      hipLaunchKernelGGL(kern, grid, dim3(64), 0, s, g);
+    }
+  };
+#define CE_GATHER(N) go(gather_kernel<T, kGatherRows, MODE, N>)
+  CE_DISPATCH_NCH(a.d, CE_GATHER)
+#undef CE_GATHER
   return hipGetLastError();
 }
 
