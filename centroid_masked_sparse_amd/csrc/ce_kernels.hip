@@ -47,6 +47,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ce_internal.h"
 
 // Wavefront reductions and scans of the ROCm device library (DPP based).
@@ -176,28 +178,12 @@ __device__ __forceinline__ void fmac_vec(double& acc, const double (&hq)[4], con
       : "v"(hq[0]), "v"(hq[1]), "v"(hq[2]), "v"(hq[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]),
         "v"(x[3]), "n"(J));
 }
-// Weight vector p of a chunk (p is a constant once the loops are unrolled).
-template <int PV>
-__device__ __forceinline__ void fmac_vec_p(int p, double& acc, const double (&hq)[4],
-                                           const double (&x)[PV]) {
-  constexpr int S = PV / 4;   // lanes per vector: 2 (bf16) or 1 (fp32)
-  switch (p) {
-    case 0: fmac_vec<0 * S>(acc, hq, x); break;
-    case 1: fmac_vec<1 * S>(acc, hq, x); break;
-    case 2: fmac_vec<2 * S>(acc, hq, x); break;
-    case 3: fmac_vec<3 * S>(acc, hq, x); break;
-    case 4: fmac_vec<4 * S>(acc, hq, x); break;
-    case 5: fmac_vec<5 * S>(acc, hq, x); break;
-    case 6: fmac_vec<6 * S>(acc, hq, x); break;
-    case 7: fmac_vec<7 * S>(acc, hq, x); break;
-    case 8: fmac_vec<(8 * S) & 15>(acc, hq, x); break;
-    case 9: fmac_vec<(9 * S) & 15>(acc, hq, x); break;
-    case 10: fmac_vec<(10 * S) & 15>(acc, hq, x); break;
-    case 11: fmac_vec<(11 * S) & 15>(acc, hq, x); break;
-    case 12: fmac_vec<(12 * S) & 15>(acc, hq, x); break;
-    case 13: fmac_vec<(13 * S) & 15>(acc, hq, x); break;
-    case 14: fmac_vec<(14 * S) & 15>(acc, hq, x); break;
-    default: fmac_vec<(15 * S) & 15>(acc, hq, x); break;
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -259,17 +245,17 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
     double hd[RB][4];
 #pragma unroll
     for (int r = 0; r < RB; ++r) widen4(st.h[r], hd[r]);
-#pragma unroll
-    for (int p = 0; p < VPC; ++p) {
+    static_for<0, VPC>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
       double x[PV];
       widen(st.e[p], x, T());
 #pragma unroll
       for (int r = 0; r < RB; ++r)
-        if (r < nrows) fmac_vec_p<PV>(p, acc[r], hd[r], x);
+        if (r < nrows) fmac_vec<p * PV / 4>(acc[r], hd[r], x);
       // widen each vector right before its use (hoisting them all would
       // hold a whole chunk of float64 weights in registers)
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   // Two register stages: while one chunk is consumed the other is in
@@ -280,15 +266,21 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
   // under a branch.
   Stage s0, s1;
   if constexpr (NCH > 0) {
+    // scheduling barriers keep each stage's loads together and in order, so
+    // that waiting for one stage never waits for the next
     load(s0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (NCH > 1) load(s1, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ch = 0; ch < NCH; ch += 2) {
       consume(s0);
       if (ch + 2 < NCH) load(s0, ch + 2);
+      __builtin_amdgcn_sched_barrier(0);
       if (ch + 1 < NCH) {
         consume(s1);
         if (ch + 3 < NCH) load(s1, ch + 3);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     return;
@@ -692,6 +684,24 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return __ockl_wfred_max_u64(v);
 }
 
+// Up to RB lowest rows of `mask` (taken out of it); unused slots repeat
+// `fill`, a valid row, so that loads for them stay in bounds.
+template <int RB>
+__device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[RB], int fill) {
+  int n = 0;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    if (mask) {
+      rows[r] = __builtin_ctzll(mask);
+      mask &= mask - 1ull;
+      ++n;
+    } else {
+      rows[r] = r == 0 ? fill : rows[0];
+    }
+  }
+  return n;
+}
+
 template <typename T, int RB, int MODE, int NCH>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
@@ -704,30 +714,17 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int q = (int)(tile >> kTileShift);
   const long j0 = (long)a.offsets[c] + (long)q * kTileTokens;
   const int nvalid = (int)min((long)kTileTokens, (long)a.offsets[c + 1] - j0);
+  // the token ids are needed only after the first batch is dotted: they
+  // are waited for there, not before the tile loads go out
   int tok = 0;
-  if (MODE == kArgmax) {
-    tok = a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)];
-    pin(tok);
-  }
+  if (MODE == kArgmax) tok = a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)];
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
   const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
   const T* h = reinterpret_cast<const T*>(a.h);
 
-  while (mask) {
-    int rows[RB];
-    int nrows = 0;
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      if (mask) {
-        rows[r] = __builtin_ctzll(mask);
-        mask &= mask - 1ull;
-        ++nrows;
-      } else {
-        rows[r] = rows[0];
-      }
-    }
-    double acc[RB];
-    dot_tile<T, RB, NCH>(wt, a.d, h, rows, nrows, acc);
+  // argmax: wave maximum of the packed (ordered logit, ~token) per row,
+  // or-ed into the row's slot; forward: the candidate logits in row order
+  auto finish = [&](const int (&rows)[RB], int nrows, const double (&acc)[RB]) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (r < nrows) {
@@ -746,6 +743,20 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
         }
       }
     }
+  };
+
+  while (mask) {
+    // the tile loads are invariant across batches; keep them in the loop
+    // (hoisted, they would all be live at once)
+    uint32_t zero = 0;
+    asm volatile("" : "+s"(zero));
+    const v4u* wtb = wt + zero;
+    int rows[RB];
+    const int nrows = take_rows<RB>(mask, rows, 0);
+    double acc[RB];
+    dot_tile<T, RB, NCH>(wtb, a.d, h, rows, nrows, acc);
+    if (MODE == kArgmax) pin(tok);   // keep the load out of the branches below
+    finish(rows, nrows, acc);
   }
 }
 
