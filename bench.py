@@ -84,6 +84,43 @@ def _time_replays(torch, graphs, steps, warmup, stream_handle):
     return start.elapsed_time(stop) / steps
 
 
+def _device_us_per_call(torch, heads, hs, K, B, steps, warmup, per_graph=8):
+    """Cold calls per microsecond of device time: ``per_graph`` consecutive calls
+    (rotating weight copies and row groups) captured into one graph, so the
+    host cost of a graph launch is spread over them."""
+    dev = "cuda:0"
+    graphs, keep = [], []
+    for r in range(len(heads)):
+        outs = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(per_graph)]
+        calls = [(heads[(r + m) % len(heads)], hs[(r * per_graph + m) % len(hs)], outs[m])
+                 for m in range(per_graph)]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for head, hg, o in calls:   # first use allocates each head's workspace
+                head.top_tokens(hg, K, out=o)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for head, hg, o in calls:
+                head.top_tokens(hg, K, out=o)
+        graphs.append(g)
+        keep.append(outs)
+    n = max(20, steps // per_graph)
+    for i in range(max(2, warmup // per_graph)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (n * per_graph)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,12 +202,14 @@ def main() -> int:
         ms_cold = _time_replays(torch, graphs_cold, args.steps, args.warmup, stream)
         ms_warm = _time_replays(torch, graphs_warm, args.steps, args.warmup, stream)
         us = ms_cold * 1e3
+        dev_us = _device_us_per_call(torch, heads, hs, K, B, args.steps, args.warmup)
         row = {
             "B": B, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
             "unique_MiB": round(unique / 2**20, 2), "union_clusters": round(clusters, 1),
             "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
             "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "warm_us_per_call": round(ms_warm * 1e3, 3),
+            "device_us_per_call": round(dev_us, 3),
             "row_groups": len(hs), "copies": len(heads),
         }
         sweep.append(row)

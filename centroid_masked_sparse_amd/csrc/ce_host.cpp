@@ -13,7 +13,6 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
-#include <functional>
 #include <new>
 #include <string>
 #include <vector>
@@ -27,10 +26,7 @@ struct ce_head {
   const void* E = nullptr;
   std::vector<int32_t> offsets;       // [Nc+1]
   std::vector<int32_t> tos;           // [V]
-  std::vector<int32_t> tok_cluster;   // [V]
-  std::vector<int32_t> tok_rank;      // [V]
   std::vector<uint32_t> tiles;        // every 64-slot tile: (index in cluster << 13) | cluster
-  std::vector<long long> cand_top;    // cand_top[K] = tokens owned by the K largest clusters
   bool prepared = false;
   ce::Tables tables{};
 };
@@ -63,8 +59,7 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
-  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, rowpos = 0, logits = 0, total = 0;
-  int ldL = 0;
+  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, total = 0;
 };
 
 Layout make_layout(const ce_head* h, int B, int K, int op) {
@@ -84,18 +79,13 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   L.topk = take(nb * (size_t)K * sizeof(int32_t));
   L.cl_sel = take(((size_t)h->Nc + 63) / 64 * ce::kPassRows * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
-  if (op == CE_OP_MASKED_LOGITS) {
-    L.rowpos = take(nb * h->Nc * sizeof(int32_t));
-    L.ldL = (int)h->cand_top[K];
-    L.logits = take(nb * (size_t)std::max(L.ldL, 1) * sizeof(float));
-  }
   L.total = off;
   return L;
 }
 
 // Offsets of the four device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t offsets, tos, tok_cluster, tok_rank, tiles, et, ct, total;
+  size_t offsets, tos, tiles, et, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -108,8 +98,6 @@ PersistLayout persist_layout(const ce_head* h) {
   };
   p.offsets = take(((size_t)h->Nc + 1) * sizeof(int32_t));
   p.tos = take((size_t)h->V * sizeof(int32_t));
-  p.tok_cluster = take((size_t)h->V * sizeof(int32_t));
-  p.tok_rank = take((size_t)h->V * sizeof(int32_t));
   p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
   const size_t tile_bytes = (size_t)ce::kTileTokens * h->d * elem_bytes(h->dtype);
   p.et = take(h->tiles.size() * tile_bytes);
@@ -148,9 +136,6 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.ldK = a.K;
   a.cl_sel = reinterpret_cast<unsigned long long*>(ws + L.cl_sel);
   a.best = reinterpret_cast<unsigned long long*>(ws + L.best);
-  a.rowpos = reinterpret_cast<int32_t*>(ws + L.rowpos);
-  a.L = reinterpret_cast<float*>(ws + L.logits);
-  a.ldL = L.ldL;
 }
 
 // The shared sequence of ce_top_tokens and ce_masked_logits, in passes of at
@@ -193,9 +178,9 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
     }
     const bool masked = op == CE_OP_MASKED_LOGITS;
     hipError_t e = ce::launch_scores(a, stream);
-    if (e == hipSuccess) e = ce::launch_topk(a, masked ? ce::kTopkMarkRowpos : ce::kTopkMark, stream);
+    if (e == hipSuccess) e = ce::launch_topk(a, ce::kTopkMark, stream);
     if (e == hipSuccess) e = ce::launch_gather(a, masked ? ce::kMasked : ce::kArgmax, stream);
-    if (e == hipSuccess) e = masked ? ce::launch_writer(a, stream) : ce::launch_finalize(a, stream);
+    if (e == hipSuccess && !masked) e = ce::launch_finalize(a, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
   }
   return CE_SUCCESS;
@@ -251,23 +236,18 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
       for (int c = 0; c <= Nc; ++c) h->offsets[c] = (int32_t)((long long)c * (V / Nc));
     }
     h->tos.assign(desc->token_of_slot, desc->token_of_slot + V);
-    h->tok_cluster.assign((size_t)V, -1);
-    h->tok_rank.assign((size_t)V, 0);
-    for (int c = 0; c < Nc; ++c) {
-      for (int j = h->offsets[c]; j < h->offsets[c + 1]; ++j) {
-        const int32_t t = h->tos[j];
-        if (t < 0 || t >= V || h->tok_cluster[t] != -1) {
-          delete h;
-          return fail(CE_ERR_BAD_LAYOUT, "token_of_slot must be a permutation of 0..V-1");
-        }
-        h->tok_cluster[t] = c;
-        h->tok_rank[t] = j - h->offsets[c];
+    std::vector<char> seen((size_t)V, 0);
+    for (int j = 0; j < V; ++j) {
+      const int32_t t = h->tos[j];
+      if (t < 0 || t >= V || seen[t]) {
+        delete h;
+        return fail(CE_ERR_BAD_LAYOUT, "token_of_slot must be a permutation of 0..V-1");
       }
+      seen[t] = 1;
     }
-    std::vector<long long> sizes(Nc);
     for (int c = 0; c < Nc; ++c) {
-      sizes[c] = h->offsets[c + 1] - h->offsets[c];
-      const long long nt = (sizes[c] + ce::kTileTokens - 1) / ce::kTileTokens;
+      const long long size = h->offsets[c + 1] - h->offsets[c];
+      const long long nt = (size + ce::kTileTokens - 1) / ce::kTileTokens;
       if (nt > ce::kMaxTilesPerCluster) {
         delete h;
         return fail(CE_ERR_UNSUPPORTED, "a cluster holds more than 2^19 * 64 tokens");
@@ -275,9 +255,6 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
       for (long long q = 0; q < nt; ++q)
         h->tiles.push_back(((uint32_t)q << ce::kTileShift) | (uint32_t)c);
     }
-    std::sort(sizes.begin(), sizes.end(), std::greater<long long>());
-    h->cand_top.assign((size_t)Nc + 1, 0);
-    for (int k = 0; k < Nc; ++k) h->cand_top[k + 1] = h->cand_top[k] + sizes[k];
   } catch (const std::bad_alloc&) {
     delete h;
     return fail(CE_ERR_UNSUPPORTED, "out of host memory");
@@ -306,8 +283,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   struct Copy {
     size_t at;
     const std::vector<int32_t>* v;
-  } copies[] = {{p.offsets, &head->offsets}, {p.tos, &head->tos},
-                {p.tok_cluster, &head->tok_cluster}, {p.tok_rank, &head->tok_rank}};
+  } copies[] = {{p.offsets, &head->offsets}, {p.tos, &head->tos}};
   for (const Copy& c : copies) {
     hipError_t e = hipMemcpyAsync(base + c.at, c.v->data(), c.v->size() * sizeof(int32_t),
                                   hipMemcpyHostToDevice, stream);
@@ -331,8 +307,6 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
   head->tables.offsets = reinterpret_cast<const int32_t*>(base + p.offsets);
   head->tables.tos = reinterpret_cast<const int32_t*>(base + p.tos);
-  head->tables.tok_cluster = reinterpret_cast<const int32_t*>(base + p.tok_cluster);
-  head->tables.tok_rank = reinterpret_cast<const int32_t*>(base + p.tok_rank);
   head->tables.tiles = reinterpret_cast<const uint32_t*>(base + p.tiles);
   head->tables.n_tiles = (int)head->tiles.size();
   head->tables.ET = base + p.et;

@@ -19,8 +19,6 @@ constexpr int kMaxD = 8192;
 struct Tables {
   const int32_t* offsets;      // [Nc+1] cluster c owns slots [offsets[c], offsets[c+1])
   const int32_t* tos;          // [V] token id of each slot
-  const int32_t* tok_cluster;  // [V] cluster owning each token
-  const int32_t* tok_rank;     // [V] slot of each token minus its cluster's first slot
   const uint32_t* tiles;       // [n_tiles] every 64-slot tile of every cluster, cluster-major
   int n_tiles;
   const void* ET;              // packed embeddings: [n_tiles][d/vec][64] 16-byte vectors
@@ -28,10 +26,9 @@ struct Tables {
 };
 
 enum GatherMode { kArgmax = 0, kMasked = 1 };
-// What the top-K kernel writes besides the ids: nothing, the rows' selection
-// words and cleared argmax slots (get_top_tokens), or the selection words and
-// candidate positions (forward).
-enum TopkMode { kTopkOnly = 1, kTopkMark = 2, kTopkMarkRowpos = 3 };
+// What the top-K kernel writes besides the ids: nothing, or the rows'
+// selection words (and, given `best`, cleared argmax slots).
+enum TopkMode { kTopkOnly = 1, kTopkMark = 2 };
 
 // Everything one pass (at most kPassRows rows) needs.
 struct PassArgs {
@@ -49,12 +46,9 @@ struct PassArgs {
   int ldK;
   unsigned long long* cl_sel;   // [ceil(Nc/64)][kPassRows] bit i of word (w, b): row b selected 64w+i
   unsigned long long* best;     // [kPassRows] packed (ordered logit, ~token)
-  int32_t* rowpos;        // [B][Nc] first candidate position of a centroid in a row, or -1
-  float* L;               // [B][ldL] candidate logits in row order
-  int ldL;
   // outputs
   int32_t* tokens;        // [B]
-  float* logits;          // [B][V]
+  float* logits;          // [B][V] forward output; the scores kernel fills it with -inf
   // measurement hook (HIP extended launch around the gather kernel)
   hipEvent_t probe_start;
   hipEvent_t probe_stop;
@@ -67,6 +61,5 @@ hipError_t launch_scores(const PassArgs& a, hipStream_t s);
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: TopkMode
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
-hipError_t launch_writer(const PassArgs& a, hipStream_t s);
 
 }  // namespace ce

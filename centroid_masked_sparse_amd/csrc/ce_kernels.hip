@@ -316,16 +316,41 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
 
 // ------------------------------------------------------------------ scores
 
-// One wave per (64-centroid tile, RB rows): S[b][c] for the tile's centroids.
+// Fill rows [r0, r0+nrows) of out ([*][V] fp32) with -inf over this
+// workgroup's share of the columns (forward: every entry that no candidate
+// overwrites).  Plain streaming stores; nothing waits on them.
+__device__ __forceinline__ void fill_neg_inf(float* __restrict__ out, int V, int r0, int nrows) {
+  const int lane = threadIdx.x;
+  const long per = ((long)V + gridDim.x - 1) / gridDim.x;
+  const long per4 = (per + 3) & ~3L;
+  const long c0 = (long)blockIdx.x * per4;
+  const long c1 = min((long)V, c0 + per4);
+  const float ninf = -__builtin_inff();
+  for (int r = 0; r < nrows; ++r) {
+    float* row = out + (long)(r0 + r) * V;
+    if ((V & 3) == 0) {
+      for (long c = c0 + 4 * lane; c < c1; c += 4 * kWave)
+        *reinterpret_cast<float4*>(row + c) = make_float4(ninf, ninf, ninf, ninf);
+    } else {
+      for (long c = c0 + lane; c < c1; c += kWave) row[c] = ninf;
+    }
+  }
+}
+
+// One wave per (64-centroid tile, RB rows): S[b][c] for the tile's
+// centroids; with `fill` (forward) the wave also fills its share of the
+// output rows with -inf.
 template <typename T, int RB, int NCH>
 __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, int Nc, int d,
                                                     const T* __restrict__ h, int B,
-                                                    float* __restrict__ S, int ldS) {
+                                                    float* __restrict__ S, int ldS,
+                                                    float* __restrict__ fill, int V) {
   const int lane = threadIdx.x;
   const int c0 = blockIdx.x * kTileTokens;
   const int r0 = blockIdx.y * RB;
   const int nvalid = min(kTileTokens, Nc - c0);
   const int nrows = min(RB, B - r0);
+  if (fill) fill_neg_inf(fill, V, r0, nrows);
   int rows[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) rows[r] = r0 + (r < nrows ? r : nrows - 1);
@@ -417,7 +442,7 @@ __device__ __forceinline__ uint32_t cand_kth(const uint32_t* cand, int n, uint32
   return T;
 }
 
-enum SelectMode { kSelIds = 1, kSelMark = 2, kSelRowpos = 3 };
+enum SelectMode { kSelIds = 1, kSelMark = 2 };
 
 struct TopkArgs {
   const float* S;
@@ -425,9 +450,7 @@ struct TopkArgs {
   int32_t* out;                    // [rows][ldK] ascending ids
   int ldK;
   unsigned long long* cl_sel;      // [ceil(Nc/64)][64]: bit i of word (w, b) = row b selected 64w+i
-  int32_t* rowpos;                 // [rows][Nc]
-  const int32_t* offsets;          // [Nc+1]
-  unsigned long long* best;        // [64] argmax slots, cleared per row
+  unsigned long long* best;        // [64] argmax slots, cleared per row (or null)
 };
 
 // Number of the values vals[0..n) (LDS, read as broadcasts; n a multiple
@@ -637,30 +660,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     __syncthreads();
     for (int w = tid; w < nwords; w += kTopkThreads) a.cl_sel[(long)w * kWave + b] = words[w];
   }
-  if (MODE == kSelMark && tid == 0) a.best[b] = 0ull;
-  if (MODE == kSelRowpos) {
-    uint32_t local = 0;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-      if (sel & (1u << i)) {
-        const int c = first + i;
-        local += (uint32_t)(a.offsets[c + 1] - a.offsets[c]);
-      }
-    uint32_t run = block_excl_scan(local, scan_sh, &tot);
-    int32_t* rp = a.rowpos + (long)b * Nc;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const int c = first + i;
-      if (c < Nc) {
-        if (sel & (1u << i)) {
-          rp[c] = (int32_t)run;
-          run += (uint32_t)(a.offsets[c + 1] - a.offsets[c]);
-        } else {
-          rp[c] = -1;
-        }
-      }
-    }
-  }
+  if (MODE == kSelMark && a.best && tid == 0) a.best[b] = 0ull;
 }
 
 // ------------------------------------------------------------------ gather
@@ -674,10 +674,9 @@ struct GatherArgs {
   const unsigned long long* cl_sel;
   int B;
   const uint32_t* tiles;
-  unsigned long long* best;
-  const int32_t* rowpos;
-  float* L;
-  int ldL;
+  unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row
+  float* out;                   // forward: [B][V] output rows (already -inf)
+  int V;
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -716,14 +715,14 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int nvalid = (int)min((long)kTileTokens, (long)a.offsets[c + 1] - j0);
   // the token ids are needed only after the first batch is dotted: they
   // are waited for there, not before the tile loads go out
-  int tok = 0;
-  if (MODE == kArgmax) tok = a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)];
+  int tok = a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)];
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
   const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
   const T* h = reinterpret_cast<const T*>(a.h);
 
   // argmax: wave maximum of the packed (ordered logit, ~token) per row,
-  // or-ed into the row's slot; forward: the candidate logits in row order
+  // max-ed into the row's slot; forward: each candidate logit stored at its
+  // token's column
   auto finish = [&](const int (&rows)[RB], int nrows, const double (&acc)[RB]) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -736,10 +735,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
           k = wave_max_u64(k);
           if (lane == 0) atomicMax(&a.best[rows[r]], k);   // result unused: no stall
         } else {
-          if (lane < nvalid) {
-            const int p = a.rowpos[(long)rows[r] * a.Nc + c];
-            a.L[(long)rows[r] * a.ldL + p + q * kTileTokens + lane] = f;
-          }
+          if (lane < nvalid) a.out[(long)rows[r] * a.V + tok] = f;
         }
       }
     }
@@ -755,7 +751,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     const int nrows = take_rows<RB>(mask, rows, 0);
     double acc[RB];
     dot_tile<T, RB, NCH>(wtb, a.d, h, rows, nrows, acc);
-    if (MODE == kArgmax) pin(tok);   // keep the load out of the branches below
+    pin(tok);   // keep the load out of the branches below
     finish(rows, nrows, acc);
   }
 }
@@ -770,52 +766,6 @@ __global__ __launch_bounds__(64) void finalize_kernel(const unsigned long long* 
     tokens[b] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
   }
 }
-
-// ------------------------------------------------------------------ writer
-
-constexpr int kWriterRows = 8;
-
-// out[b][t] for 4 consecutive tokens t and kWriterRows rows per thread:
-// the candidate logit when t's centroid is selected by row b, else -inf.
-__global__ __launch_bounds__(256) void writer_kernel(float* __restrict__ out, int B, int V, int Nc,
-                                                     const int32_t* __restrict__ tok_cluster,
-                                                     const int32_t* __restrict__ tok_rank,
-                                                     const int32_t* __restrict__ rowpos,
-                                                     const float* __restrict__ L, int ldL) {
-  const long t0 = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (t0 >= V) return;
-  const int n = (int)min(4L, (long)V - t0);
-  int cl[4], rk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    cl[i] = i < n ? tok_cluster[t0 + i] : 0;
-    rk[i] = i < n ? tok_rank[t0 + i] : 0;
-  }
-  const int b0 = blockIdx.y * kWriterRows;
-  const bool vec = (n == 4) && ((V & 3) == 0);
-#pragma unroll
-  for (int rr = 0; rr < kWriterRows; ++rr) {
-    const int b = b0 + rr;
-    if (b < B) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = -__builtin_inff();
-        if (i < n) {
-          const int p = rowpos[(long)b * Nc + cl[i]];
-          if (p >= 0) v[i] = L[(long)b * ldL + p + rk[i]];
-        }
-      }
-      float* o = out + (long)b * V + t0;
-      if (vec) {
-        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        for (int i = 0; i < n; ++i) o[i] = v[i];
-      }
-    }
-  }
-}
-
 
 }  // namespace
 
@@ -839,7 +789,7 @@ static void launch_scores_n(const PassArgs& a, hipStream_t s) {
   const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
   hipLaunchKernelGGL((scores_kernel<T, RB, NCH>), grid, dim3(64), 0, s,
                      static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
-                     a.S, a.ldS);
+                     a.S, a.ldS, a.logits, a.V);
 }
 
 // Hidden sizes with a straight-line chunk pipeline; others take the generic one.
@@ -872,10 +822,8 @@ template <int EPT>
 static void launch_topk_ept(const TopkArgs& t, int B, int mode, hipStream_t s) {
   if (mode == kTopkOnly)
     hipLaunchKernelGGL((topk_kernel<EPT, kSelIds>), dim3(B), dim3(kTopkThreads), 0, s, t);
-  else if (mode == kTopkMark)
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
   else
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelRowpos>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
 }
 
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
@@ -887,8 +835,6 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.out = a.topk;
   t.ldK = a.ldK;
   t.cl_sel = a.cl_sel;
-  t.rowpos = a.rowpos;
-  t.offsets = a.t.offsets;
   t.best = a.best;
   const int ept = (a.Nc + kTopkThreads - 1) / kTopkThreads;
   if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, s);
@@ -913,9 +859,8 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.B = a.B;
   g.tiles = a.t.tiles;
   g.best = a.best;
-  g.rowpos = a.rowpos;
-  g.L = a.L;
-  g.ldL = a.ldL;
+  g.out = a.logits;
+  g.V = a.V;
   const dim3 grid(a.t.n_tiles > 0 ? a.t.n_tiles : 1);
   auto go = [&](auto kern) {
     if (a.probe_start && a.probe_stop) {
@@ -944,11 +889,5 @@ hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_writer(const PassArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.V + 1023) / 1024), (unsigned)((a.B + kWriterRows - 1) / kWriterRows));
-  hipLaunchKernelGGL(writer_kernel, grid, dim3(256), 0, s, a.logits, a.B, a.V, a.Nc,
-                     a.t.tok_cluster, a.t.tok_rank, a.rowpos, a.L, a.ldL);
-  return hipGetLastError();
-}
 
 }  // namespace ce
