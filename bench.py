@@ -121,6 +121,75 @@ def _device_us_per_call(torch, heads, hs, K, B, steps, warmup, per_graph=8):
     return a.elapsed_time(b) * 1e3 / (n * per_graph)
 
 
+def _wide_section(torch, args, stream, log):
+    """The wide head at B=64: the sparse head at K=64 and at K=Nc (every
+    centroid: the exact dense argmax), beside a dense comparison path, the
+    vendor bf16 GEMM (fp32 output) of all V logits followed by an argmax.
+    Cold over two weight copies."""
+    from centroid_masked_sparse_amd import OP_TOP_TOKENS, Head
+    from workloads import make_workload
+    w = make_workload(4)
+    d, V, Nc, K, B = w.d, w.V, w.Nc, w.K, 64
+    sizes = w.sizes
+    ncopy = 2
+    C0 = _to_device(w.C, w.dtype, torch)
+    E0 = _to_device(w.E, w.dtype, torch)
+    H = _to_device(w.h, w.dtype, torch)[:B].contiguous()
+    heads = [Head(C0 if m == 0 else C0.clone(), E0 if m == 0 else E0.clone(), w.tos,
+                  max_B=B, max_K=Nc) for m in range(ncopy)]
+    out = {"workload": f"wide head d={d} V={V} Nc={Nc} bf16, B={B}, cold ({ncopy} weight copies)"}
+    for k in (K, Nc):
+        topk = torch.empty((B, k), dtype=torch.int32, device="cuda:0")
+        heads[0].top_tokens(H, k, topk_out=topk)
+        torch.cuda.synchronize()
+        slab, _ = _union_bytes(topk.cpu().numpy(), sizes, d, 2)
+        unique = Nc * d * 2 + slab
+        outs = [torch.empty((B,), dtype=torch.int32, device="cuda:0") for _ in heads]
+        graphs = [hd.capture(OP_TOP_TOKENS, H, k, o) for hd, o in zip(heads, outs)]
+        ms = _time_replays(torch, graphs, max(50, args.steps // 8), max(5, args.warmup // 8), stream)
+        us = ms * 1e3
+        out[f"sparse_K{k}"] = {"us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
+                               "unique_MiB": round(unique / 2**20, 2),
+                               "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
+                               "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        for g in graphs:
+            g.close()
+        log(f"[bench] wide sparse K={k}: {out[f'sparse_K{k}']}")
+    # dense comparison: E in token order, logits^T = E_tok @ h^T (fp32 out)
+    inv = torch.from_numpy(np.argsort(w.tos).astype(np.int64)).to("cuda:0")
+    E_tok = [E0.index_select(0, inv).contiguous()]
+    E_tok.append(E_tok[0].clone())
+    hT = H.t().contiguous()
+    del heads, E0, C0
+    torch.cuda.empty_cache()
+
+    def dense(e):
+        return torch.argmax(torch.mm(e, hT, out_dtype=torch.float32), dim=0)
+
+    for i in range(3):
+        dense(E_tok[i % 2])
+    torch.cuda.synchronize()
+    n = max(20, args.steps // 20)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        dense(E_tok[i % 2])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n
+    dense_bytes = V * d * 2
+    out["dense_gemm_argmax"] = {
+        "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
+        "bytes_MiB": round(dense_bytes / 2**20, 1), "GB_s": round(dense_bytes / (us * 1e-6) / 1e9, 1),
+        "tflops": round(2.0 * B * d * V / (us * 1e-6) / 1e12, 2),
+        "path": "vendor bf16 GEMM (torch.mm, fp32 out) of all V logits + argmax; eager, not captured"}
+    log(f"[bench] wide dense comparison: {out['dense_gemm_argmax']}")
+    del E_tok
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +198,7 @@ def main() -> int:
     ap.add_argument("--batches", default="1,2,4,8,16,32,64")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-masked", action="store_true")
+    ap.add_argument("--no-wide", action="store_true")
     ap.add_argument("--probe-calls", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,6 +346,11 @@ def main() -> int:
             del per_copy
             torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ wide head (d=1024, Nc=4096)
+    wide = None
+    if not args.no_wide:
+        wide = _wide_section(torch, args, stream, log)
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -322,6 +397,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "sweep": sweep,
         "masked": masked,
+        "wide": wide,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -64,8 +64,18 @@ def test_masked_config_full_rows(sweep):
         assert np.all(np.isfinite(M).sum(axis=1) == w.K * (w.V // w.Nc))
 
 
-def test_wide_config_K64_and_full_K():
+WIDE_SAMPLE = [0, 17, 42, 63]
+
+
+@pytest.fixture(scope="module")
+def wide():
     w = make_workload(4)
+    D = oracle.dense_logits(rows(w, 64)[WIDE_SAMPLE], w.E, w.tos, w.dtype)
+    return w, D
+
+
+def test_wide_config_K64_and_full_K(wide):
+    w, D = wide
     head = make_head(w)
     tok_o, sel_o, _ = oracle.top_tokens(rows(w, 64), w.C, w.E, w.offsets, w.tos, w.K, w.dtype)
     tok, tk = _run_tokens(head, w, 64, w.K)
@@ -73,9 +83,39 @@ def test_wide_config_K64_and_full_K():
     assert tok.tolist() == tok_o.tolist()
     # K = Nc: every centroid is selected, so the sparse argmax is the dense one
     tok_full, _ = _run_tokens(head, w, 64, w.Nc)
-    sample = [0, 17, 42, 63]
-    D = oracle.dense_logits(rows(w, 64)[sample], w.E, w.tos, w.dtype)
-    assert tok_full[sample].tolist() == np.argmax(D, axis=1).tolist()
+    assert tok_full[WIDE_SAMPLE].tolist() == np.argmax(D, axis=1).tolist()
+
+
+def test_wide_dense_comparison_path(wide):
+    """The dense comparison path the benchmark times (vendor bf16 GEMM with
+    fp32 output over all V tokens, then argmax) against the oracle's dense
+    argmax.  Its fp32 sums follow the library's order, so a row is checked
+    only where the oracle's two best logits differ by more than twice the
+    worst-case fp32 summation error, d*2^-24/(1-d*2^-24) * sum|h_k e_k| plus
+    an ulp, of either token."""
+    torch = torch_mod()
+    w, D = wide
+    inv = np.argsort(w.tos)
+    E_tok = to_device(np.ascontiguousarray(w.E[inv]), w.dtype)
+    h = to_device(rows(w, 64), w.dtype)
+    tok = torch.argmax(torch.mm(E_tok, h.t().contiguous(), out_dtype=torch.float32), dim=0)
+    tok = tok.cpu().numpy()
+    del E_tok
+    H64 = oracle.upcast(rows(w, 64)[WIDE_SAMPLE], w.dtype)
+    u = 2.0 ** -24
+    gamma = w.d * u / (1 - w.d * u)
+    checked = 0
+    for i, b in enumerate(WIDE_SAMPLE):
+        order = np.argsort(-D[i], kind="stable")
+        t1, t2 = int(order[0]), int(order[1])
+        bound = 0.0
+        for t in (t1, t2):
+            e = oracle.upcast(w.E[inv[t]][None, :], w.dtype)[0]
+            bound = max(bound, gamma * float(np.abs(H64[i] * e).sum()) + u * abs(float(D[i][t])))
+        if float(D[i][t1]) - float(D[i][t2]) > 2 * bound:
+            assert int(tok[b]) == t1, (b, int(tok[b]), t1)
+            checked += 1
+    assert checked >= 1
 
 
 def test_skewed_config():
