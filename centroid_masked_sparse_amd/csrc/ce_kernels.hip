@@ -13,22 +13,22 @@
 // v of a row, the vectors of its 64 rows side by side, [t][v][lane].  Lane l
 // of a wave then reads its own row's next 8 bf16 (or 4 fp32) elements while
 // the wave reads 1 KiB of contiguous memory, so slabs stream from HBM straight
-// into registers, fully coalesced, and LDS only carries the hidden rows.
+// into registers, fully coalesced.
 //
 // One pass handles at most 64 rows and runs these kernels in stream order:
-//   scores   centroid projection S[b][c] (canonical dot, see below); also
-//            clears the per-centroid row masks and the argmax slots
-//   topk     one workgroup per row: radix select of the K best centroids; the
-//            row's bit is or-ed into the mask of every centroid it selected
+//   scores   centroid projection S[b][c] (canonical dot, see below); for
+//            forward it also fills the output rows with -inf
+//   topk     one workgroup per row: the K best centroids (a threshold from
+//            the waves' maxima, then parallel rank counts among the keys
+//            above it); writes the ids and the row's 64-centroid selection
+//            words
 //   gather   one wave per 64-token tile of the static tile list; a tile whose
 //            centroid no row selected exits at once, so each selected slab is
 //            read exactly once however many rows share it (cross-row dedup).
-//            The tile is dotted with every row in its mask, then reduced to a
-//            per-row packed argmax (64-bit atomicMax) or stored as candidate
-//            logits
+//            The tile is dotted with every row that selected it, then reduced
+//            to a per-row packed argmax (64-bit atomicMax) or stored at the
+//            candidates' token columns of the forward rows
 //   finalize (get_top_tokens) decode the packed argmax into token ids
-//   writer   (forward) one coalesced pass over [B][V]: -inf or the candidate
-//            logit of each token
 //
 // No kernel waits on another workgroup and none uses a device-scope fence:
 // on a multi-XCD part such a fence writes back the L2, so results travel
