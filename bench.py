@@ -2,10 +2,14 @@
 
 Workload: the greedy sweep (d=256, V=262144, Nc=2048 equal clusters of 128,
 K=32, bf16 inputs, synthetic seeded data).  A step is one ``top_tokens`` call
-(centroid projection, top-K, deduplicated slab gather, sparse dot, argmax)
-replayed from a captured HIP graph, at B=64 for the headline ``value``; the
-line also carries every batch size of the sweep and the masked full-vocabulary
-output (forward) at B in {1, 16, 64}.
+(centroid projection, top-K, deduplicated slab gather, sparse dot, argmax) at
+B=64 for the headline ``value``, issued straight through the C ABI (four
+kernel launches).  Each sweep row also reports the same call replayed from a
+captured HIP graph (the pages' sequencing; on ROCm a graph launch costs more
+host and device time than the four launches it replaces) and the device time
+per call with eight calls captured in one graph.  The line also carries every
+batch size of the sweep, the masked full-vocabulary output (forward) at B in
+{1, 16, 64} (graph replays) and the wide head with its dense comparison path.
 
 Cold HBM: every step uses a different copy of the weights (``--copies``,
 default 8, about 1 GiB) and, for B < 64, a different group of hidden rows, so
@@ -82,6 +86,36 @@ def _time_replays(torch, graphs, steps, warmup, stream_handle):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
+
+
+def _eager_us_per_call(torch, heads, hs, K, B, steps, warmup, stream):
+    """Cold eager calls: ce_top_tokens straight through the C ABI (four kernel
+    launches), rotating weight copies and row groups like the graph replays."""
+    from centroid_masked_sparse_amd import OP_TOP_TOKENS
+    calls = []
+    for s_ in range(len(hs)):
+        for head in heads:
+            out = torch.empty((B,), dtype=torch.int32, device="cuda:0")
+            ws = head._workspace(B, K, OP_TOP_TOKENS)
+            calls.append((head._lib.ce_top_tokens,
+                          (head._handle, hs[s_].data_ptr(), B, K, out.data_ptr(), None,
+                           ws.data_ptr(), ws.numel(), stream), out))
+    n = len(calls)
+    for i in range(max(warmup, n)):
+        f, a, _ = calls[i % n]
+        st = f(*a)
+        if st != 0:
+            raise RuntimeError(f"ce_top_tokens failed with status {st}")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        f, a, _ = calls[i % n]
+        f(*a)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / steps
 
 
 def _device_us_per_call(torch, heads, hs, K, B, steps, warmup, per_graph=8):
@@ -271,14 +305,16 @@ def main() -> int:
         graphs_warm = [per_copy[0][0]]
         ms_cold = _time_replays(torch, graphs_cold, args.steps, args.warmup, stream)
         ms_warm = _time_replays(torch, graphs_warm, args.steps, args.warmup, stream)
-        us = ms_cold * 1e3
+        graph_us = ms_cold * 1e3
         dev_us = _device_us_per_call(torch, heads, hs, K, B, args.steps, args.warmup)
+        us = _eager_us_per_call(torch, heads, hs, K, B, args.steps, args.warmup, stream)
         row = {
             "B": B, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
             "unique_MiB": round(unique / 2**20, 2), "union_clusters": round(clusters, 1),
             "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
             "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "warm_us_per_call": round(ms_warm * 1e3, 3),
+            "graph_us_per_call": round(graph_us, 3),
+            "graph_warm_us_per_call": round(ms_warm * 1e3, 3),
             "device_us_per_call": round(dev_us, 3),
             "row_groups": len(hs), "copies": len(heads),
         }
@@ -387,6 +423,7 @@ def main() -> int:
         "config": {"workload": f"greedy sweep d={d} V={V} Nc={Nc} K={K} bf16, B={Bp}, cold HBM "
                                f"({len(heads)} weight copies, {head_row['row_groups']} row groups)",
                    "B": Bp, "d": d, "V": V, "Nc": Nc, "K": K, "inputs": "bf16",
+                   "calls": "eager C-ABI calls (graph replays reported per row)",
                    "accumulate": "f64 canonical chain, fp32 results"},
         "hbm_GB_s": head_row["GB_s"],
         "hbm_frac_peak": head_row["frac_peak"],
