@@ -54,6 +54,7 @@ __all__ = [
     "select_and_score",
     "masked_logits",
     "top_tokens",
+    "top_m",
     "dense_logits",
 ]
 
@@ -184,6 +185,27 @@ def top_tokens(h, C, E, offsets, tos, K: int, dtype: str):
             tok[b] = tokens[logits == m].min()
             best[b] = m
     return tok, np.array(sels, dtype=np.int64), best
+
+
+def top_m(h, C, E, offsets, tos, K: int, m: int, dtype: str):
+    """The m best candidates of each row: ``[B, m]`` token ids and their fp32
+    logits, ordered by (logit descending, token ascending).
+
+    The next step after ``get_top_tokens`` for tree drafting or sampling: the
+    same candidates as the masked row, reduced to its m largest entries
+    without building the row.  A row with fewer than m candidates is padded
+    with token -1 and logit -inf.
+    """
+    h = np.atleast_2d(np.asarray(h))
+    B = h.shape[0]
+    tok = np.full((B, m), -1, dtype=np.int64)
+    val = np.full((B, m), -np.inf, dtype=np.float32)
+    for b in range(B):
+        logits, tokens, _ = select_and_score(h[b], C, E, offsets, tos, K, dtype)
+        order = np.lexsort((tokens, -logits.astype(np.float64)))[:m]
+        tok[b, :len(order)] = tokens[order]
+        val[b, :len(order)] = logits[order]
+    return tok, val
 
 
 def dense_logits(h, E, tos, dtype: str, chunk: int = 8192) -> np.ndarray:

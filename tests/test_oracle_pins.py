@@ -73,6 +73,24 @@ def test_golden_masked_and_dense():
     assert not np.any(D.view(np.uint32) == 0x80000000)
 
 
+def test_golden_top_m():
+    g = _golden()
+    C = np.array(g["centroids"], dtype=np.float32)
+    E = np.array(g["emb_ordered"], dtype=np.float32)
+    off = np.array(g["offsets"])
+    tos = np.array(g["token_of_slot"])
+    for b, row in enumerate(g["rows"]):
+        h = np.array([row["h"]], dtype=np.float32)
+        for key, want in row["top_m"].items():
+            if key == "derivation":
+                continue
+            K, m = int(key[1]), int(key.split("_m")[1])
+            tok, val = oracle.top_m(h, C, E, off, tos, K, m, "f32")
+            assert tok[0].tolist() == want["tokens"], (b, key)
+            wv = np.array([_as_f32(v) for v in want["logits"]], dtype=np.float32)
+            assert val[0].view(np.uint32).tolist() == wv.view(np.uint32).tolist(), (b, key)
+
+
 def test_golden_rounding_cases():
     for case in _golden()["rounding_cases"]["cases"]:
         x = np.array(case["x"], dtype=np.float32)
@@ -257,6 +275,47 @@ def test_top_token_is_argmax_of_masked_row_and_monotone_in_K():
         if prev is not None:
             assert np.all(best >= prev)
         prev = best
+
+
+def test_top_m_first_is_top_token_and_matches_masked_row():
+    """top_m against get_top_tokens (m=1) and against a brute-force reading of
+    the masked row: its finite entries ordered by (value desc, token asc)."""
+    for w in (make_random(13, d=64, V=1024, Nc=32, dtype="bf16", rows=5),
+              make_random(14, d=64, V=600, Nc=30, dtype="bf16", rows=4, ragged=True)):
+        K, m = 3, 7
+        tok1, _, best = oracle.top_tokens(w.h, w.C, w.E, w.offsets, w.tos, K, "bf16")
+        t, v = oracle.top_m(w.h, w.C, w.E, w.offsets, w.tos, K, 1, "bf16")
+        assert t[:, 0].tolist() == tok1.tolist()
+        assert v[:, 0].tolist() == best.tolist()
+        M, _ = oracle.masked_logits(w.h, w.C, w.E, w.offsets, w.tos, K, "bf16")
+        t, v = oracle.top_m(w.h, w.C, w.E, w.offsets, w.tos, K, m, "bf16")
+        for b in range(w.h.shape[0]):
+            entries = sorted((-float(M[b, x]), x) for x in range(w.V) if np.isfinite(M[b, x]))
+            want = [x for _, x in entries[:m]]
+            want += [-1] * (m - len(want))
+            assert t[b].tolist() == want, b
+            for i, x in enumerate(want):
+                if x < 0:
+                    assert np.isneginf(v[b, i])
+                else:
+                    assert v[b, i].view(np.uint32) == M[b, x].view(np.uint32)
+
+
+def test_top_m_ties_and_padding():
+    # four equal candidates: ascending token order; m above the candidate
+    # count pads with -1 / -inf
+    d = 64
+    h = np.zeros((1, d), dtype=np.float32)
+    h[0, 0] = 1.0
+    C = np.zeros((2, d), dtype=np.float32)
+    C[0, 0] = 1.0
+    E = np.zeros((8, d), dtype=np.float32)
+    E[:4, 0] = 2.0
+    off = np.array([0, 4, 8])
+    tos = np.array([6, 1, 7, 3, 0, 2, 4, 5])
+    tok, val = oracle.top_m(h, C, E, off, tos, 1, 6, "f32")
+    assert tok[0].tolist() == [1, 3, 6, 7, -1, -1]
+    assert val[0, :4].tolist() == [2.0] * 4 and np.all(np.isneginf(val[0, 4:]))
 
 
 def test_tied_logits_choose_lowest_token():
