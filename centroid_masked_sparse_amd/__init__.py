@@ -19,7 +19,8 @@ import ctypes
 import numpy as np
 
 from . import _ffi
-from ._ffi import CE_BF16, CE_F32, CE_OP_MASKED_LOGITS, CE_OP_TOP_TOKENS, CeError, check
+from ._ffi import (CE_BF16, CE_F32, CE_MAX_TOP_M, CE_OP_MASKED_LOGITS, CE_OP_TOP_M,
+                   CE_OP_TOP_TOKENS, CeError, check)
 
 __all__ = ["Head", "Graph", "CeError", "load_library"]
 
@@ -203,6 +204,25 @@ class Head:
               "ce_masked_logits")
         return out
 
+    def top_m(self, h, m: int, K: int | None = None, out=None, logits_out=None, topk_out=None):
+        """The m best candidates per row: ``([B, m]`` int32 token ids, ``[B, m]``
+        fp32 logits), ordered by logit descending then token id ascending;
+        rows with fewer than m candidates are padded with -1 / -inf."""
+        torch = _torch()
+        B = self._check_h(h)
+        K = self._k(K)
+        if out is None:
+            out = torch.empty((B, m), dtype=torch.int32, device=self.device)
+        if logits_out is None:
+            logits_out = torch.empty((B, m), dtype=torch.float32, device=self.device)
+        ws = self._workspace(B, K, CE_OP_TOP_M)
+        check(self._lib.ce_top_m(self._handle, h.data_ptr(), B, K, m, out.data_ptr(),
+                                 logits_out.data_ptr(),
+                                 0 if topk_out is None else topk_out.data_ptr(),
+                                 ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
+              "ce_top_m")
+        return out, logits_out
+
     def capture(self, op: int, h, K: int | None, out, topk_out=None, stream=None) -> Graph:
         """Capture one call into a HIP graph with its own workspace.
 
@@ -236,3 +256,5 @@ class Head:
 
 OP_TOP_TOKENS = CE_OP_TOP_TOKENS
 OP_MASKED_LOGITS = CE_OP_MASKED_LOGITS
+OP_TOP_M = CE_OP_TOP_M
+MAX_TOP_M = CE_MAX_TOP_M

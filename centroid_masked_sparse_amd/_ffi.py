@@ -14,7 +14,8 @@ STATUS_NAMES = {
     7: "CE_ERR_NOT_PREPARED", 8: "CE_ERR_HIP", 9: "CE_ERR_UNSUPPORTED",
 }
 CE_F32, CE_BF16 = 0, 1
-CE_OP_SCORE, CE_OP_TOPK, CE_OP_TOP_TOKENS, CE_OP_MASKED_LOGITS = 0, 1, 2, 3
+CE_OP_SCORE, CE_OP_TOPK, CE_OP_TOP_TOKENS, CE_OP_MASKED_LOGITS, CE_OP_TOP_M = 0, 1, 2, 3, 4
+CE_MAX_TOP_M = 32
 
 # Every symbol the header declares, with (restype, argtypes).
 _vp = ctypes.c_void_p
@@ -40,6 +41,7 @@ SIGNATURES = {
     "ce_topk": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "ce_top_tokens": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "ce_masked_logits": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "ce_top_m": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ce_graph_capture": (_i32, [_vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp,
                                 ctypes.POINTER(_vp)]),
     "ce_graph_launch": (_i32, [_vp, _vp]),

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <functional>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -27,6 +28,7 @@ struct ce_head {
   std::vector<int32_t> offsets;       // [Nc+1]
   std::vector<int32_t> tos;           // [V]
   std::vector<uint32_t> tiles;        // every 64-slot tile: (index in cluster << 13) | cluster
+  std::vector<long long> tiles_top;   // tiles_top[K] = tiles of the K clusters with the most tiles
   bool prepared = false;
   ce::Tables tables{};
 };
@@ -59,7 +61,8 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
-  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, total = 0;
+  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, tm_keys = 0, tm_heads = 0, total = 0;
+  int tm_segcap = 0;
 };
 
 Layout make_layout(const ce_head* h, int B, int K, int op) {
@@ -79,6 +82,11 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   L.topk = take(nb * (size_t)K * sizeof(int32_t));
   L.cl_sel = take(((size_t)h->Nc + 63) / 64 * ce::kPassRows * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
+  if (op == CE_OP_TOP_M) {
+    L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);
+    L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kMaxTopM * sizeof(unsigned long long));
+    L.tm_heads = take(nb * (size_t)L.tm_segcap * sizeof(unsigned long long));
+  }
   L.total = off;
   return L;
 }
@@ -136,19 +144,29 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.ldK = a.K;
   a.cl_sel = reinterpret_cast<unsigned long long*>(ws + L.cl_sel);
   a.best = reinterpret_cast<unsigned long long*>(ws + L.best);
+  a.tm_keys = reinterpret_cast<unsigned long long*>(ws + L.tm_keys);
+  a.tm_heads = reinterpret_cast<unsigned long long*>(ws + L.tm_heads);
+  a.tm_segcap = L.tm_segcap;
 }
 
 // The shared sequence of ce_top_tokens and ce_masked_logits, in passes of at
 // most kPassRows rows.
 ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* out,
-                     int32_t* topk_ids, void* ws, size_t ws_bytes, hipStream_t stream) {
+                     int32_t* topk_ids, void* ws, size_t ws_bytes, hipStream_t stream,
+                     int m = 0, float* out2 = nullptr) {
   ce_status st = check_call(h, hin, B, K, true);
   if (st != CE_SUCCESS) return st;
-  if (B > 0 && !out) return fail(CE_ERR_NULL_POINTER, "output pointer is NULL");
+  if (B > 0 && (!out || (op == CE_OP_TOP_M && !out2)))
+    return fail(CE_ERR_NULL_POINTER, "output pointer is NULL");
+  if (op == CE_OP_TOP_M) {
+    if (m < 1 || m > ce::kMaxTopM) return fail(CE_ERR_BAD_SHAPE, "m must lie in [1, CE_MAX_TOP_M]");
+    if (h->tiles_top[K] > ce::kTopMMaxSegs)
+      return fail(CE_ERR_UNSUPPORTED, "the K largest clusters hold too many tiles for the top-m merge");
+  }
   if (B == 0) return CE_SUCCESS;
   if (!ws) return fail(CE_ERR_NULL_POINTER, "workspace is NULL");
   if (!aligned(hin, 16) || !aligned(out, op == CE_OP_MASKED_LOGITS ? 16 : 4) || !aligned(ws, 256) ||
-      (topk_ids && !aligned(topk_ids, 4)))
+      (topk_ids && !aligned(topk_ids, 4)) || (out2 && !aligned(out2, 4)))
     return fail(CE_ERR_MISALIGNED, "h and logits need 16-byte, ws 256-byte alignment");
   const Layout L = make_layout(h, B, K, op);
   if (ws_bytes < L.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than ce_workspace_bytes");
@@ -170,17 +188,26 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.topk = topk_ids + (size_t)b0 * K;
       a.ldK = K;
     }
-    if (op == CE_OP_TOP_TOKENS) a.tokens = static_cast<int32_t*>(out) + b0;
-    else a.logits = static_cast<float*>(out) + (size_t)b0 * h->V;
+    if (op == CE_OP_TOP_TOKENS) {
+      a.tokens = static_cast<int32_t*>(out) + b0;
+    } else if (op == CE_OP_TOP_M) {
+      a.m = m;
+      a.tm_cap = L.tm_segcap * m;
+      a.tm_tokens = static_cast<int32_t*>(out) + (size_t)b0 * m;
+      a.tm_logits = out2 + (size_t)b0 * m;
+    } else {
+      a.logits = static_cast<float*>(out) + (size_t)b0 * h->V;
+    }
     if (b0 == 0) {
       a.probe_start = pstart;
       a.probe_stop = pstop;
     }
-    const bool masked = op == CE_OP_MASKED_LOGITS;
+    const int mode = op == CE_OP_MASKED_LOGITS ? ce::kMasked : op == CE_OP_TOP_M ? ce::kTopM : ce::kArgmax;
     hipError_t e = ce::launch_scores(a, stream);
     if (e == hipSuccess) e = ce::launch_topk(a, ce::kTopkMark, stream);
-    if (e == hipSuccess) e = ce::launch_gather(a, masked ? ce::kMasked : ce::kArgmax, stream);
-    if (e == hipSuccess && !masked) e = ce::launch_finalize(a, stream);
+    if (e == hipSuccess) e = ce::launch_gather(a, mode, stream);
+    if (e == hipSuccess && mode == ce::kArgmax) e = ce::launch_finalize(a, stream);
+    if (e == hipSuccess && mode == ce::kTopM) e = ce::launch_topm_merge(a, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
   }
   return CE_SUCCESS;
@@ -245,9 +272,11 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
       }
       seen[t] = 1;
     }
+    std::vector<long long> ntiles((size_t)Nc);
     for (int c = 0; c < Nc; ++c) {
       const long long size = h->offsets[c + 1] - h->offsets[c];
       const long long nt = (size + ce::kTileTokens - 1) / ce::kTileTokens;
+      ntiles[c] = nt;
       if (nt > ce::kMaxTilesPerCluster) {
         delete h;
         return fail(CE_ERR_UNSUPPORTED, "a cluster holds more than 2^19 * 64 tokens");
@@ -255,6 +284,9 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
       for (long long q = 0; q < nt; ++q)
         h->tiles.push_back(((uint32_t)q << ce::kTileShift) | (uint32_t)c);
     }
+    std::sort(ntiles.begin(), ntiles.end(), std::greater<long long>());
+    h->tiles_top.assign((size_t)Nc + 1, 0);
+    for (int k = 0; k < Nc; ++k) h->tiles_top[k + 1] = h->tiles_top[k] + ntiles[k];
   } catch (const std::bad_alloc&) {
     delete h;
     return fail(CE_ERR_UNSUPPORTED, "out of host memory");
@@ -317,7 +349,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
 
 ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op, size_t* bytes) {
   if (!head || !bytes) return fail(CE_ERR_NULL_POINTER, "head or bytes is NULL");
-  if (op < CE_OP_SCORE || op > CE_OP_MASKED_LOGITS) return fail(CE_ERR_UNSUPPORTED, "unknown op");
+  if (op < CE_OP_SCORE || op > CE_OP_TOP_M) return fail(CE_ERR_UNSUPPORTED, "unknown op");
   if (B < 0 || B > head->max_B) return fail(CE_ERR_BAD_SHAPE, "B must lie in [0, max_B]");
   if (op == CE_OP_TOPK) {
     *bytes = 0;
@@ -375,6 +407,11 @@ ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K, int
 ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K, float* logits,
                            int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_sparse(head, CE_OP_MASKED_LOGITS, h, B, K, logits, topk_ids_or_null, ws, ws_bytes, stream);
+}
+
+ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m, int32_t* tokens,
+                   float* logits, int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_sparse(head, CE_OP_TOP_M, h, B, K, tokens, topk_ids_or_null, ws, ws_bytes, stream, m, logits);
 }
 
 ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B, int32_t K, void* out,

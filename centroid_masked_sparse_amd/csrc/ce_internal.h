@@ -25,7 +25,10 @@ struct Tables {
   const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
 };
 
-enum GatherMode { kArgmax = 0, kMasked = 1 };
+enum GatherMode { kArgmax = 0, kMasked = 1, kTopM = 2 };
+constexpr int kMaxTopM = 32;        // m of the fused top-m
+constexpr int kTopMCand = kMaxTopM * kMaxTopM;   // merge candidates per row (at most m*m)
+constexpr int kTopMMaxSegs = 6144;  // per-row tile segments the merge keeps in LDS
 // What the top-K kernel writes besides the ids: nothing, or the rows'
 // selection words (and, given `best`, cleared argmax slots).
 enum TopkMode { kTopkOnly = 1, kTopkMark = 2 };
@@ -46,6 +49,14 @@ struct PassArgs {
   int ldK;
   unsigned long long* cl_sel;   // [ceil(Nc/64)][kPassRows] bit i of word (w, b): row b selected 64w+i
   unsigned long long* best;     // [kPassRows] packed (ordered logit, ~token)
+  // fused top-m: per row, a packed count (segments << 32 | keys) in `best`,
+  // the tiles' local top-m keys and each tile segment's head key
+  int m;
+  unsigned long long* tm_keys;   // [B][tm_cap]
+  unsigned long long* tm_heads;  // [B][tm_segcap]
+  int tm_cap, tm_segcap;
+  int32_t* tm_tokens;     // [B][m]
+  float* tm_logits;       // [B][m]
   // outputs
   int32_t* tokens;        // [B]
   float* logits;          // [B][V] forward output; the scores kernel fills it with -inf
@@ -60,6 +71,7 @@ hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint
 hipError_t launch_scores(const PassArgs& a, hipStream_t s);
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: TopkMode
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
+hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
 
 }  // namespace ce

@@ -55,6 +55,7 @@
 extern "C" __device__ unsigned int __ockl_wfred_add_u32(unsigned int);
 extern "C" __device__ unsigned int __ockl_wfscan_add_u32(unsigned int, bool inclusive);
 extern "C" __device__ unsigned long long __ockl_wfred_max_u64(unsigned long long);
+extern "C" __device__ unsigned long long __ockl_wfred_min_u64(unsigned long long);
 
 namespace ce {
 namespace {
@@ -674,9 +675,14 @@ struct GatherArgs {
   const unsigned long long* cl_sel;
   int B;
   const uint32_t* tiles;
-  unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row
+  unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
+                                // top-m: [64] packed (segments << 32 | keys) per row
   float* out;                   // forward: [B][V] output rows (already -inf)
   int V;
+  int m;                        // top-m
+  unsigned long long* tm_keys;  // top-m: [B][tm_cap] tile segments of keys
+  unsigned long long* tm_heads; // top-m: [B][tm_segcap] each segment's first key
+  int tm_cap, tm_segcap;
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -722,7 +728,8 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 
   // argmax: wave maximum of the packed (ordered logit, ~token) per row,
   // max-ed into the row's slot; forward: each candidate logit stored at its
-  // token's column
+  // token's column; top-m: the tile's m largest packed keys for the row, in
+  // descending order, appended as one segment of the row's list
   auto finish = [&](const int (&rows)[RB], int nrows, const double (&acc)[RB]) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -734,8 +741,26 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           k = wave_max_u64(k);
           if (lane == 0) atomicMax(&a.best[rows[r]], k);   // result unused: no stall
-        } else {
+        } else if (MODE == kMasked) {
           if (lane < nvalid) a.out[(long)rows[r] * a.V + tok] = f;
+        } else {
+          unsigned long long k = 0ull;
+          if (lane < nvalid)
+            k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
+          const int mm = min(a.m, nvalid);
+          unsigned long long at = 0ull;
+          if (lane == 0) at = atomicAdd(&a.best[rows[r]], (1ull << 32) | (unsigned long long)mm);
+          const uint32_t seg = __builtin_amdgcn_readfirstlane((uint32_t)(at >> 32));
+          const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)at);
+          unsigned long long* keys = a.tm_keys + (long)rows[r] * a.tm_cap + base;
+          for (int i = 0; i < mm; ++i) {
+            const unsigned long long mx = wave_max_u64(k);
+            if (k == mx) k = 0ull;   // keys are unique (they hold the token)
+            if (lane == 0) {
+              keys[i] = mx;
+              if (i == 0) a.tm_heads[(long)rows[r] * a.tm_segcap + seg] = mx;
+            }
+          }
         }
       }
     }
@@ -764,6 +789,91 @@ __global__ __launch_bounds__(64) void finalize_kernel(const unsigned long long* 
   if (b < B) {
     const unsigned long long v = best[b];
     tokens[b] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
+  }
+}
+
+// ------------------------------------------------------------------ top-m merge
+
+struct TopmArgs {
+  const unsigned long long* cnt;    // [B] packed (segments << 32 | keys)
+  const unsigned long long* keys;   // [B][cap]
+  const unsigned long long* heads;  // [B][segcap]
+  int cap, segcap, m;
+  int32_t* tokens;                  // [B][m]
+  float* logits;                    // [B][m]
+};
+
+// Inverse of order_key (the canonical logits carry no -0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One 256-thread workgroup per row.  Each gather segment (one tile's keys
+// for the row) is sorted descending, so the m-th largest segment head mu is
+// a lower bound of the row's m-th largest key (m heads are keys >= mu), and
+// at most m segments reach it: the keys >= mu number at most m*m.  Each of
+// those counts the candidates above it; a count below m is its output
+// position.  With fewer than m segments every key is a candidate (fewer
+// than m*m of them).
+__global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
+  extern __shared__ unsigned long long tm_lds[];   // heads [segcap], then candidates
+  __shared__ uint32_t ncand;
+  __shared__ unsigned long long wred[kTopkWaves];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int m = a.m;
+  const unsigned long long c = a.cnt[b];
+  const int segs = (int)(c >> 32);
+  const int n = (int)(uint32_t)c;
+  unsigned long long* heads = tm_lds;
+  unsigned long long* cand = tm_lds + a.segcap;
+  const unsigned long long* hsrc = a.heads + (long)b * a.segcap;
+  const unsigned long long* ksrc = a.keys + (long)b * a.cap;
+  for (int i = tid; i < segs; i += kTopkThreads) heads[i] = hsrc[i];
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+
+  unsigned long long mu = 0ull;
+  if (segs >= m) {
+    unsigned long long low = ~0ull;
+    for (int i = tid; i < segs; i += kTopkThreads) {
+      const unsigned long long x = heads[i];
+      int above = 0;
+      for (int j = 0; j < segs; ++j) above += heads[j] > x ? 1 : 0;
+      if (above < m) low = min(low, x);
+    }
+    low = __ockl_wfred_min_u64(low);
+    if (lane == 0) wred[wv] = low;
+    __syncthreads();
+    mu = wred[0];
+#pragma unroll
+    for (int i = 1; i < kTopkWaves; ++i) mu = min(mu, wred[i]);
+  }
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const unsigned long long k = ksrc[i];
+    if (k >= mu) {
+      const uint32_t at = atomicAdd(&ncand, 1u);
+      if (at < (uint32_t)kTopMCand) cand[at] = k;
+    }
+  }
+  __syncthreads();
+  const int nc = min((int)ncand, kTopMCand);
+  int32_t* tok = a.tokens + (long)b * m;
+  float* val = a.logits + (long)b * m;
+  for (int i = tid; i < nc; i += kTopkThreads) {
+    const unsigned long long x = cand[i];
+    int above = 0;
+    for (int j = 0; j < nc; ++j) above += cand[j] > x ? 1 : 0;
+    if (above < m) {
+      tok[above] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
+      val[above] = key_value((uint32_t)(x >> 32));
+    }
+  }
+  for (int p = min(n, m) + tid; p < m; p += kTopkThreads) {
+    tok[p] = -1;
+    val[p] = -__builtin_inff();
   }
 }
 
@@ -861,6 +971,11 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.best = a.best;
   g.out = a.logits;
   g.V = a.V;
+  g.m = a.m;
+  g.tm_keys = a.tm_keys;
+  g.tm_heads = a.tm_heads;
+  g.tm_cap = a.tm_cap;
+  g.tm_segcap = a.tm_segcap;
   const dim3 grid(a.t.n_tiles > 0 ? a.t.n_tiles : 1);
   auto go = [&](auto kern) {
     if (a.probe_start && a.probe_stop) {
@@ -877,11 +992,29 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
 
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s) {
   if (a.t.n_tiles == 0) return hipSuccess;   // every cluster is empty
-  if (a.dtype == 1)
-    return mode == kArgmax ? launch_gather_t<uint16_t, kArgmax>(a, s)
-                           : launch_gather_t<uint16_t, kMasked>(a, s);
-  return mode == kArgmax ? launch_gather_t<float, kArgmax>(a, s)
-                         : launch_gather_t<float, kMasked>(a, s);
+  if (a.dtype == 1) {
+    if (mode == kArgmax) return launch_gather_t<uint16_t, kArgmax>(a, s);
+    if (mode == kMasked) return launch_gather_t<uint16_t, kMasked>(a, s);
+    return launch_gather_t<uint16_t, kTopM>(a, s);
+  }
+  if (mode == kArgmax) return launch_gather_t<float, kArgmax>(a, s);
+  if (mode == kMasked) return launch_gather_t<float, kMasked>(a, s);
+  return launch_gather_t<float, kTopM>(a, s);
+}
+
+hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s) {
+  TopmArgs t;
+  t.cnt = a.best;
+  t.keys = a.tm_keys;
+  t.heads = a.tm_heads;
+  t.cap = a.tm_cap;
+  t.segcap = a.tm_segcap;
+  t.m = a.m;
+  t.tokens = a.tm_tokens;
+  t.logits = a.tm_logits;
+  const size_t lds = ((size_t)a.tm_segcap + kTopMCand) * sizeof(unsigned long long);
+  hipLaunchKernelGGL(topm_merge_kernel, dim3(a.B), dim3(kTopkThreads), lds, s, t);
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {

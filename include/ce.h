@@ -75,7 +75,8 @@ typedef enum ce_op {
   CE_OP_SCORE = 0,          /* ce_score_centroids */
   CE_OP_TOPK = 1,           /* ce_topk */
   CE_OP_TOP_TOKENS = 2,     /* ce_top_tokens */
-  CE_OP_MASKED_LOGITS = 3   /* ce_masked_logits */
+  CE_OP_MASKED_LOGITS = 3,  /* ce_masked_logits */
+  CE_OP_TOP_M = 4           /* ce_top_m */
 } ce_op;
 
 typedef struct ce_head* ce_head_t;
@@ -187,6 +188,26 @@ ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K,
 ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K,
                            float* logits, int32_t* topk_ids_or_null, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/* Fused top-m over the candidates, the step after get_top_tokens that tree
+ * drafting and sampling need (next step named with the page's argmax): for
+ * every row b < B, the m candidate tokens (those owned by the row's K
+ * selected centroids) with the largest canonical logits, ordered by logit
+ * descending then token id ascending, and their fp32 logits, without
+ * building the full-vocabulary row.  A row with fewer than m candidates is
+ * padded with token -1 and logit -inf.
+ *   m        1..CE_MAX_TOP_M
+ *   tokens   DEVICE [B][m] int32
+ *   logits   DEVICE [B][m] fp32
+ *   ws       DEVICE workspace of ce_workspace_bytes(head, B, K, CE_OP_TOP_M)
+ *            (sized for m = CE_MAX_TOP_M), 256-byte aligned
+ * Other arguments and errors as ce_top_tokens, plus BAD_SHAPE for m out of
+ * range and UNSUPPORTED when a row's K largest clusters hold too many tiles
+ * for the merge (more than 6144 64-token tiles). */
+#define CE_MAX_TOP_M 32
+ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m,
+                   int32_t* tokens, float* logits, int32_t* topk_ids_or_null,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Capture one call of ce_top_tokens (op CE_OP_TOP_TOKENS, out = tokens) or
  * ce_masked_logits (op CE_OP_MASKED_LOGITS, out = logits) into an

@@ -135,6 +135,10 @@ def test_create_ragged_and_sizes(lib):
         assert lib.ce_workspace_bytes(h, 8, 5, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
         assert lib.ce_workspace_bytes(h, 8, 0, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
         assert lib.ce_workspace_bytes(h, 8, 1, 9, ctypes.byref(n)) == ERR["CE_ERR_UNSUPPORTED"]
+        # top-m: the masked sizes plus its segment lists (tiles of the K
+        # largest clusters: 2 + 2 for K=2, for m = CE_MAX_TOP_M keys each)
+        assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_M, ctypes.byref(n)) == 0
+        assert n.value >= sizes[_ffi.CE_OP_TOP_TOKENS] + 8 * 4 * _ffi.CE_MAX_TOP_M * 8
     finally:
         lib.ce_head_destroy(h)
 
@@ -147,6 +151,7 @@ def test_compute_calls_before_prepare_fail_on_host(lib):
         NP = ERR["CE_ERR_NOT_PREPARED"]
         assert lib.ce_top_tokens(h, FAKE, 1, 2, FAKE, None, FAKE, 1 << 20, None) == NP
         assert lib.ce_masked_logits(h, FAKE, 1, 2, FAKE, None, FAKE, 1 << 20, None) == NP
+        assert lib.ce_top_m(h, FAKE, 1, 2, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == NP
         assert lib.ce_score_centroids(h, FAKE, 1, FAKE, None) == NP
         assert lib.ce_topk(h, FAKE, 1, 2, FAKE, None) == NP
         assert "prepare" in lib.ce_last_error().decode()
