@@ -88,6 +88,28 @@ def _time_replays(torch, graphs, steps, warmup, stream_handle):
     return start.elapsed_time(stop) / steps
 
 
+def _time_calls(torch, calls, steps, warmup):
+    """Microseconds per call over ``steps`` eager C-ABI calls cycling through
+    ``calls`` ((function, args, keep-alive...) tuples); every distinct call is
+    run (and its status checked) during warm-up."""
+    n = len(calls)
+    for i in range(max(warmup, n)):
+        f, a = calls[i % n][0], calls[i % n][1]
+        st = f(*a)
+        if st != 0:
+            raise RuntimeError(f"{f.__name__} failed with status {st}")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        f, a = calls[i % n][0], calls[i % n][1]
+        f(*a)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / steps
+
+
 def _eager_us_per_call(torch, heads, hs, K, B, steps, warmup, stream):
     """Cold eager calls: ce_top_tokens straight through the C ABI (four kernel
     launches), rotating weight copies and row groups like the graph replays."""
@@ -233,6 +255,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-masked", action="store_true")
     ap.add_argument("--no-wide", action="store_true")
+    ap.add_argument("--no-top-m", action="store_true")
     ap.add_argument("--probe-calls", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,6 +405,28 @@ def main() -> int:
             del per_copy
             torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ fused top-m
+    top_m = []
+    if not args.no_top_m:
+        from centroid_masked_sparse_amd import OP_TOP_M
+        m = 8
+        for B in (1, 16, 64):
+            hs = groups(B)
+            calls = []
+            for s_ in range(len(hs)):
+                for head in heads:
+                    tok = torch.empty((B, m), dtype=torch.int32, device=dev)
+                    val = torch.empty((B, m), dtype=torch.float32, device=dev)
+                    ws = head._workspace(B, K, OP_TOP_M)
+                    calls.append((head._lib.ce_top_m,
+                                  (head._handle, hs[s_].data_ptr(), B, K, m, tok.data_ptr(),
+                                   val.data_ptr(), None, ws.data_ptr(), ws.numel(), stream),
+                                  tok, val))
+            us = _time_calls(torch, calls, args.steps, args.warmup)
+            row = {"B": B, "m": m, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1)}
+            top_m.append(row)
+            log(f"[bench] top_m: {row}")
+
     # ------------------------------------------------------------ wide head (d=1024, Nc=4096)
     wide = None
     if not args.no_wide:
@@ -434,6 +479,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "sweep": sweep,
         "masked": masked,
+        "top_m": top_m,
         "wide": wide,
     }
     print(json.dumps(line), flush=True)
