@@ -82,3 +82,34 @@ def test_bad_m_rejected():
             head.top_m(h, m, 4, out=torch.empty((1, max(m, 1)), dtype=torch.int32, device="cuda:0"),
                        logits_out=torch.empty((1, max(m, 1)), dtype=torch.float32, device="cuda:0"))
         assert e.value.status_name == "CE_ERR_BAD_SHAPE"
+
+
+def test_top_m_under_stream_capture():
+    """ce_top_m is capture-safe: a graph captured around it replays to the
+    eager result, with eager work and synchronisation between replays."""
+    torch = torch_mod()
+    w = make_random(45, d=128, V=8192, Nc=64, dtype="bf16", rows=16)
+    head = make_head(w, max_B=16)
+    h = to_device(rows(w, 16), w.dtype)
+    tok_e, val_e = head.top_m(h, 6, 4)
+    tok_e, val_e = tok_e.clone(), val_e.clone()
+    tok = torch.empty((16, 6), dtype=torch.int32, device="cuda:0")
+    val = torch.empty((16, 6), dtype=torch.float32, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        head.top_m(h, 6, 4, out=tok, logits_out=val)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        head.top_m(h, 6, 4, out=tok, logits_out=val)
+    for _ in range(3):
+        tok.fill_(-5)
+        val.fill_(7.0)
+        head.top_tokens(h, 4)          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tok, tok_e)
+        assert torch.equal(val.view(torch.int32), val_e.view(torch.int32))
