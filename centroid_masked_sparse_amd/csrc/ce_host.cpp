@@ -28,6 +28,8 @@ struct ce_head {
   std::vector<int32_t> offsets;       // [Nc+1]
   std::vector<int32_t> tos;           // [V]
   std::vector<uint32_t> tiles;        // every 64-slot tile: (index in cluster << 13) | cluster
+  int tpc = 0;                        // tiles per cluster if all clusters hold as many, else 0
+  std::vector<int32_t> ttok;          // [n_tiles][64] token id of each tile slot, -1 past the end
   std::vector<long long> tiles_top;   // tiles_top[K] = tiles of the K clusters with the most tiles
   bool prepared = false;
   ce::Tables tables{};
@@ -91,9 +93,9 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   return L;
 }
 
-// Offsets of the four device tables inside the persistent buffer.
+// Offsets of the device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t offsets, tos, tiles, et, ct, total;
+  size_t offsets, tos, tiles, ttok, et, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -107,6 +109,7 @@ PersistLayout persist_layout(const ce_head* h) {
   p.offsets = take(((size_t)h->Nc + 1) * sizeof(int32_t));
   p.tos = take((size_t)h->V * sizeof(int32_t));
   p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
+  p.ttok = take(std::max<size_t>(h->ttok.size(), 1) * sizeof(int32_t));
   const size_t tile_bytes = (size_t)ce::kTileTokens * h->d * elem_bytes(h->dtype);
   p.et = take(h->tiles.size() * tile_bytes);
   p.ct = take((((size_t)h->Nc + ce::kTileTokens - 1) / ce::kTileTokens) * tile_bytes);
@@ -281,9 +284,17 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
         delete h;
         return fail(CE_ERR_UNSUPPORTED, "a cluster holds more than 2^19 * 64 tokens");
       }
-      for (long long q = 0; q < nt; ++q)
+      for (long long q = 0; q < nt; ++q) {
         h->tiles.push_back(((uint32_t)q << ce::kTileShift) | (uint32_t)c);
+        for (int l = 0; l < ce::kTileTokens; ++l) {
+          const long long j = h->offsets[c] + q * ce::kTileTokens + l;
+          h->ttok.push_back(j < h->offsets[c + 1] ? h->tos[j] : -1);
+        }
+      }
     }
+    h->tpc = (int)ntiles[0];
+    for (int c = 1; c < Nc; ++c)
+      if (ntiles[c] != ntiles[0]) h->tpc = 0;
     std::sort(ntiles.begin(), ntiles.end(), std::greater<long long>());
     h->tiles_top.assign((size_t)Nc + 1, 0);
     for (int k = 0; k < Nc; ++k) h->tiles_top[k + 1] = h->tiles_top[k] + ntiles[k];
@@ -315,7 +326,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   struct Copy {
     size_t at;
     const std::vector<int32_t>* v;
-  } copies[] = {{p.offsets, &head->offsets}, {p.tos, &head->tos}};
+  } copies[] = {{p.offsets, &head->offsets}, {p.tos, &head->tos}, {p.ttok, &head->ttok}};
   for (const Copy& c : copies) {
     hipError_t e = hipMemcpyAsync(base + c.at, c.v->data(), c.v->size() * sizeof(int32_t),
                                   hipMemcpyHostToDevice, stream);
@@ -341,6 +352,8 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   head->tables.tos = reinterpret_cast<const int32_t*>(base + p.tos);
   head->tables.tiles = reinterpret_cast<const uint32_t*>(base + p.tiles);
   head->tables.n_tiles = (int)head->tiles.size();
+  head->tables.tpc = head->tpc;
+  head->tables.ttok = reinterpret_cast<const int32_t*>(base + p.ttok);
   head->tables.ET = base + p.et;
   head->tables.CT = base + p.ct;
   head->prepared = true;

@@ -21,6 +21,8 @@ struct Tables {
   const int32_t* tos;          // [V] token id of each slot
   const uint32_t* tiles;       // [n_tiles] every 64-slot tile of every cluster, cluster-major
   int n_tiles;
+  int tpc;                     // tiles per cluster when every cluster holds as many, else 0
+  const int32_t* ttok;         // [n_tiles][64] token id of each tile slot, -1 past the cluster's end
   const void* ET;              // packed embeddings: [n_tiles][d/vec][64] 16-byte vectors
   const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
 };

@@ -214,7 +214,7 @@ __device__ __forceinline__ void widen4(const v4u r, double (&x)[4]) {
 // consecutive elements of each hidden row: lane l of every 16-lane row holds
 // elements 4l..4l+3 of the chunk, widened to float64, and element k reaches
 // every lane by a 64-bit DPP broadcast from lane k/4 of its row.
-template <typename T, int RB, int NCH>
+template <typename T, int RB, int NCH, int STAGES = 2>
 __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
                                          const T* __restrict__ h, const int (&rows)[RB], int nrows,
                                          double (&acc)[RB]) {
@@ -259,33 +259,30 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
     });
   };
 
-  // Two register stages: while one chunk is consumed the other is in
-  // flight; a stage is reloaded only after it has been consumed.  With the
-  // chunk count NCH known at compile time the pipeline is straight-line
-  // code; otherwise the steady-state loop (even chunk counts) reloads
-  // unconditionally and the last two chunks are peeled, so no load sits
-  // under a branch.
-  Stage s0, s1;
+  // A ring of register stages: while one chunk is consumed the next
+  // STAGES-1 are in flight; a stage is reloaded only after it has been
+  // consumed.  With the chunk count NCH known at compile time the pipeline
+  // is straight-line code; otherwise two stages, where the steady-state loop
+  // (even chunk counts) reloads unconditionally and the last two chunks are
+  // peeled, so no load sits under a branch.
   if constexpr (NCH > 0) {
+    constexpr int S = STAGES < NCH ? STAGES : NCH;
+    Stage st[S];
     // scheduling barriers keep each stage's loads together and in order, so
     // that waiting for one stage never waits for the next
-    load(s0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NCH > 1) load(s1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ch = 0; ch < NCH; ch += 2) {
-      consume(s0);
-      if (ch + 2 < NCH) load(s0, ch + 2);
+    static_for<0, S>([&](auto i) {
+      load(st[decltype(i)::value], decltype(i)::value);
       __builtin_amdgcn_sched_barrier(0);
-      if (ch + 1 < NCH) {
-        consume(s1);
-        if (ch + 3 < NCH) load(s1, ch + 3);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    });
+    static_for<0, NCH>([&](auto c) {
+      constexpr int ch = decltype(c)::value;
+      consume(st[ch % S]);
+      if constexpr (ch + S < NCH) load(st[ch % S], ch + S);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     return;
   }
+  Stage s0, s1;
   const int nch = d / kChunk;
   if (nch == 1) {
     load(s0, 0);
@@ -667,14 +664,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 // ------------------------------------------------------------------ gather
 
 struct GatherArgs {
-  const v4u* ET;
+  const v4u* ET;                // [n_tiles][d/vec][64] packed tiles
   const void* h;
-  int d, Nc;
-  const int32_t* offsets;
-  const int32_t* tos;
-  const unsigned long long* cl_sel;
+  int d;
+  const unsigned long long* cl_sel;  // [ceil(Nc/64)][64] row selection words of the centroids
   int B;
-  const uint32_t* tiles;
+  const uint32_t* tiles;        // [n_tiles] (index in cluster << 13) | cluster
+  int tpc;                      // tiles per cluster when all clusters hold as many, else 0
+  const int32_t* ttok;          // [n_tiles][64] token of each slot, -1 past the cluster's end
   unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
                                 // top-m: [64] packed (segments << 32 | keys) per row
   float* out;                   // forward: [B][V] output rows (already -inf)
@@ -707,21 +704,23 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
   return n;
 }
 
+// One wave per packed tile.  Once the rows that selected the tile's
+// cluster are known, the tile, the hidden rows and the slots' token ids are
+// all requested at once: they are addressed by the tile index alone.  With
+// equal tile counts per cluster the cluster follows from the tile index
+// too, so the selection words are the only load before the tile's.
 template <typename T, int RB, int MODE, int NCH>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
-  const uint32_t tile = a.tiles[blockIdx.x];
-  const int c = (int)(tile & ((1u << kTileShift) - 1u));
+  const int t = blockIdx.x;
+  const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
   // lane b reads row b's selection word of c's 64-centroid block
   const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
   unsigned long long mask = __ballot((word >> (c % kWave)) & 1ull);
-  if (!mask) return;   // no row selected this centroid
-  const int q = (int)(tile >> kTileShift);
-  const long j0 = (long)a.offsets[c] + (long)q * kTileTokens;
-  const int nvalid = (int)min((long)kTileTokens, (long)a.offsets[c + 1] - j0);
+  if (!mask) return;   // no row selected this tile's cluster
   // the token ids are needed only after the first batch is dotted: they
   // are waited for there, not before the tile loads go out
-  int tok = a.tos[j0 + (lane < nvalid ? lane : nvalid - 1)];
+  int tok = a.ttok[(long)blockIdx.x * kWave + lane];
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
   const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
   const T* h = reinterpret_cast<const T*>(a.h);
@@ -737,17 +736,17 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
         const float f = canon(acc[r]);
         if (MODE == kArgmax) {
           unsigned long long k = 0ull;
-          if (lane < nvalid)
+          if (tok >= 0)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           k = wave_max_u64(k);
           if (lane == 0) atomicMax(&a.best[rows[r]], k);   // result unused: no stall
         } else if (MODE == kMasked) {
-          if (lane < nvalid) a.out[(long)rows[r] * a.V + tok] = f;
+          if (tok >= 0) a.out[(long)rows[r] * a.V + tok] = f;
         } else {
           unsigned long long k = 0ull;
-          if (lane < nvalid)
+          if (tok >= 0)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
-          const int mm = min(a.m, nvalid);
+          const int mm = min(a.m, (int)__builtin_popcountll(__ballot(tok >= 0)));
           unsigned long long at = 0ull;
           if (lane == 0) at = atomicAdd(&a.best[rows[r]], (1ull << 32) | (unsigned long long)mm);
           const uint32_t seg = __builtin_amdgcn_readfirstlane((uint32_t)(at >> 32));
@@ -962,12 +961,11 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.ET = static_cast<const v4u*>(a.t.ET);
   g.h = a.h;
   g.d = a.d;
-  g.Nc = a.Nc;
-  g.offsets = a.t.offsets;
-  g.tos = a.t.tos;
   g.cl_sel = a.cl_sel;
   g.B = a.B;
   g.tiles = a.t.tiles;
+  g.tpc = a.t.tpc;
+  g.ttok = a.t.ttok;
   g.best = a.best;
   g.out = a.logits;
   g.V = a.V;

@@ -113,10 +113,10 @@ def test_create_ragged_and_sizes(lib):
         n = ctypes.c_size_t()
         assert lib.ce_head_persistent_bytes(h, ctypes.byref(n)) == 0
         # offsets (5 ints) + token_of_slot (V ints) + the tile list (clusters
-        # of 0, 100, 30 and 126 tokens: 0+2+1+2 = 5 words), each rounded up to
-        # 256 bytes, + packed embeddings (5 tiles) and centroids (1 tile) of
-        # 64 rows x 64 bf16
-        assert n.value == 256 + 1024 + 256 + 5 * 8192 + 8192
+        # of 0, 100, 30 and 126 tokens: 0+2+1+2 = 5 words) + the tiles' slot
+        # tokens (5 x 64 ints), each rounded up to 256 bytes, + packed
+        # embeddings (5 tiles) and centroids (1 tile) of 64 rows x 64 bf16
+        assert n.value == 256 + 1024 + 256 + 5 * 256 + 5 * 8192 + 8192
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOPK, ctypes.byref(n)) == 0
         assert n.value == 0
         sizes = {}
