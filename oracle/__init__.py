@@ -5,3 +5,4 @@ leg may import this package.  The product path never does.
 """
 
 from .masked_head import *  # noqa: F401,F403
+from .draft import *  # noqa: F401,F403

@@ -1,0 +1,210 @@
+"""Pins of the draft-step oracle (final RMSNorm and scaled embedding lookup).
+
+Each check ties the oracle to something other than itself: hand-derived
+values (tests/golden/draft_step.json), an exact rational evaluation of the
+norm, scale invariance, signed-zero special cases.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import draft as ds
+from workloads.synth import f32_to_bf16_bits as _synth_bf16
+
+def to_bf16_bits(a):
+    """Seeded test inputs as bf16 bit patterns (the workload generator's
+    rounding, which is input generation, not the method)."""
+    return _synth_bf16(np.asarray(a, dtype=np.float32))
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "draft_step.json")
+
+
+def _bits(s):
+    return np.array([int(t, 16) for t in s.split()], dtype=np.uint16)
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _case_arrays(c):
+    d = c["d"]
+    if "x_fill" in c:
+        x = np.full(d, int(c["x_fill"], 16), dtype=np.uint16)
+    else:
+        x = np.zeros(d, dtype=np.uint16)
+        for k, v in c["x"].items():
+            x[int(k)] = int(v, 16)
+    if "w_fill" in c:
+        w = np.full(d, int(c["w_fill"], 16), dtype=np.uint16)
+    else:
+        w = np.tile(_bits(c["w"]), c["w_repeat"])
+    return x, w
+
+
+def test_golden_rms_norm(golden):
+    for c in golden["rms_norm"]:
+        x, w = _case_arrays(c)
+        got = ds.rms_norm(x[None, :], w, c["eps"], "bf16")[0]
+        if c["expect"] == "same as w":
+            want = w
+        elif isinstance(c["expect"], dict):
+            want = np.full(c["d"], int(c["expect_rest"], 16), dtype=np.uint16)
+            for k, v in c["expect"].items():
+                want[int(k)] = int(v, 16)
+        else:
+            want = np.tile(_bits(c["expect"]), c["expect_repeat"])
+        assert np.array_equal(got, want), c["name"]
+
+
+def test_golden_embedding(golden):
+    for c in golden["embed"]:
+        n = np.float32(c["normalizer_num"] * 2.0 ** c["normalizer_exp2"])
+        assert float(n) == c["normalizer_num"] * 2.0 ** c["normalizer_exp2"]   # exact in fp32
+        table = np.array([[int(c["e"], 16)]], dtype=np.uint16)
+        got = ds.embed_rows(table, np.array([0]), n, "bf16")
+        assert got[0, 0] == int(c["expect"], 16), c["name"]
+
+
+def _bf16_of_fraction(q: Fraction) -> int:
+    """bf16 bits of the exact rational q rounded to nearest, ties to even
+    (normal range only)."""
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    m = a / Fraction(2) ** e * 128          # in [128, 256)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2):
+        fl += 1
+    if fl == 256:
+        fl, e = 128, e + 1
+    return sign | ((e + 127) << 7) | (fl - 128)
+
+
+def _distance_to_tie(q: Fraction) -> float:
+    """Relative distance of q to the nearest bf16 rounding boundary."""
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    m = a / Fraction(2) ** e * 128
+    frac = m - m.numerator // m.denominator
+    return float(abs(frac - Fraction(1, 2))) / 128.0
+
+
+def _isqrt_fraction(v: Fraction, bits: int = 200) -> Fraction:
+    """sqrt(v) to `bits` fractional bits (floor), exactly from integers."""
+    scale = 1 << (2 * bits)
+    n = v.numerator * scale // v.denominator
+    from math import isqrt
+    return Fraction(isqrt(n), 1 << bits)
+
+
+@pytest.mark.parametrize("seed,d,eps", [(1, 64, 1e-6), (2, 128, 1e-6), (3, 256, 0.5), (4, 64, 0.0)])
+def test_rms_norm_matches_exact_value(seed, d, eps):
+    """Each bf16 output is the exact real x_k w_k / sqrt(mean x^2 + eps)
+    rounded to bf16, except where that value sits within float64 noise of a
+    bf16 rounding boundary (skipped: the canonical float64 steps decide)."""
+    rng = np.random.default_rng(seed)
+    x = to_bf16_bits(rng.standard_normal((3, d)) * 2.0)
+    w = to_bf16_bits(1.0 + 0.25 * rng.standard_normal(d))
+    got = ds.rms_norm(x, w, eps, "bf16")
+    X = (x.astype(np.uint32) << 16).view(np.float32)
+    W = (w.astype(np.uint32) << 16).view(np.float32)
+    eps_q = Fraction(float(np.float32(eps)))
+    checked = 0
+    for b in range(3):
+        ss = sum(Fraction(float(v)) ** 2 for v in X[b])
+        s = _isqrt_fraction(ss / d + eps_q)
+        for k in range(d):
+            y = Fraction(float(X[b, k])) * Fraction(float(W[k])) / s
+            if y == 0:
+                assert got[b, k] & 0x7FFF == 0
+                continue
+            if _distance_to_tie(y) < 1e-12:
+                continue
+            assert got[b, k] == _bf16_of_fraction(y), (b, k)
+            checked += 1
+    assert checked > 3 * d * 0.99
+
+
+@pytest.mark.parametrize("k", [-5, 3])
+def test_rms_norm_scale_invariance(k):
+    """With eps = 0, scaling x by 2^k changes nothing: every float64 step
+    scales exactly (squares by 4^k, sqrt by 2^k, r by 2^-k)."""
+    rng = np.random.default_rng(11)
+    x = to_bf16_bits(rng.standard_normal((4, 192)))
+    w = to_bf16_bits(rng.standard_normal(192))
+    xs = x.astype(np.int32)
+    nz = (xs & 0x7F80) != 0
+    xs[nz] += k << 7                        # exponent shift of the normal values
+    h0 = ds.rms_norm(x, w, 0.0, "bf16")
+    h1 = ds.rms_norm(xs.astype(np.uint16), w, 0.0, "bf16")
+    assert np.array_equal(h0, h1)
+
+
+def test_rms_norm_f32_constant_row():
+    d = 128
+    x = np.full((1, d), -0.5, dtype=np.float32)
+    w = np.random.default_rng(5).standard_normal(d).astype(np.float32)
+    h = ds.rms_norm(x, w, 0.0, "f32")
+    # ss = d/4, v = 1/4, r = 2, x r = -1: y = -w exactly
+    assert np.array_equal(h[0], -w)
+
+
+def test_rms_norm_rejects_ragged_d():
+    with pytest.raises(ValueError):
+        ds.rms_norm(np.zeros((1, 96), np.uint16), np.zeros(96, np.uint16), 1e-6, "bf16")
+
+
+def test_embed_rows_identity_zero_and_padding():
+    rng = np.random.default_rng(3)
+    table = to_bf16_bits(rng.standard_normal((10, 24)))
+    out = ds.embed_rows(table, np.array([7, -1, 2]), 1.0, "bf16")
+    assert np.array_equal(out[0], table[7])          # times 1 is exact
+    assert not out[1].any()                          # no candidate: zeros
+    assert np.array_equal(out[2], table[2])
+    # times 4: the exponent field grows by 2 for every normal value
+    t4 = ds.embed_rows(table, np.array([5]), 4.0, "bf16")[0].astype(np.int32)
+    assert np.array_equal(t4, table[5].astype(np.int32) + (2 << 7))
+
+
+def test_bf16_rounding_edges():
+    f = np.array([np.inf, -np.inf, np.nan, 3.4e38, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8],
+                 dtype=np.float32)
+    got = ds.f32_to_bf16_bits(f)
+    # inf stays inf; NaN is quiet; 3.4e38 rounds past the largest finite bf16
+    # to inf; halfway cases go to the even neighbour (1.0 and 1 + 2^-6)
+    assert list(got) == [0x7F80, 0xFF80, 0x7FC0, 0x7F80, 0x3F80, 0x3F82]
+
+
+def test_draft_step_uses_normalised_rows():
+    """The draft step is the head applied to the normalised rows, and the
+    embeddings are those of the tokens it picked."""
+    from oracle import top_tokens
+    rng = np.random.default_rng(9)
+    d, Nc, vpc = 64, 16, 8
+    V = Nc * vpc
+    C = to_bf16_bits(rng.standard_normal((Nc, d)) / 8)
+    E = to_bf16_bits(rng.standard_normal((V, d)) / 8)
+    offsets = np.arange(Nc + 1) * vpc
+    tos = rng.permutation(V)
+    x = to_bf16_bits(rng.standard_normal((5, d)))
+    w = to_bf16_bits(np.ones(d))
+    table = to_bf16_bits(rng.standard_normal((V, 16)))
+    h, tok, emb, sel = ds.draft_step(x, w, 1e-6, C, E, offsets, tos, 3, table, 2.0, "bf16")
+    tok2, sel2, _ = top_tokens(h, C, E, offsets, tos, 3, "bf16")
+    assert np.array_equal(tok, tok2) and np.array_equal(sel, sel2)
+    assert np.array_equal(emb, ds.embed_rows(table, tok, 2.0, "bf16"))
