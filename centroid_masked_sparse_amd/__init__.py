@@ -19,8 +19,8 @@ import ctypes
 import numpy as np
 
 from . import _ffi
-from ._ffi import (CE_BF16, CE_F32, CE_MAX_TOP_M, CE_OP_MASKED_LOGITS, CE_OP_TOP_M,
-                   CE_OP_TOP_TOKENS, CeError, check)
+from ._ffi import (CE_BF16, CE_F32, CE_MAX_TOP_M, CE_OP_DRAFT_STEP, CE_OP_MASKED_LOGITS,
+                   CE_OP_TOP_M, CE_OP_TOP_TOKENS, CeError, check)
 
 __all__ = ["Head", "Graph", "CeError", "load_library"]
 
@@ -223,6 +223,40 @@ class Head:
               "ce_top_m")
         return out, logits_out
 
+    def draft_step(self, x, norm_weight, eps: float, K: int | None = None, emb_table=None,
+                   normalizer: float = 1.0, h_out=None, out=None, emb_out=None, topk_out=None):
+        """One fused draft step: the final RMSNorm of the rows x, the top token of
+        each normalised row, and (given ``emb_table``, ``[V, emb_dim]`` indexed
+        by token id) that token's embedding times ``normalizer``.
+
+        Returns ``(h, tokens, emb)`` (``emb`` is None without a table)."""
+        torch = _torch()
+        B = self._check_h(x)
+        K = self._k(K)
+        if norm_weight.dtype != self.dtype or not norm_weight.is_cuda or norm_weight.numel() != self.d:
+            raise ValueError("norm_weight must be a [d] tensor of the head's dtype on its device")
+        if h_out is None:
+            h_out = torch.empty_like(x)
+        if out is None:
+            out = torch.empty(B, dtype=torch.int32, device=self.device)
+        emb_dim = 0
+        if emb_table is not None:
+            if emb_table.dtype != self.dtype or emb_table.dim() != 2 or not emb_table.is_contiguous():
+                raise ValueError("emb_table must be a contiguous [V, emb_dim] tensor of the head's dtype")
+            emb_dim = emb_table.shape[1]
+            if emb_out is None:
+                emb_out = torch.empty((B, emb_dim), dtype=self.dtype, device=self.device)
+        ws = self._workspace(B, K, CE_OP_DRAFT_STEP)
+        check(self._lib.ce_draft_step(self._handle, x.data_ptr(), norm_weight.data_ptr(), float(eps),
+                                      B, K, h_out.data_ptr(), out.data_ptr(),
+                                      0 if emb_table is None else emb_table.data_ptr(), emb_dim,
+                                      float(normalizer),
+                                      0 if emb_out is None else emb_out.data_ptr(),
+                                      0 if topk_out is None else topk_out.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
+              "ce_draft_step")
+        return h_out, out, (emb_out if emb_table is not None else None)
+
     def capture(self, op: int, h, K: int | None, out, topk_out=None, stream=None) -> Graph:
         """Capture one call into a HIP graph with its own workspace.
 
@@ -257,4 +291,5 @@ class Head:
 OP_TOP_TOKENS = CE_OP_TOP_TOKENS
 OP_MASKED_LOGITS = CE_OP_MASKED_LOGITS
 OP_TOP_M = CE_OP_TOP_M
+OP_DRAFT_STEP = CE_OP_DRAFT_STEP
 MAX_TOP_M = CE_MAX_TOP_M

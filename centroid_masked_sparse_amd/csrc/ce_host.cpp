@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <functional>
 #include <cstdio>
 #include <cstring>
@@ -152,13 +153,51 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.tm_segcap = L.tm_segcap;
 }
 
-// The shared sequence of ce_top_tokens and ce_masked_logits, in passes of at
-// most kPassRows rows.
+// The draft step's extra operands (ce_draft_step).
+struct DraftArgs {
+  const void* norm_w;
+  float eps;
+  void* h_out;
+  const void* emb_table;
+  int emb_dim;
+  float normalizer;
+  void* emb_out;
+};
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+ce_status check_draft(const ce_head* h, const void* x, int B, const DraftArgs& dr) {
+  if (!(dr.eps > 0.0f) || !std::isfinite(dr.eps)) return fail(CE_ERR_BAD_SHAPE, "eps must be finite and > 0");
+  if (dr.emb_table) {
+    if (dr.emb_dim < 1 || ((size_t)dr.emb_dim * elem_bytes(h->dtype)) % 16)
+      return fail(CE_ERR_BAD_SHAPE, "emb_dim must be > 0 with 16-byte rows");
+    if (!std::isfinite(dr.normalizer)) return fail(CE_ERR_BAD_SHAPE, "normalizer must be finite");
+  }
+  if (B == 0) return CE_SUCCESS;
+  if (!dr.norm_w || !dr.h_out || (dr.emb_table && !dr.emb_out))
+    return fail(CE_ERR_NULL_POINTER, "norm_weight, h_out and (with a table) emb_out are required");
+  if (!aligned(dr.norm_w, 16) || !aligned(dr.h_out, 16) ||
+      (dr.emb_table && (!aligned(dr.emb_table, 16) || !aligned(dr.emb_out, 16))))
+    return fail(CE_ERR_MISALIGNED, "norm_weight, h_out, emb_table and emb_out need 16-byte alignment");
+  const size_t rows = (size_t)B * h->d * elem_bytes(h->dtype);
+  if (overlaps(x, rows, dr.h_out, rows)) return fail(CE_ERR_UNSUPPORTED, "x and h_out overlap");
+  return CE_SUCCESS;
+}
+
+// The shared sequence of ce_top_tokens, ce_masked_logits, ce_top_m and
+// ce_draft_step, in passes of at most kPassRows rows.
 ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* out,
                      int32_t* topk_ids, void* ws, size_t ws_bytes, hipStream_t stream,
-                     int m = 0, float* out2 = nullptr) {
+                     int m = 0, float* out2 = nullptr, const DraftArgs* draft = nullptr) {
   ce_status st = check_call(h, hin, B, K, true);
   if (st != CE_SUCCESS) return st;
+  if (op == CE_OP_DRAFT_STEP) {
+    st = check_draft(h, hin, B, *draft);
+    if (st != CE_SUCCESS) return st;
+  }
   if (B > 0 && (!out || (op == CE_OP_TOP_M && !out2)))
     return fail(CE_ERR_NULL_POINTER, "output pointer is NULL");
   if (op == CE_OP_TOP_M) {
@@ -191,7 +230,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.topk = topk_ids + (size_t)b0 * K;
       a.ldK = K;
     }
-    if (op == CE_OP_TOP_TOKENS) {
+    if (op == CE_OP_TOP_TOKENS || op == CE_OP_DRAFT_STEP) {
       a.tokens = static_cast<int32_t*>(out) + b0;
     } else if (op == CE_OP_TOP_M) {
       a.m = m;
@@ -206,7 +245,26 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.probe_stop = pstop;
     }
     const int mode = op == CE_OP_MASKED_LOGITS ? ce::kMasked : op == CE_OP_TOP_M ? ce::kTopM : ce::kArgmax;
+    void* h_out = nullptr;
+    if (op == CE_OP_DRAFT_STEP) {
+      // scores reads the rows before the norm and writes the normalised ones
+      h_out = static_cast<char*>(draft->h_out) + (size_t)b0 * in_row;
+      a.norm_w = draft->norm_w;
+      a.norm_eps = draft->eps;
+      a.h_out = h_out;
+      if (draft->emb_table) {
+        a.emb_table = draft->emb_table;
+        a.emb_dim = draft->emb_dim;
+        a.emb_normalizer = draft->normalizer;
+        a.emb_out = static_cast<char*>(draft->emb_out) +
+                    (size_t)b0 * draft->emb_dim * elem_bytes(h->dtype);
+      }
+    }
     hipError_t e = ce::launch_scores(a, stream);
+    if (h_out) {
+      a.h = h_out;   // the rest of the pass works on the normalised rows
+      a.norm_w = nullptr;
+    }
     if (e == hipSuccess) e = ce::launch_topk(a, ce::kTopkMark, stream);
     if (e == hipSuccess) e = ce::launch_gather(a, mode, stream);
     if (e == hipSuccess && mode == ce::kArgmax) e = ce::launch_finalize(a, stream);
@@ -362,7 +420,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
 
 ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op, size_t* bytes) {
   if (!head || !bytes) return fail(CE_ERR_NULL_POINTER, "head or bytes is NULL");
-  if (op < CE_OP_SCORE || op > CE_OP_TOP_M) return fail(CE_ERR_UNSUPPORTED, "unknown op");
+  if (op < CE_OP_SCORE || op > CE_OP_DRAFT_STEP) return fail(CE_ERR_UNSUPPORTED, "unknown op");
   if (B < 0 || B > head->max_B) return fail(CE_ERR_BAD_SHAPE, "B must lie in [0, max_B]");
   if (op == CE_OP_TOPK) {
     *bytes = 0;
@@ -425,6 +483,16 @@ ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K, 
 ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m, int32_t* tokens,
                    float* logits, int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_sparse(head, CE_OP_TOP_M, h, B, K, tokens, topk_ids_or_null, ws, ws_bytes, stream, m, logits);
+}
+
+ce_status ce_draft_step(ce_head_t head, const void* x, const void* norm_weight, float eps,
+                        int32_t B, int32_t K, void* h_out, int32_t* tokens,
+                        const void* emb_table, int32_t emb_dim, float normalizer,
+                        void* emb_out, int32_t* topk_ids_or_null, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  const DraftArgs dr{norm_weight, eps, h_out, emb_table, emb_dim, normalizer, emb_out};
+  return run_sparse(head, CE_OP_DRAFT_STEP, x, B, K, tokens, topk_ids_or_null, ws, ws_bytes,
+                    stream, 0, nullptr, &dr);
 }
 
 ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B, int32_t K, void* out,

@@ -59,6 +59,17 @@ struct PassArgs {
   int tm_cap, tm_segcap;
   int32_t* tm_tokens;     // [B][m]
   float* tm_logits;       // [B][m]
+  // fused draft step: h holds the rows before the final RMSNorm when norm_w
+  // is set; the scores kernel writes the normalised rows to h_out (which the
+  // gather then reads), and the finalize kernel writes the chosen tokens'
+  // scaled embeddings when emb_table is set
+  const void* norm_w;     // [d] or null
+  float norm_eps;
+  void* h_out;            // [B][d]
+  const void* emb_table;  // [V][emb_dim] or null
+  int emb_dim;
+  float emb_normalizer;
+  void* emb_out;          // [B][emb_dim]
   // outputs
   int32_t* tokens;        // [B]
   float* logits;          // [B][V] forward output; the scores kernel fills it with -inf

@@ -312,6 +312,94 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
   }
 }
 
+// ------------------------------------------------------------------ final norm
+
+// float32 -> bf16 bits, nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four normalised elements, stored as the head's element type.
+__device__ __forceinline__ v2u pack_norm(const double (&y)[4], uint16_t) {
+  v2u o;
+  o[0] = bf16_rne((float)y[0]) | (bf16_rne((float)y[1]) << 16);
+  o[1] = bf16_rne((float)y[2]) | (bf16_rne((float)y[3]) << 16);
+  return o;
+}
+__device__ __forceinline__ v4u pack_norm(const double (&y)[4], float) {
+  v4u o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __float_as_uint((float)y[i]);
+  return o;
+}
+
+struct NormArgs {
+  const void* w;       // [d] norm weight, head dtype
+  double eps;          // widened from float32
+  void* out;           // [B][d] normalised rows, head dtype
+};
+
+// The final RMSNorm of the rows rows[0..RB) of x ([*][d]), written to
+// lds ([RB][d], slot r for rows[r]) and, given `out`, to out[rows[r]] for
+// r < nrows.  Canonical rounding: squares are exact in float64; each chunk
+// of 64 elements is summed by a balanced pairwise tree, the chunk sums in
+// chunk order from +0.0; v = ss / d + eps, r = 1 / sqrt(v), y = (x r) w, each
+// one correctly rounded float64 operation; y is rounded to float32 and then
+// to the head's element type (nearest, ties to even).
+//
+// Lane l works on chunk 4j + l/16 of each group of four chunks, elements
+// 4(l%16) .. 4(l%16)+3: its four squares make the tree's first two levels,
+// a butterfly over its 16-lane row the other four.
+template <typename T, int RB>
+__device__ __forceinline__ void normalize_rows(const T* __restrict__ x, const int (&rows)[RB],
+                                               int nrows, int d, const NormArgs& nm,
+                                               T* lds, T* __restrict__ out) {
+  using HR = typename HQuad<T>::raw;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int e4 = 4 * (lane & 15);
+  const int nch = d / kChunk;
+  const T* w = static_cast<const T*>(nm.w);
+  double rr[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const T* xr = x + (long)rows[r] * d;
+    double ss = 0.0;
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+      const int ch = min(c0 + g, nch - 1);   // clamped: lanes past the end are not read back
+      double q[4];
+      widen4(*reinterpret_cast<const HR*>(xr + ch * kChunk + e4), q);
+      double t = (q[0] * q[0] + q[1] * q[1]) + (q[2] * q[2] + q[3] * q[3]);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) t = t + __shfl_xor(t, m, 16);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        if (c0 + gg < nch) ss = ss + __shfl(t, 16 * gg);
+    }
+    rr[r] = 1.0 / sqrt(ss / (double)d + nm.eps);
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const T* xr = x + (long)rows[r] * d;
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+      const int ch = c0 + g;
+      if (ch < nch) {
+        const int k = ch * kChunk + e4;
+        double xv[4], wv[4], y[4];
+        widen4(*reinterpret_cast<const HR*>(xr + k), xv);
+        widen4(*reinterpret_cast<const HR*>(w + k), wv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = (xv[i] * rr[r]) * wv[i];
+        const HR o = pack_norm(y, T());
+        *reinterpret_cast<HR*>(lds + r * d + k) = o;
+        if (out && r < nrows) *reinterpret_cast<HR*>(out + (long)rows[r] * d + k) = o;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ scores
 
 // Fill rows [r0, r0+nrows) of out ([*][V] fp32) with -inf over this
@@ -338,11 +426,17 @@ __device__ __forceinline__ void fill_neg_inf(float* __restrict__ out, int V, int
 // One wave per (64-centroid tile, RB rows): S[b][c] for the tile's
 // centroids; with `fill` (forward) the wave also fills its share of the
 // output rows with -inf.
-template <typename T, int RB, int NCH>
+//
+// With NORM, h holds the rows before the final RMSNorm: the wave normalises
+// its rows into LDS (dynamic, [RB][d]) and dots the tile with those; the
+// waves of the first centroid tile also write them to nm.out.
+template <typename T, int RB, int NCH, bool NORM>
 __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, int Nc, int d,
                                                     const T* __restrict__ h, int B,
                                                     float* __restrict__ S, int ldS,
-                                                    float* __restrict__ fill, int V) {
+                                                    float* __restrict__ fill, int V,
+                                                    NormArgs nm) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char norm_lds[];
   const int lane = threadIdx.x;
   const int c0 = blockIdx.x * kTileTokens;
   const int r0 = blockIdx.y * RB;
@@ -354,7 +448,18 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   for (int r = 0; r < RB; ++r) rows[r] = r0 + (r < nrows ? r : nrows - 1);
   double acc[RB];
   const long tile_vecs = (long)(d / Elem<T>::kPerVec) * kWave;
-  dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
+  if constexpr (NORM) {
+    T* hn = reinterpret_cast<T*>(norm_lds);
+    normalize_rows<T, RB>(h, rows, nrows, d, nm, hn,
+                          blockIdx.x == 0 ? static_cast<T*>(nm.out) : nullptr);
+    __syncthreads();
+    int lrows[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) lrows[r] = r < nrows ? r : 0;
+    dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, hn, lrows, nrows, acc);
+  } else {
+    dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
+  }
   if (lane < nvalid) {
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -791,6 +896,51 @@ __global__ __launch_bounds__(64) void finalize_kernel(const unsigned long long* 
   }
 }
 
+// Finalize plus the next step's input embedding: one workgroup per row
+// decodes the row's token and writes emb[b] = table[token] * normalizer
+// (float32 product, then the head's element type; zeros without a token).
+struct EmbedArgs {
+  const void* table;   // [V][dim] head dtype, indexed by token id
+  int dim;             // elements per row, 16-byte rows
+  float normalizer;
+  void* out;           // [B][dim]
+};
+constexpr int kEmbedThreads = 256;
+
+__device__ __forceinline__ v4u scale_vec(v4u v, float n, uint16_t) {
+  v4u o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = bf16_rne(__uint_as_float(v[i] << 16) * n);
+    const uint32_t hi = bf16_rne(__uint_as_float(v[i] & 0xFFFF0000u) * n);
+    o[i] = lo | (hi << 16);
+  }
+  return o;
+}
+__device__ __forceinline__ v4u scale_vec(v4u v, float n, float) {
+  v4u o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * n);
+  return o;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kEmbedThreads) void finalize_embed_kernel(
+    const unsigned long long* __restrict__ best, int32_t* __restrict__ tokens, EmbedArgs e) {
+  const int b = blockIdx.x;
+  const unsigned long long v = best[b];
+  const int tok = v ? (int)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
+  if (threadIdx.x == 0) tokens[b] = tok;
+  const int nvec = e.dim / Elem<T>::kPerVec;
+  v4u* dst = static_cast<v4u*>(e.out) + (long)b * nvec;
+  if (tok < 0) {
+    for (int i = threadIdx.x; i < nvec; i += kEmbedThreads) dst[i] = v4u{0u, 0u, 0u, 0u};
+    return;
+  }
+  const v4u* src = static_cast<const v4u*>(e.table) + (long)tok * nvec;
+  for (int i = threadIdx.x; i < nvec; i += kEmbedThreads) dst[i] = scale_vec(src[i], e.normalizer, T());
+}
+
 // ------------------------------------------------------------------ top-m merge
 
 struct TopmArgs {
@@ -896,9 +1046,15 @@ hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint
 template <typename T, int RB, int NCH>
 static void launch_scores_n(const PassArgs& a, hipStream_t s) {
   const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
-  hipLaunchKernelGGL((scores_kernel<T, RB, NCH>), grid, dim3(64), 0, s,
-                     static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
-                     a.S, a.ldS, a.logits, a.V);
+  NormArgs nm{a.norm_w, (double)a.norm_eps, a.h_out};
+  if (a.norm_w)
+    hipLaunchKernelGGL((scores_kernel<T, RB, NCH, true>), grid, dim3(64),
+                       (size_t)RB * a.d * sizeof(T), s, static_cast<const v4u*>(a.t.CT), a.Nc,
+                       a.d, static_cast<const T*>(a.h), a.B, a.S, a.ldS, a.logits, a.V, nm);
+  else
+    hipLaunchKernelGGL((scores_kernel<T, RB, NCH, false>), grid, dim3(64), 0, s,
+                       static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
+                       a.S, a.ldS, a.logits, a.V, nm);
 }
 
 // Hidden sizes with a straight-line chunk pipeline; others take the generic one.
@@ -1016,7 +1172,17 @@ hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.best, a.B, a.tokens);
+  if (a.emb_table) {
+    EmbedArgs e{a.emb_table, a.emb_dim, a.emb_normalizer, a.emb_out};
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(finalize_embed_kernel<uint16_t>, dim3(a.B), dim3(kEmbedThreads), 0, s,
+                         a.best, a.tokens, e);
+    else
+      hipLaunchKernelGGL(finalize_embed_kernel<float>, dim3(a.B), dim3(kEmbedThreads), 0, s,
+                         a.best, a.tokens, e);
+  } else {
+    hipLaunchKernelGGL(finalize_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.best, a.B, a.tokens);
+  }
   return hipGetLastError();
 }
 

@@ -76,7 +76,8 @@ typedef enum ce_op {
   CE_OP_TOPK = 1,           /* ce_topk */
   CE_OP_TOP_TOKENS = 2,     /* ce_top_tokens */
   CE_OP_MASKED_LOGITS = 3,  /* ce_masked_logits */
-  CE_OP_TOP_M = 4           /* ce_top_m */
+  CE_OP_TOP_M = 4,          /* ce_top_m */
+  CE_OP_DRAFT_STEP = 5      /* ce_draft_step */
 } ce_op;
 
 typedef struct ce_head* ce_head_t;
@@ -208,6 +209,42 @@ ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K,
 ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m,
                    int32_t* tokens, float* logits, int32_t* topk_ids_or_null,
                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Fused draft step around the head (the step after the head that fuses its
+ * neighbours).  In the page's multi-token predictor (Gemma4MultiTokenPredictor
+ * forward) the head scores the output of the final RMSNorm, and the next
+ * draft step starts from embed_input_ids: the chosen token's backbone
+ * embedding times the float32 `normalizer` buffer.  For every row b < B:
+ *   h_out[b]  = RMSNorm(x[b]) with weight norm_weight and epsilon eps:
+ *               x_k w_k / sqrt(mean_j x_j^2 + eps) in the canonical norm
+ *               rounding: squares exact in float64, each 64-element chunk
+ *               summed by a balanced pairwise tree and the chunk sums in
+ *               order from +0.0, then v = ss/d + eps, r = 1/sqrt(v),
+ *               y = (x_k r) w_k in correctly rounded float64 steps, y rounded
+ *               to float32 and then to the head's dtype (nearest, ties even);
+ *   tokens[b] = get_top_tokens of h_out[b], exactly as ce_top_tokens;
+ *   emb_out[b] = emb_table[tokens[b]] * normalizer, the float32 product
+ *               rounded to the head's dtype; zeros when tokens[b] is -1.
+ *               Only when emb_table is not NULL.
+ *   x            DEVICE [B][d] rows before the norm, head dtype, 16-byte aligned
+ *   norm_weight  DEVICE [d] head dtype, 16-byte aligned
+ *   eps          finite, > 0
+ *   h_out        DEVICE [B][d] head dtype, 16-byte aligned
+ *   tokens       DEVICE [B] int32
+ *   emb_table    DEVICE [V][emb_dim] head dtype indexed by token id, 16-byte
+ *                aligned, or NULL
+ *   emb_dim      > 0, emb_dim * element size a multiple of 16 (with a table)
+ *   normalizer   finite float32 scale (with a table)
+ *   emb_out      DEVICE [B][emb_dim] head dtype, 16-byte aligned (with a table)
+ *   ws           DEVICE workspace of ce_workspace_bytes(head, B, K,
+ *                CE_OP_DRAFT_STEP), 256-byte aligned
+ * Other arguments and errors as ce_top_tokens, plus BAD_SHAPE for eps,
+ * emb_dim or normalizer out of range.  x and h_out must not overlap. */
+ce_status ce_draft_step(ce_head_t head, const void* x, const void* norm_weight, float eps,
+                        int32_t B, int32_t K, void* h_out, int32_t* tokens,
+                        const void* emb_table, int32_t emb_dim, float normalizer,
+                        void* emb_out, int32_t* topk_ids_or_null, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 /* Capture one call of ce_top_tokens (op CE_OP_TOP_TOKENS, out = tokens) or
  * ce_masked_logits (op CE_OP_MASKED_LOGITS, out = logits) into an

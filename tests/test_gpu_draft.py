@@ -1,0 +1,158 @@
+"""GPU parity of the fused draft step (ce_draft_step) against the oracle.
+
+The normalised rows, the selected centroids, the tokens and the scaled
+embeddings must all match the oracle bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import draft as od
+from tests.gpu_helpers import make_head, to_device, torch_mod
+from workloads import make_random, make_workload
+from workloads.synth import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, d, V, emb_dim, dtype):
+    """Pre-norm rows x ~ N(0, 4), norm weight 1 + N(0, 0.01), an embedding
+    table ~ N(0, 1) of emb_dim columns indexed by token id."""
+    rng = np.random.default_rng(seed)
+    cast = (lambda a: f32_to_bf16_bits(a.astype(np.float32))) if dtype == "bf16" else \
+        (lambda a: a.astype(np.float32))
+    x = cast(2.0 * rng.standard_normal((B, d)))
+    w = cast(1.0 + 0.1 * rng.standard_normal(d))
+    table = cast(rng.standard_normal((V, emb_dim))) if emb_dim else None
+    return x, w, table
+
+
+def _bits(t, dtype):
+    torch = torch_mod()
+    if dtype == "bf16":
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def _np_bits(a, dtype):
+    return a.view(np.uint16) if dtype == "bf16" else np.asarray(a, np.float32).view(np.uint32)
+
+
+def _check(head, w, x, nw, table, eps, normalizer, K):
+    torch = torch_mod()
+    B = x.shape[0]
+    tk = torch.full((B, K), -7, dtype=torch.int32, device="cuda:0")
+    h, tok, emb = head.draft_step(to_device(x, w.dtype), to_device(nw, w.dtype), eps, K,
+                                  None if table is None else to_device(table, w.dtype),
+                                  normalizer, topk_out=tk)
+    torch.cuda.synchronize()
+    h_o, tok_o, emb_o, sel_o = od.draft_step(x, nw, eps, w.C, w.E, w.offsets, w.tos, K, table,
+                                             normalizer, w.dtype)
+    assert np.array_equal(_bits(h, w.dtype), _np_bits(h_o, w.dtype))
+    assert tk.cpu().numpy().tolist() == sel_o.tolist()
+    assert tok.cpu().numpy().tolist() == tok_o.tolist()
+    if table is None:
+        assert emb is None
+    else:
+        assert np.array_equal(_bits(emb, w.dtype), _np_bits(emb_o, w.dtype))
+
+
+@pytest.mark.parametrize("K,B", [(4, 3), (64, 4)])
+def test_tiny_config_f32(K, B):
+    w = make_workload(1)
+    x, nw, table = _inputs(1, B, w.d, w.V, 12, "f32")
+    _check(make_head(w, max_B=4), w, x, nw, table, 1e-6, 2.5, K)
+
+
+@pytest.mark.parametrize("seed,d,V,Nc,K,B,emb_dim,ragged", [
+    (51, 128, 8192, 64, 4, 9, 64, False),
+    (52, 64, 3000, 40, 3, 7, 40, True),      # ragged clusters, some tiny
+    (53, 256, 16384, 256, 16, 64, 2560, False),
+    (54, 320, 5000, 50, 2, 70, 8, True),     # two passes of rows, d not a multiple of 256
+    (55, 192, 4096, 64, 5, 5, 0, False),     # no embedding table
+])
+def test_random_shapes(seed, d, V, Nc, K, B, emb_dim, ragged):
+    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)
+    x, nw, table = _inputs(seed, B, d, V, emb_dim, "bf16")
+    _check(make_head(w, max_B=B), w, x, nw, table, 1e-6, float(np.sqrt(2560.0)), K)
+
+
+def test_sweep_config_full_size():
+    """The sweep head (d=256, V=262144, Nc=2048, K=32, bf16) at B=64 as the
+    bench runs it: every normalised row and token against the oracle."""
+    w = make_workload(2)
+    x, nw, table = _inputs(60, 64, w.d, w.V, 128, "bf16")
+    _check(make_head(w, max_B=64), w, x, nw, table, 1e-6, float(np.sqrt(2560.0)), w.K)
+
+
+def test_zero_rows_large_eps_and_identity_scale():
+    """A zero row normalises to signed zeros; eps = 4 dominates; normalizer 1
+    returns the table rows unchanged."""
+    w = make_random(56, d=128, V=4096, Nc=32, dtype="bf16", rows=64, ragged=False)
+    x, nw, table = _inputs(56, 6, 128, 4096, 16, "bf16")
+    x[2] = 0
+    x[4] = 0x8000   # -0 everywhere
+    _check(make_head(w, max_B=6), w, x, nw, table, 4.0, 1.0, 4)
+
+
+def test_empty_clusters_embed_zeros():
+    """A row whose selected clusters own no token gets token -1 and a zero
+    embedding."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import Head
+    d = 64
+    x = np.zeros((2, d), dtype=np.float32)
+    x[0, 0] = 3.0
+    x[1, 0] = -3.0
+    C = np.zeros((4, d), dtype=np.float32)
+    C[:, 0] = [5.0, 4.0, -1.0, -2.0]       # row 0 picks clusters 0,1 (empty)
+    E = np.random.default_rng(0).standard_normal((128, d)).astype(np.float32)
+    off = np.array([0, 0, 0, 100, 128], dtype=np.int32)
+    tos = np.random.default_rng(1).permutation(128).astype(np.int32)
+    nw = np.ones(d, dtype=np.float32)
+    table = np.random.default_rng(2).standard_normal((128, 4)).astype(np.float32)
+    head = Head(torch.from_numpy(C).cuda(), torch.from_numpy(E).cuda(), tos, off, max_B=2, max_K=4)
+    h, tok, emb = head.draft_step(torch.from_numpy(x).cuda(), torch.from_numpy(nw).cuda(), 1e-6, 2,
+                                  torch.from_numpy(table).cuda(), 3.0)
+    torch.cuda.synchronize()
+    tok = tok.cpu().numpy()
+    assert tok[0] == -1 and tok[1] >= 0
+    e = emb.cpu().numpy()
+    assert not e[0].any()
+    assert np.array_equal(e[1], (table[tok[1]] * np.float32(3.0)).astype(np.float32))
+
+
+def test_draft_step_errors():
+    import ctypes
+    from centroid_masked_sparse_amd import _ffi
+    torch = torch_mod()
+    w = make_workload(1)
+    head = make_head(w, max_B=4)
+    x, nw, table = _inputs(3, 2, w.d, w.V, 12, "f32")
+    xd, nwd = to_device(x, "f32"), to_device(nw, "f32")
+    td = to_device(table, "f32")
+    lib = head._lib
+    ws = head.new_workspace(2, 4, _ffi.CE_OP_DRAFT_STEP)
+    hout = torch.empty_like(xd)
+    tok = torch.empty(2, dtype=torch.int32, device="cuda:0")
+    emb = torch.empty((2, 12), dtype=torch.float32, device="cuda:0")
+
+    def call(x_ptr=xd.data_ptr(), nw_ptr=nwd.data_ptr(), eps=1e-6, h_ptr=hout.data_ptr(),
+             t_ptr=td.data_ptr(), emb_dim=12, norm=1.0, e_ptr=emb.data_ptr()):
+        return lib.ce_draft_step(head._handle, x_ptr, nw_ptr, ctypes.c_float(eps), 2, 4, h_ptr,
+                                 tok.data_ptr(), t_ptr, emb_dim, ctypes.c_float(norm), e_ptr, None,
+                                 ws.data_ptr(), ws.numel(), None)
+
+    assert call(eps=0.0) == 2
+    assert call(eps=-1.0) == 2
+    assert call(eps=float("nan")) == 2
+    assert call(emb_dim=3) == 2                 # 12-byte rows
+    assert call(norm=float("inf")) == 2
+    assert call(nw_ptr=None) == 1
+    assert call(h_ptr=None) == 1
+    assert call(e_ptr=None) == 1
+    assert call(h_ptr=xd.data_ptr()) == 9       # in place: x and h_out overlap
+    assert call(nw_ptr=nwd.data_ptr() + 4) == 4
+    assert call(t_ptr=None, e_ptr=None) == 0    # no table: tokens only
+    assert call() == 0
+    torch.cuda.synchronize()
