@@ -22,6 +22,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -177,6 +178,72 @@ def _device_us_per_call(torch, heads, hs, K, B, steps, warmup, per_graph=8):
     return a.elapsed_time(b) * 1e3 / (n * per_graph)
 
 
+EMB_DIM = 2560   # backbone width of the embedding table (assumed: the pages give none)
+
+
+def _draft_section(torch, heads, groups, K, args, stream, log):
+    """The fused draft step (final RMSNorm, head, next step's scaled embedding:
+    four launches) against the same step unfused (PyTorch RMSNorm in float32,
+    ce_top_tokens, PyTorch embedding lookup and scale), at B in {1, 16, 64}.
+    Seeded synthetic norm weight and embedding table; the 64 hidden rows of
+    the sweep workload serve as the rows before the norm."""
+    from centroid_masked_sparse_amd import OP_DRAFT_STEP
+    dev = "cuda:0"
+    V, d = heads[0].V, heads[0].d
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    nw = (1.0 + 0.1 * torch.randn(d, generator=g, device=dev)).to(torch.bfloat16)
+    table = torch.randn((V, EMB_DIM), generator=g, device=dev).to(torch.bfloat16)
+    normalizer = float(EMB_DIM) ** 0.5
+    n32 = torch.tensor(normalizer, dtype=torch.float32, device=dev)
+    eps = 1e-6
+    rows = []
+    for B in (1, 16, 64):
+        hs = groups(B)
+        calls, keep = [], []
+        for s_ in range(len(hs)):
+            for head in heads:
+                h_out = torch.empty_like(hs[s_])
+                tok = torch.empty((B,), dtype=torch.int32, device=dev)
+                emb = torch.empty((B, EMB_DIM), dtype=torch.bfloat16, device=dev)
+                ws = head._workspace(B, K, OP_DRAFT_STEP)
+                calls.append((head._lib.ce_draft_step,
+                              (head._handle, hs[s_].data_ptr(), nw.data_ptr(), ctypes.c_float(eps),
+                               B, K, h_out.data_ptr(), tok.data_ptr(), table.data_ptr(), EMB_DIM,
+                               ctypes.c_float(normalizer), emb.data_ptr(), None, ws.data_ptr(),
+                               ws.numel(), stream)))
+                keep.append((h_out, tok, emb))
+        fused = _time_calls(torch, calls, args.steps, args.warmup)
+
+        def unfused(i):
+            head = heads[i % len(heads)]
+            x = hs[(i // len(heads)) % len(hs)]
+            xf = x.float()
+            h = (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps)).to(torch.bfloat16) * nw
+            tok = head.top_tokens(h, K)
+            return table[tok.long()] * n32
+
+        for i in range(max(args.warmup, 2 * len(heads))):
+            unfused(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        n = max(50, args.steps // 4)
+        a.record()
+        for i in range(n):
+            unfused(i)
+        b.record()
+        torch.cuda.synchronize()
+        unf = a.elapsed_time(b) * 1e3 / n
+        row = {"B": B, "emb_dim": EMB_DIM, "us_per_call": round(fused, 3),
+               "rows_per_s": round(B / (fused * 1e-6), 1), "unfused_us_per_call": round(unf, 3)}
+        rows.append(row)
+        log(f"[bench] draft_step: {row}")
+    del table
+    torch.cuda.empty_cache()
+    return rows
+
+
 def _wide_section(torch, args, stream, log):
     """The wide head at B=64: the sparse head at K=64 and at K=Nc (every
     centroid: the exact dense argmax), beside a dense comparison path, the
@@ -256,6 +323,7 @@ def main() -> int:
     ap.add_argument("--no-masked", action="store_true")
     ap.add_argument("--no-wide", action="store_true")
     ap.add_argument("--no-top-m", action="store_true")
+    ap.add_argument("--no-draft", action="store_true")
     ap.add_argument("--probe-calls", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -427,6 +495,11 @@ def main() -> int:
             top_m.append(row)
             log(f"[bench] top_m: {row}")
 
+    # ------------------------------------------------------------ fused draft step
+    draft = []
+    if not args.no_draft:
+        draft = _draft_section(torch, heads, groups, K, args, stream, log)
+
     # ------------------------------------------------------------ wide head (d=1024, Nc=4096)
     wide = None
     if not args.no_wide:
@@ -480,6 +553,7 @@ def main() -> int:
         "sweep": sweep,
         "masked": masked,
         "top_m": top_m,
+        "draft_step": draft,
         "wide": wide,
     }
     print(json.dumps(line), flush=True)

@@ -214,10 +214,17 @@ __device__ __forceinline__ void widen4(const v4u r, double (&x)[4]) {
 // consecutive elements of each hidden row: lane l of every 16-lane row holds
 // elements 4l..4l+3 of the chunk, widened to float64, and element k reaches
 // every lane by a 64-bit DPP broadcast from lane k/4 of its row.
-template <typename T, int RB, int NCH, int STAGES = 2>
+struct NoOp {
+  __device__ void operator()() const {}
+};
+
+// With SPLIT (a compile-time chunk count only), the first stages' tile loads
+// are issued, then mid() runs, then the first stages' hidden loads: mid may
+// produce the hidden rows (in LDS) while the tile loads are in flight.
+template <typename T, int RB, int NCH, int STAGES = 2, bool SPLIT = false, typename Mid = NoOp>
 __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
                                          const T* __restrict__ h, const int (&rows)[RB], int nrows,
-                                         double (&acc)[RB]) {
+                                         double (&acc)[RB], Mid&& mid = Mid()) {
   constexpr int PV = Elem<T>::kPerVec;
   constexpr int VPC = kChunk / PV;              // weight vectors per chunk
   using HR = typename HQuad<T>::raw;
@@ -236,11 +243,17 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
     v4u e[VPC];
     HR h[RB];
   };
-  auto load = [&](Stage& st, int ch) {
+  auto load_w = [&](Stage& st, int ch) {
 #pragma unroll
     for (int p = 0; p < VPC; ++p) st.e[p] = wt[(ch * VPC + p) * kWave + lane];
+  };
+  auto load_h = [&](Stage& st, int ch) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) st.h[r] = *reinterpret_cast<const HR*>(hp[r] + ch * kChunk);
+  };
+  auto load = [&](Stage& st, int ch) {
+    load_w(st, ch);
+    load_h(st, ch);
   };
   auto consume = [&](const Stage& st) {
     double hd[RB][4];
@@ -270,10 +283,21 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
     Stage st[S];
     // scheduling barriers keep each stage's loads together and in order, so
     // that waiting for one stage never waits for the next
-    static_for<0, S>([&](auto i) {
-      load(st[decltype(i)::value], decltype(i)::value);
+    if constexpr (SPLIT) {
+      static_for<0, S>([&](auto i) {
+        load_w(st[decltype(i)::value], decltype(i)::value);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mid();
       __builtin_amdgcn_sched_barrier(0);
-    });
+      static_for<0, S>([&](auto i) { load_h(st[decltype(i)::value], decltype(i)::value); });
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      static_for<0, S>([&](auto i) {
+        load(st[decltype(i)::value], decltype(i)::value);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
     static_for<0, NCH>([&](auto c) {
       constexpr int ch = decltype(c)::value;
       consume(st[ch % S]);
@@ -335,6 +359,39 @@ __device__ __forceinline__ v4u pack_norm(const double (&y)[4], float) {
   return o;
 }
 
+// A double from another lane of the same 16-lane row (DPP on both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i of 8 <- lane 7-i
+constexpr int kDppMirror = 0x140;      // lane i of 16 <- lane 15-i
+
+// Sum of t over each 16-lane row as a balanced tree over lane order (lanes
+// 2m and 2m+1 first, then pairs of pairs, ...); every lane of the row ends
+// with the row's sum.  After each level the lanes of a group hold equal
+// values, so the mirrors pair whole groups.
+__device__ __forceinline__ double row16_tree_sum(double t) {
+  t = t + dpp_f64<kDppXor1>(t);
+  t = t + dpp_f64<kDppXor2>(t);
+  t = t + dpp_f64<kDppHalfMirror>(t);
+  t = t + dpp_f64<kDppMirror>(t);
+  return t;
+}
+
+__device__ __forceinline__ double read_lane_f64(double v, int lane) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
 struct NormArgs {
   const void* w;       // [d] norm weight, head dtype
   double eps;          // widened from float32
@@ -371,12 +428,10 @@ __device__ __forceinline__ void normalize_rows(const T* __restrict__ x, const in
       const int ch = min(c0 + g, nch - 1);   // clamped: lanes past the end are not read back
       double q[4];
       widen4(*reinterpret_cast<const HR*>(xr + ch * kChunk + e4), q);
-      double t = (q[0] * q[0] + q[1] * q[1]) + (q[2] * q[2] + q[3] * q[3]);
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) t = t + __shfl_xor(t, m, 16);
+      const double t = row16_tree_sum((q[0] * q[0] + q[1] * q[1]) + (q[2] * q[2] + q[3] * q[3]));
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg)
-        if (c0 + gg < nch) ss = ss + __shfl(t, 16 * gg);
+        if (c0 + gg < nch) ss = ss + read_lane_f64(t, 16 * gg);
     }
     rr[r] = 1.0 / sqrt(ss / (double)d + nm.eps);
   }
@@ -396,6 +451,64 @@ __device__ __forceinline__ void normalize_rows(const T* __restrict__ x, const in
         *reinterpret_cast<HR*>(lds + r * d + k) = o;
         if (out && r < nrows) *reinterpret_cast<HR*>(out + (long)rows[r] * d + k) = o;
       }
+    }
+  }
+}
+
+// The same norm with its loads split from its arithmetic: norm_load issues
+// the rows' and the weight's loads (NG groups of four chunks, d = 256 NG),
+// norm_finish does the rest, so that other loads can go out in between.
+template <typename T, int RB, int NG>
+struct NormRegs {
+  typename HQuad<T>::raw x[RB][NG];
+  typename HQuad<T>::raw w[NG];
+};
+
+template <typename T, int RB, int NG>
+__device__ __forceinline__ void norm_load(NormRegs<T, RB, NG>& nr, const T* __restrict__ x,
+                                          const int (&rows)[RB], int d, const NormArgs& nm) {
+  using HR = typename HQuad<T>::raw;
+  const int lane = threadIdx.x;
+  const int k = (lane >> 4) * kChunk + 4 * (lane & 15);
+  const T* w = static_cast<const T*>(nm.w);
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+      nr.x[r][q] = *reinterpret_cast<const HR*>(x + (long)rows[r] * d + q * 4 * kChunk + k);
+    nr.w[q] = *reinterpret_cast<const HR*>(w + q * 4 * kChunk + k);
+  }
+}
+
+template <typename T, int RB, int NG>
+__device__ __forceinline__ void norm_finish(const NormRegs<T, RB, NG>& nr, const int (&rows)[RB],
+                                            int nrows, int d, const NormArgs& nm, T* lds,
+                                            T* __restrict__ out) {
+  using HR = typename HQuad<T>::raw;
+  const int lane = threadIdx.x;
+  const int k = (lane >> 4) * kChunk + 4 * (lane & 15);
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    double ss = 0.0;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      double v[4];
+      widen4(nr.x[r][q], v);
+      const double t = row16_tree_sum((v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]));
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) ss = ss + read_lane_f64(t, 16 * gg);
+    }
+    const double rr = 1.0 / sqrt(ss / (double)d + nm.eps);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      double xv[4], wv[4], y[4];
+      widen4(nr.x[r][q], xv);
+      widen4(nr.w[q], wv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = (xv[i] * rr) * wv[i];
+      const HR o = pack_norm(y, T());
+      *reinterpret_cast<HR*>(lds + r * d + q * 4 * kChunk + k) = o;
+      if (out && r < nrows) *reinterpret_cast<HR*>(out + (long)rows[r] * d + q * 4 * kChunk + k) = o;
     }
   }
 }
@@ -450,13 +563,25 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   const long tile_vecs = (long)(d / Elem<T>::kPerVec) * kWave;
   if constexpr (NORM) {
     T* hn = reinterpret_cast<T*>(norm_lds);
-    normalize_rows<T, RB>(h, rows, nrows, d, nm, hn,
-                          blockIdx.x == 0 ? static_cast<T*>(nm.out) : nullptr);
-    __syncthreads();
+    T* out = blockIdx.x == 0 ? static_cast<T*>(nm.out) : nullptr;
     int lrows[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) lrows[r] = r < nrows ? r : 0;
-    dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, hn, lrows, nrows, acc);
+    if constexpr (NCH > 0 && NCH % 4 == 0) {
+      // row and weight loads first, then the tile's first stages; the norm
+      // is computed while those are in flight
+      NormRegs<T, RB, NCH / 4> nr;
+      norm_load<T, RB, NCH / 4>(nr, h, rows, d, nm);
+      __builtin_amdgcn_sched_barrier(0);
+      dot_tile<T, RB, NCH, 2, true>(CT + blockIdx.x * tile_vecs, d, hn, lrows, nrows, acc, [&] {
+        norm_finish<T, RB, NCH / 4>(nr, rows, nrows, d, nm, hn, out);
+        __syncthreads();
+      });
+    } else {
+      normalize_rows<T, RB>(h, rows, nrows, d, nm, hn, out);
+      __syncthreads();
+      dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, hn, lrows, nrows, acc);
+    }
   } else {
     dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
   }
