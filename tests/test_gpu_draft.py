@@ -156,3 +156,38 @@ def test_draft_step_errors():
     assert call(t_ptr=None, e_ptr=None) == 0    # no table: tokens only
     assert call() == 0
     torch.cuda.synchronize()
+
+
+def test_draft_step_under_stream_capture():
+    """ce_draft_step is capture-safe: a graph captured around it replays to
+    the eager result, with other eager work and synchronisation between
+    replays."""
+    torch = torch_mod()
+    w = make_random(57, d=256, V=8192, Nc=64, dtype="bf16", rows=16)
+    head = make_head(w, max_B=16)
+    x, nw, table = _inputs(57, 16, 256, 8192, 64, "bf16")
+    xd, nwd, td = to_device(x, "bf16"), to_device(nw, "bf16"), to_device(table, "bf16")
+    h_e, tok_e, emb_e = [t.clone() for t in head.draft_step(xd, nwd, 1e-6, 4, td, 3.0)]
+    h = torch.empty_like(xd)
+    tok = torch.empty(16, dtype=torch.int32, device="cuda:0")
+    emb = torch.empty((16, 64), dtype=torch.bfloat16, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        head.draft_step(xd, nwd, 1e-6, 4, td, 3.0, h_out=h, out=tok, emb_out=emb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        head.draft_step(xd, nwd, 1e-6, 4, td, 3.0, h_out=h, out=tok, emb_out=emb)
+    for _ in range(3):
+        h.zero_()
+        tok.fill_(-5)
+        emb.fill_(7.0)
+        head.top_tokens(h_e, 4)          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h.view(torch.int16), h_e.view(torch.int16))
+        assert torch.equal(tok, tok_e)
+        assert torch.equal(emb.view(torch.int16), emb_e.view(torch.int16))
