@@ -6,3 +6,4 @@ leg may import this package.  The product path never does.
 
 from .masked_head import *  # noqa: F401,F403
 from .draft import *  # noqa: F401,F403
+from .fp8_slabs import *  # noqa: F401,F403
