@@ -84,10 +84,14 @@ class Head:
     ``token_of_slot`` (host, ``[V]``) gives the token id of each embedding row;
     ``cluster_offsets`` (host, ``[Nc+1]``) gives each centroid's slot range, or
     None for equal clusters.  ``max_B``/``max_K`` bound later calls.
+    ``slabs="fp8"`` stores the embedding slabs as OCP E4M3 codes with a
+    float32 scale per row (bf16 heads only; logits change accordingly).
     """
 
     def __init__(self, centroids, emb_ordered, token_of_slot, cluster_offsets=None,
-                 max_B: int = 64, max_K: int | None = None):
+                 max_B: int = 64, max_K: int | None = None, slabs: str = "native"):
+        if slabs not in ("native", "fp8"):
+            raise ValueError("slabs must be 'native' or 'fp8'")
         torch = _torch()
         self._lib = _ffi.load()
         for name, t in (("centroids", centroids), ("emb_ordered", emb_ordered)):
@@ -110,7 +114,9 @@ class Head:
             emb_ordered=emb_ordered.data_ptr(),
             cluster_offsets=None if self._off is None else
             self._off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-            token_of_slot=self._tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+            token_of_slot=self._tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            slab_format=_ffi.CE_SLAB_FP8_E4M3 if slabs == "fp8" else _ffi.CE_SLAB_NATIVE)
+        self.slabs = slabs
         handle = ctypes.c_void_p()
         check(self._lib.ce_head_create(ctypes.byref(desc), ctypes.byref(handle)), "ce_head_create")
         self._handle = handle

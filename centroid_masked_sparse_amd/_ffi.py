@@ -17,6 +17,7 @@ CE_F32, CE_BF16 = 0, 1
 CE_OP_SCORE, CE_OP_TOPK, CE_OP_TOP_TOKENS, CE_OP_MASKED_LOGITS, CE_OP_TOP_M = 0, 1, 2, 3, 4
 CE_OP_DRAFT_STEP = 5
 CE_MAX_TOP_M = 32
+CE_SLAB_NATIVE, CE_SLAB_FP8_E4M3 = 0, 1
 
 # Every symbol the header declares, with (restype, argtypes).
 _vp = ctypes.c_void_p
@@ -29,6 +30,7 @@ class HeadDesc(ctypes.Structure):
         ("d", _i32), ("V", _i32), ("Nc", _i32), ("max_B", _i32), ("max_K", _i32),
         ("dtype", _i32), ("centroids", _vp), ("emb_ordered", _vp),
         ("cluster_offsets", ctypes.POINTER(_i32)), ("token_of_slot", ctypes.POINTER(_i32)),
+        ("slab_format", _i32),
     ]
 
 

@@ -23,7 +23,7 @@
 #include "ce_internal.h"
 
 struct ce_head {
-  int32_t d = 0, V = 0, Nc = 0, max_B = 0, max_K = 0, dtype = 0;
+  int32_t d = 0, V = 0, Nc = 0, max_B = 0, max_K = 0, dtype = 0, slab = CE_SLAB_NATIVE;
   const void* C = nullptr;
   const void* E = nullptr;
   std::vector<int32_t> offsets;       // [Nc+1]
@@ -96,7 +96,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
 
 // Offsets of the device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t offsets, tos, tiles, ttok, et, ct, total;
+  size_t offsets, tos, tiles, ttok, et, escale, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -112,7 +112,9 @@ PersistLayout persist_layout(const ce_head* h) {
   p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
   p.ttok = take(std::max<size_t>(h->ttok.size(), 1) * sizeof(int32_t));
   const size_t tile_bytes = (size_t)ce::kTileTokens * h->d * elem_bytes(h->dtype);
-  p.et = take(h->tiles.size() * tile_bytes);
+  const size_t slab_tile = h->slab == CE_SLAB_FP8_E4M3 ? (size_t)ce::kTileTokens * h->d : tile_bytes;
+  p.et = take(h->tiles.size() * slab_tile);
+  p.escale = h->slab == CE_SLAB_FP8_E4M3 ? take(h->tiles.size() * ce::kTileTokens * sizeof(float)) : 0;
   p.ct = take((((size_t)h->Nc + ce::kTileTokens - 1) / ce::kTileTokens) * tile_bytes);
   p.total = off;
   return p;
@@ -284,6 +286,10 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
   if (!desc->centroids || !desc->emb_ordered || !desc->token_of_slot)
     return fail(CE_ERR_NULL_POINTER, "centroids, emb_ordered and token_of_slot are required");
   if (desc->dtype != CE_F32 && desc->dtype != CE_BF16) return fail(CE_ERR_BAD_DTYPE, "dtype must be CE_F32 or CE_BF16");
+  if (desc->slab_format != CE_SLAB_NATIVE && desc->slab_format != CE_SLAB_FP8_E4M3)
+    return fail(CE_ERR_BAD_DTYPE, "slab_format must be CE_SLAB_NATIVE or CE_SLAB_FP8_E4M3");
+  if (desc->slab_format == CE_SLAB_FP8_E4M3 && desc->dtype != CE_BF16)
+    return fail(CE_ERR_BAD_DTYPE, "FP8 slabs are quantised from bf16 heads only");
   const int d = desc->d, V = desc->V, Nc = desc->Nc;
   if (d < 64 || d > ce::kMaxD || d % 64) return fail(CE_ERR_BAD_SHAPE, "d must be a multiple of 64 in [64, 8192]");
   if (V < 1) return fail(CE_ERR_BAD_SHAPE, "V must be >= 1");
@@ -301,6 +307,7 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
   h->max_B = desc->max_B;
   h->max_K = desc->max_K;
   h->dtype = desc->dtype;
+  h->slab = desc->slab_format;
   h->C = desc->centroids;
   h->E = desc->emb_ordered;
   try {
@@ -395,10 +402,16 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
                                   hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
   }
-  hipError_t e = ce::launch_pack(head->E, head->dtype, head->d, (long)head->tiles.size(),
-                                 reinterpret_cast<const uint32_t*>(base + p.tiles),
-                                 reinterpret_cast<const int32_t*>(base + p.offsets), head->V,
-                                 base + p.et, stream);
+  hipError_t e =
+      head->slab == CE_SLAB_FP8_E4M3
+          ? ce::launch_pack_fp8(head->E, head->d, (long)head->tiles.size(),
+                                reinterpret_cast<const uint32_t*>(base + p.tiles),
+                                reinterpret_cast<const int32_t*>(base + p.offsets), base + p.et,
+                                reinterpret_cast<float*>(base + p.escale), stream)
+          : ce::launch_pack(head->E, head->dtype, head->d, (long)head->tiles.size(),
+                            reinterpret_cast<const uint32_t*>(base + p.tiles),
+                            reinterpret_cast<const int32_t*>(base + p.offsets), head->V,
+                            base + p.et, stream);
   if (e == hipSuccess)
     e = ce::launch_pack(head->C, head->dtype, head->d,
                         ((long)head->Nc + ce::kTileTokens - 1) / ce::kTileTokens, nullptr, nullptr,
@@ -413,6 +426,9 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   head->tables.tpc = head->tpc;
   head->tables.ttok = reinterpret_cast<const int32_t*>(base + p.ttok);
   head->tables.ET = base + p.et;
+  head->tables.slab = head->slab == CE_SLAB_FP8_E4M3 ? 1 : 0;
+  head->tables.escale = head->slab == CE_SLAB_FP8_E4M3 ? reinterpret_cast<const float*>(base + p.escale)
+                                                        : nullptr;
   head->tables.CT = base + p.ct;
   head->prepared = true;
   return CE_SUCCESS;

@@ -24,6 +24,8 @@ struct Tables {
   int tpc;                     // tiles per cluster when every cluster holds as many, else 0
   const int32_t* ttok;         // [n_tiles][64] token id of each tile slot, -1 past the cluster's end
   const void* ET;              // packed embeddings: [n_tiles][d/vec][64] 16-byte vectors
+  int slab;                    // 0: the head's dtype; 1: E4M3 codes (16 per vector)
+  const float* escale;         // E4M3 slabs: [n_tiles][64] row scales
   const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
 };
 
@@ -81,6 +83,9 @@ struct PassArgs {
 // Pack rows of W into 64-row tiles [t][v][lane] (see ce_kernels.hip).
 hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint32_t* tiles,
                        const int32_t* offsets, int nrows_total, void* out, hipStream_t s);
+// Quantise bf16 rows to E4M3 with row scales and pack them the same way.
+hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* tiles,
+                           const int32_t* offsets, void* out, float* scale, hipStream_t s);
 hipError_t launch_scores(const PassArgs& a, hipStream_t s);
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: TopkMode
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);

@@ -69,9 +69,12 @@ constexpr int kGatherRows = 4;   // hidden rows dotted per pass over a gather ti
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef double v2d __attribute__((ext_vector_type(2)));
 
+// Weight element types: fp32, bf16 bits, and OCP E4M3 codes (FP8 slabs,
+// whose hidden rows stay bf16).
 template <typename T> struct Elem;
-template <> struct Elem<float> { static constexpr int kPerVec = 4; };      // fp32
-template <> struct Elem<uint16_t> { static constexpr int kPerVec = 8; };   // bf16 bits
+template <> struct Elem<float> { static constexpr int kPerVec = 4; typedef float hidden; };
+template <> struct Elem<uint16_t> { static constexpr int kPerVec = 8; typedef uint16_t hidden; };
+template <> struct Elem<uint8_t> { static constexpr int kPerVec = 16; typedef uint16_t hidden; };
 
 // 16 bytes of elements -> float64, exactly.
 __device__ __forceinline__ void widen(const v4u v, double (&x)[4], float) {
@@ -83,6 +86,20 @@ __device__ __forceinline__ void widen(const v4u v, double (&x)[8], uint16_t) {
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = (double)__uint_as_float(v[i] << 16);
     x[2 * i + 1] = (double)__uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+// E4M3 codes: gfx950's packed conversion decodes OCP E4M3 exactly (all 256
+// codes checked against the format's definition).
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void widen(const v4u v, double (&x)[16], uint8_t) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
+    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
+    x[4 * i] = (double)lo.x;
+    x[4 * i + 1] = (double)lo.y;
+    x[4 * i + 2] = (double)hi.x;
+    x[4 * i + 3] = (double)hi.y;
   }
 }
 
@@ -140,6 +157,80 @@ __global__ __launch_bounds__(256) void pack_kernel(const v4u* __restrict__ W, in
   }
 }
 
+// OCP E4M3 code of a finite float64: nearest, ties to even, magnitudes
+// beyond 448 saturate to 448, the sign of zero kept.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t sign = (uint32_t)(u >> 56) & 0x80u;
+  const unsigned long long mag = u & 0x7FFFFFFFFFFFFFFFull;
+  const double a = __longlong_as_double((long long)mag);
+  if (a < 0x1p-6) {
+    // subnormal codes k * 2^-9; k = 8 is code 0x08, the smallest normal
+    return sign | (uint32_t)rint(a * 512.0);
+  }
+  int e = (int)(mag >> 52) - 1023;
+  const unsigned long long m = (mag & ((1ull << 52) - 1ull)) | (1ull << 52);
+  unsigned long long q = m >> 49;                 // leading one and three fraction bits
+  const unsigned long long rem = m & ((1ull << 49) - 1ull), half = 1ull << 48;
+  if (rem > half || (rem == half && (q & 1ull))) ++q;
+  if (q == 16) {
+    q = 8;
+    ++e;
+  }
+  if (e > 8 || (e == 8 && q > 14)) return sign | 0x7Eu;
+  return sign | ((uint32_t)(e + 7) << 3) | (uint32_t)(q - 8);
+}
+
+// Quantise the rows of W (bf16, [rows][d] row-major) to E4M3 with one float32
+// scale per row, s = fl32(max |w| / 448) (1 for a zero row), codes
+// E4M3(fl64(w / s)), and pack them like pack_kernel: tile t of the cluster
+// tile list, [t][d/16][lane] vectors of 16 codes, scale[t][lane].  One
+// thread per tile row; lanes past a tile's last row get zero codes and scale.
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restrict__ W, int d,
+                                                       long n_rows_out,
+                                                       const uint32_t* __restrict__ tiles,
+                                                       const int32_t* __restrict__ offsets,
+                                                       v4u* __restrict__ out,
+                                                       float* __restrict__ scale) {
+  const int nvec = d / 16;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < n_rows_out; o += stride) {
+    const int lane = (int)(o % kTileTokens);
+    const long t = o / kTileTokens;
+    const uint32_t w = tiles[t];
+    const int c = (int)(w & ((1u << kTileShift) - 1u));
+    const long row = (long)offsets[c] + (long)(w >> kTileShift) * kTileTokens + lane;
+    v4u* dst = out + t * (long)nvec * kTileTokens + lane;
+    if (row >= offsets[c + 1]) {
+      for (int v = 0; v < nvec; ++v) dst[(long)v * kTileTokens] = v4u{0u, 0u, 0u, 0u};
+      scale[o] = 0.0f;
+      continue;
+    }
+    const uint16_t* x = W + row * d;
+    float amax = 0.0f;
+    for (int k = 0; k < d; ++k) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)x[k] << 16)));
+    // fl64 then fl32 of amax/448 equals the correctly rounded float32
+    // quotient: for a bf16 amax it is exact or far from a float32 midpoint
+    const float s = amax > 0.0f ? (float)((double)amax / 448.0) : 1.0f;
+    const double sd = (double)s;
+    for (int v = 0; v < nvec; ++v) {
+      v4u q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const double xv = (double)__uint_as_float((uint32_t)x[16 * v + 4 * i + b] << 16);
+          word |= e4m3_rne_sat(xv / sd) << (8 * b);
+        }
+        q[i] = word;
+      }
+      dst[(long)v * kTileTokens] = q;
+    }
+    scale[o] = s;
+  }
+}
+
 // ------------------------------------------------------------------ dot tile
 
 // acc = fma(h_k, x_k, acc) for the elements k of one weight vector, in
@@ -178,6 +269,33 @@ __device__ __forceinline__ void fmac_vec(double& acc, const double (&hq)[4], con
       : "+v"(acc)
       : "v"(hq[0]), "v"(hq[1]), "v"(hq[2]), "v"(hq[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]),
         "v"(x[3]), "n"(J));
+}
+template <int J>
+__device__ __forceinline__ void fmac_vec(double& acc, const double (&hq)[4], const double (&x)[16]) {
+  // E4M3: elements 16p..16p+15 sit in lanes J = 4p .. 4p+3, four each
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f64_dpp %0, %1, %5 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %6 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %7 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %8 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %1, %9 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %10 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %11 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %12 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %1, %13 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %14 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %15 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %16 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %1, %17 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %18 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %19 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(hq[0]), "v"(hq[1]), "v"(hq[2]), "v"(hq[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]),
+        "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]),
+        "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]), "n"(J),
+        "n"(J + 1), "n"(J + 2), "n"(J + 3));
 }
 // f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, typename F>
@@ -223,15 +341,17 @@ struct NoOp {
 // produce the hidden rows (in LDS) while the tile loads are in flight.
 template <typename T, int RB, int NCH, int STAGES = 2, bool SPLIT = false, typename Mid = NoOp>
 __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
-                                         const T* __restrict__ h, const int (&rows)[RB], int nrows,
-                                         double (&acc)[RB], Mid&& mid = Mid()) {
+                                         const typename Elem<T>::hidden* __restrict__ h,
+                                         const int (&rows)[RB], int nrows, double (&acc)[RB],
+                                         Mid&& mid = Mid()) {
+  using TH = typename Elem<T>::hidden;
   constexpr int PV = Elem<T>::kPerVec;
   constexpr int VPC = kChunk / PV;              // weight vectors per chunk
-  using HR = typename HQuad<T>::raw;
+  using HR = typename HQuad<TH>::raw;
   const int lane = threadIdx.x;
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = 0.0;
-  const T* hp[RB];
+  const TH* hp[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) hp[r] = h + (long)rows[r] * d + 4 * (lane & 15);
 
@@ -902,6 +1022,7 @@ struct GatherArgs {
   const uint32_t* tiles;        // [n_tiles] (index in cluster << 13) | cluster
   int tpc;                      // tiles per cluster when all clusters hold as many, else 0
   const int32_t* ttok;          // [n_tiles][64] token of each slot, -1 past the cluster's end
+  const float* escale;          // FP8 slabs: [n_tiles][64] row scales
   unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
                                 // top-m: [64] packed (segments << 32 | keys) per row
   float* out;                   // forward: [B][V] output rows (already -inf)
@@ -951,9 +1072,12 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   // the token ids are needed only after the first batch is dotted: they
   // are waited for there, not before the tile loads go out
   int tok = a.ttok[(long)blockIdx.x * kWave + lane];
+  // FP8 slabs: the slot's row scale, applied to the finished chain
+  float sc = 1.0f;
+  if constexpr (std::is_same<T, uint8_t>::value) sc = a.escale[(long)blockIdx.x * kWave + lane];
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
   const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
-  const T* h = reinterpret_cast<const T*>(a.h);
+  const auto* h = reinterpret_cast<const typename Elem<T>::hidden*>(a.h);
 
   // argmax: wave maximum of the packed (ordered logit, ~token) per row,
   // max-ed into the row's slot; forward: each candidate logit stored at its
@@ -963,7 +1087,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (r < nrows) {
-        const float f = canon(acc[r]);
+        const float f = std::is_same<T, uint8_t>::value ? canon(acc[r] * (double)sc) : canon(acc[r]);
         if (MODE == kArgmax) {
           unsigned long long k = 0ull;
           if (tok >= 0)
@@ -1005,7 +1129,8 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     const int nrows = take_rows<RB>(mask, rows, 0);
     double acc[RB];
     dot_tile<T, RB, NCH>(wtb, a.d, h, rows, nrows, acc);
-    pin(tok);   // keep the load out of the branches below
+    pin(tok);   // keep the loads out of the branches below
+    pin(sc);
     finish(rows, nrows, acc);
   }
 }
@@ -1168,6 +1293,18 @@ hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint
   return hipGetLastError();
 }
 
+hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* tiles,
+                           const int32_t* offsets, void* out, float* scale, hipStream_t s) {
+  const long n_rows_out = n_tiles * kTileTokens;
+  if (n_rows_out == 0) return hipSuccess;
+  long blocks = (n_rows_out + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(W), d, n_rows_out, tiles, offsets,
+                     static_cast<v4u*>(out), scale);
+  return hipGetLastError();
+}
+
 template <typename T, int RB, int NCH>
 static void launch_scores_n(const PassArgs& a, hipStream_t s) {
   const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
@@ -1247,6 +1384,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tiles = a.t.tiles;
   g.tpc = a.t.tpc;
   g.ttok = a.t.ttok;
+  g.escale = a.t.escale;
   g.best = a.best;
   g.out = a.logits;
   g.V = a.V;
@@ -1271,6 +1409,11 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
 
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s) {
   if (a.t.n_tiles == 0) return hipSuccess;   // every cluster is empty
+  if (a.t.slab == 1) {
+    if (mode == kArgmax) return launch_gather_t<uint8_t, kArgmax>(a, s);
+    if (mode == kMasked) return launch_gather_t<uint8_t, kMasked>(a, s);
+    return launch_gather_t<uint8_t, kTopM>(a, s);
+  }
   if (a.dtype == 1) {
     if (mode == kArgmax) return launch_gather_t<uint16_t, kArgmax>(a, s);
     if (mode == kMasked) return launch_gather_t<uint16_t, kMasked>(a, s);

@@ -71,6 +71,25 @@ typedef enum ce_dtype {
   CE_BF16 = 1   /* bfloat16 (upper half of a binary32) */
 } ce_dtype;
 
+/* Storage of the embedding slabs the gather reads (ce_head_desc.slab_format).
+ *   CE_SLAB_NATIVE    the head's dtype (default; zero-initialised descs)
+ *   CE_SLAB_FP8_E4M3  bf16 heads only: each ordered row j stored as OCP
+ *                     8-bit E4M3 codes q_jk = E4M3(fl64(E[j,k] / s_j)) (round
+ *                     to nearest even, saturating at 448) with the float32
+ *                     scale s_j = fl32(max_k |E[j,k]| / 448) (1 for a zero
+ *                     row), packed at prepare time.  Candidate logits become
+ *                     fl32(fl64(acc * s_j)) with acc the canonical float64
+ *                     chain over the decoded codes; centroid scores and top-K
+ *                     are unchanged (the centroids stay bf16).  Half the
+ *                     gathered bytes; the error against the bf16 head is at
+ *                     most sum_k |h_k| (2^-4 |E[j,k]| + 2^-10 s_j) plus the
+ *                     final rounding.  The pages do not quantise; this is a
+ *                     reduced-precision option with numerics of its own. */
+typedef enum ce_slab {
+  CE_SLAB_NATIVE = 0,
+  CE_SLAB_FP8_E4M3 = 1
+} ce_slab;
+
 typedef enum ce_op {
   CE_OP_SCORE = 0,          /* ce_score_centroids */
   CE_OP_TOPK = 1,           /* ce_topk */
@@ -101,6 +120,7 @@ typedef struct ce_graph* ce_graph_t;
  *                   offsets[Nc] = V; or NULL for equal clusters (V % Nc == 0).
  *                   Empty clusters are allowed.  Copied at create.
  *   token_of_slot   HOST [V], a permutation of 0..V-1.  Copied at create.
+ *   slab_format     ce_slab; CE_SLAB_FP8_E4M3 needs dtype CE_BF16.
  * The two device arrays are read only by ce_head_prepare, which packs them
  * into the persistent buffer; they may be freed or changed afterwards. */
 typedef struct ce_head_desc {
@@ -114,6 +134,7 @@ typedef struct ce_head_desc {
   const void* emb_ordered;
   const int32_t* cluster_offsets;
   const int32_t* token_of_slot;
+  int32_t slab_format;
 } ce_head_desc;
 
 /* Validate desc on the host and create a head.  Makes no HIP call.
@@ -128,11 +149,12 @@ ce_status ce_head_destroy(ce_head_t head);
 ce_status ce_head_persistent_bytes(ce_head_t head, size_t* bytes);
 
 /* Fill the caller's persistent device buffer (256-byte aligned, at least
- * ce_head_persistent_bytes): the derived tables (offsets, slot->token and
- * token->(cluster, rank) maps, the list of 64-slot cluster tiles) and packed
- * copies of the centroids and embeddings in 64-row tiles whose 16-byte
- * vectors are interleaved across rows, so that the hot kernels stream them
- * with fully coalesced loads (one more copy of the weights in HBM).  Set-up
+ * ce_head_persistent_bytes): the derived tables (offsets, the slot->token
+ * map, the list of 64-slot cluster tiles and each tile's slot tokens) and
+ * packed copies of the centroids and embeddings (quantised for FP8 slabs,
+ * with their row scales) in 64-row tiles whose 16-byte vectors are
+ * interleaved across rows, so that the hot kernels stream them with fully
+ * coalesced loads (one more copy of the weights in HBM).  Set-up
  * only: copies and packs on `stream` and synchronises it.  The buffer must
  * live as long as the head is used.
  * Errors: NULL_POINTER, MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */

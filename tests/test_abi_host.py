@@ -48,12 +48,13 @@ def test_header_symbols_exported(lib):
 
 
 def _desc(d=64, V=256, Nc=4, max_B=8, max_K=4, dtype=_ffi.CE_BF16, tos=None, off=None,
-          c_ptr=FAKE, e_ptr=FAKE):
+          c_ptr=FAKE, e_ptr=FAKE, slab=_ffi.CE_SLAB_NATIVE):
     tos = np.arange(V, dtype=np.int32) if tos is None else np.asarray(tos, dtype=np.int32)
     keep = [tos]
     desc = _ffi.HeadDesc(d=d, V=V, Nc=Nc, max_B=max_B, max_K=max_K, dtype=dtype,
                          centroids=c_ptr, emb_ordered=e_ptr,
-                         token_of_slot=tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+                         token_of_slot=tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         slab_format=slab)
     if off is not None:
         off = np.asarray(off, dtype=np.int32)
         keep.append(off)
@@ -87,6 +88,8 @@ ERR = {v: k for k, v in _ffi.STATUS_NAMES.items()}
     (dict(off=[0, 10, 20, 30, 255]), "CE_ERR_BAD_LAYOUT"),    # does not end at V
     (dict(off=[1, 10, 20, 30, 256]), "CE_ERR_BAD_LAYOUT"),    # does not start at 0
     (dict(c_ptr=0), "CE_ERR_NULL_POINTER"),
+    (dict(slab=2), "CE_ERR_BAD_DTYPE"),
+    (dict(slab=_ffi.CE_SLAB_FP8_E4M3, dtype=_ffi.CE_F32), "CE_ERR_BAD_DTYPE"),   # FP8 from bf16 only
 ])
 def test_create_rejects(lib, kw, want):
     desc, _keep = _desc(**kw)
@@ -184,3 +187,28 @@ def test_product_path_never_imports_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "workloads" not in text, f
+
+
+def test_fp8_slab_sizes(lib):
+    """FP8 slabs halve the packed embedding bytes of a bf16 head and add a
+    float32 scale per tile row; the workspace does not change."""
+    off = [0, 0, 100, 130, 256]
+    tos = np.random.default_rng(0).permutation(256)
+    sizes = {}
+    for slab in (_ffi.CE_SLAB_NATIVE, _ffi.CE_SLAB_FP8_E4M3):
+        desc, _keep = _desc(tos=tos, off=off, max_B=100, max_K=4, slab=slab)
+        st, h = _create(lib, desc)
+        assert st == 0
+        try:
+            n = ctypes.c_size_t()
+            assert lib.ce_head_persistent_bytes(h, ctypes.byref(n)) == 0
+            w = ctypes.c_size_t()
+            assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(w)) == 0
+            sizes[slab] = (n.value, w.value)
+        finally:
+            lib.ce_head_destroy(h)
+    native, fp8 = sizes[_ffi.CE_SLAB_NATIVE], sizes[_ffi.CE_SLAB_FP8_E4M3]
+    # 5 tiles of 64 rows x 64 elements: 5 * 8192 bytes of bf16 become 5 * 4096
+    # bytes of codes plus 5 * 256 bytes of scales (each region 256-aligned)
+    assert native[0] - fp8[0] == 5 * 8192 - 5 * 4096 - 5 * 256
+    assert native[1] == fp8[1]
