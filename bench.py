@@ -244,6 +244,65 @@ def _draft_section(torch, heads, groups, K, args, stream, log):
     return rows
 
 
+def _fp8_section(torch, heads, groups, H, w, K, args, stream, log):
+    """Top tokens with FP8 (E4M3) slabs: one FP8 head quantised at prepare
+    time from each bf16 weight copy, timed like the headline (eager C-ABI
+    calls, rotating copies and row groups) at B in {1, 16, 64}.  Bytes are
+    the union of selected clusters' codes and float32 row scales plus the bf16
+    centroids.  Also: how often the FP8 argmax equals the bf16 argmax on the
+    64 rows, and the FP8 gather kernel alone at B=64."""
+    from centroid_masked_sparse_amd import Head, _ffi
+    dev = "cuda:0"
+    d, Nc, sizes = w.d, w.Nc, w.sizes
+    fheads = [Head(h._keep[0], h._keep[1], w.tos, max_B=64, max_K=K, slabs="fp8") for h in heads]
+    torch.cuda.synchronize()
+    rows = []
+    slab64 = None
+    for B in (1, 16, 64):
+        hs = groups(B)
+        topk = torch.empty((B, K), dtype=torch.int32, device=dev)
+        ub = []
+        for hg in hs:
+            heads[0].top_tokens(hg, K, topk_out=topk)
+            torch.cuda.synchronize()
+            ub.append(_union_bytes(topk.cpu().numpy(), sizes, d + 4, 1)[0])
+        slab = float(np.mean(ub))
+        unique = Nc * d * 2 + slab
+        us = _eager_us_per_call(torch, fheads, hs, K, B, args.steps, args.warmup, stream)
+        row = {"B": B, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
+               "unique_MiB": round(unique / 2**20, 2), "GB_s": round(unique / (us * 1e-6) / 1e9, 1)}
+        rows.append(row)
+        log(f"[bench] fp8 top_tokens B={B}: {row}")
+        if B == 64:
+            slab64 = slab
+    tb = heads[0].top_tokens(H, K)
+    tf = fheads[0].top_tokens(H, K)
+    agree = float((tb == tf).float().mean().item())
+    n = args.probe_calls
+    start_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    stop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in start_ev + stop_ev:
+        e.record()                      # creates the HIP events
+    torch.cuda.synchronize()
+    out = torch.empty((64,), dtype=torch.int32, device=dev)
+    for i in range(n):
+        _ffi.check(fheads[0]._lib.ce_probe_gather_events(start_ev[i].cuda_event, stop_ev[i].cuda_event),
+                   "ce_probe_gather_events")
+        fheads[i % len(fheads)].top_tokens(H, K, out=out)
+    torch.cuda.synchronize()
+    g_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(start_ev, stop_ev)]))
+    res = {"format": "OCP E4M3 codes + fp32 row scale", "argmax_agreement_with_bf16": round(agree, 4),
+           "sweep": rows, "gather_us_B64": round(g_ms * 1e3, 3),
+           "gather_GB_s_B64": round(slab64 / (g_ms * 1e-3) / 1e9, 1)}
+    log(f"[bench] fp8 slabs: agreement {agree:.4f}, gather B=64 {g_ms * 1e3:.2f} us, "
+        f"{res['gather_GB_s_B64']} GB/s")
+    for h in fheads:
+        h.close()
+    del fheads
+    torch.cuda.empty_cache()
+    return res
+
+
 def _wide_section(torch, args, stream, log):
     """The wide head at B=64: the sparse head at K=64 and at K=Nc (every
     centroid: the exact dense argmax), beside a dense comparison path, the
@@ -324,6 +383,7 @@ def main() -> int:
     ap.add_argument("--no-wide", action="store_true")
     ap.add_argument("--no-top-m", action="store_true")
     ap.add_argument("--no-draft", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--probe-calls", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -500,6 +560,11 @@ def main() -> int:
     if not args.no_draft:
         draft = _draft_section(torch, heads, groups, K, args, stream, log)
 
+    # ------------------------------------------------------------ FP8 slabs
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = _fp8_section(torch, heads, groups, H, w, K, args, stream, log)
+
     # ------------------------------------------------------------ wide head (d=1024, Nc=4096)
     wide = None
     if not args.no_wide:
@@ -554,6 +619,7 @@ def main() -> int:
         "masked": masked,
         "top_m": top_m,
         "draft_step": draft,
+        "fp8_slabs": fp8,
         "wide": wide,
     }
     print(json.dumps(line), flush=True)
