@@ -8,8 +8,10 @@ kernel launches).  Each sweep row also reports the same call replayed from a
 captured HIP graph (the pages' sequencing; on ROCm a graph launch costs more
 host and device time than the four launches it replaces) and the device time
 per call with eight calls captured in one graph.  The line also carries every
-batch size of the sweep, the masked full-vocabulary output (forward) at B in
-{1, 16, 64} (graph replays) and the wide head with its dense comparison path.
+batch size of the sweep, the masked full-vocabulary output (forward), the
+fused top-m, the fused draft step and FP8 slabs at B in {1, 16, 64} (eager
+calls; forward also as graph replays), and the wide head with its dense
+comparison path.
 
 Cold HBM: every step uses a different copy of the weights (``--copies``,
 default 8, about 1 GiB) and, for B < 64, a different group of hidden rows, so
@@ -520,11 +522,23 @@ def main() -> int:
             cold = [per_copy[m][s][0] for s in range(len(hs)) for m in range(len(heads))]
             steps = max(50, args.steps // 4)
             ms = _time_replays(torch, cold, steps, max(10, args.warmup // 4), stream)
-            us = ms * 1e3
+            graph_us = ms * 1e3
+            # eager C-ABI calls (the fill then runs beside the projection and
+            # top-K on the library's side stream), same rotation
+            calls = []
+            for s_ in range(len(hs)):
+                for m_, head in enumerate(heads):
+                    o = per_copy[m_][s_][1]
+                    ws = head._workspace(B, K, OP_MASKED_LOGITS)
+                    calls.append((head._lib.ce_masked_logits,
+                                  (head._handle, hs[s_].data_ptr(), B, K, o.data_ptr(), None,
+                                   ws.data_ptr(), ws.numel(), stream)))
+            us = _time_calls(torch, calls, steps, max(10, args.warmup // 4))
             row = {"B": B, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
                    "bytes_MiB": round(unique / 2**20, 2),
                    "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
-                   "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+                   "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                   "graph_us_per_call": round(graph_us, 3)}
             masked.append(row)
             log(f"[bench] masked_logits B={B}: {row}")
             for gl in per_copy:

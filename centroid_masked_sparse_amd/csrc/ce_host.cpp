@@ -241,6 +241,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.tm_logits = out2 + (size_t)b0 * m;
     } else {
       a.logits = static_cast<float*>(out) + (size_t)b0 * h->V;
+      a.fill = a.logits;
     }
     if (b0 == 0) {
       a.probe_start = pstart;

@@ -74,7 +74,8 @@ struct PassArgs {
   void* emb_out;          // [B][emb_dim]
   // outputs
   int32_t* tokens;        // [B]
-  float* logits;          // [B][V] forward output; the scores kernel fills it with -inf
+  float* logits;          // [B][V] forward output
+  float* fill;            // [B][V] rows the scores kernel's extra waves fill with -inf, or null
   // measurement hook (HIP extended launch around the gather kernel)
   hipEvent_t probe_start;
   hipEvent_t probe_stop;

@@ -47,6 +47,7 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ce_internal.h"
@@ -635,30 +636,24 @@ __device__ __forceinline__ void norm_finish(const NormRegs<T, RB, NG>& nr, const
 
 // ------------------------------------------------------------------ scores
 
-// Fill rows [r0, r0+nrows) of out ([*][V] fp32) with -inf over this
-// workgroup's share of the columns (forward: every entry that no candidate
-// overwrites).  Plain streaming stores; nothing waits on them.
-__device__ __forceinline__ void fill_neg_inf(float* __restrict__ out, int V, int r0, int nrows) {
+// Forward: -inf over out[0..n) ([B][V] rows, contiguous, 16-byte aligned),
+// the share of fill wave f of nfill: runs of 64 float4 (1 KiB per wave
+// store), strided over the fill waves.  Plain streaming stores.
+__device__ __forceinline__ void fill_share(float* __restrict__ out, long n, long f, long nfill) {
   const int lane = threadIdx.x;
-  const long per = ((long)V + gridDim.x - 1) / gridDim.x;
-  const long per4 = (per + 3) & ~3L;
-  const long c0 = (long)blockIdx.x * per4;
-  const long c1 = min((long)V, c0 + per4);
   const float ninf = -__builtin_inff();
-  for (int r = 0; r < nrows; ++r) {
-    float* row = out + (long)(r0 + r) * V;
-    if ((V & 3) == 0) {
-      for (long c = c0 + 4 * lane; c < c1; c += 4 * kWave)
-        *reinterpret_cast<float4*>(row + c) = make_float4(ninf, ninf, ninf, ninf);
-    } else {
-      for (long c = c0 + lane; c < c1; c += kWave) row[c] = ninf;
-    }
-  }
+  const long n4 = n / 4;
+  for (long i = f * kWave + lane; i < n4; i += nfill * kWave)
+    reinterpret_cast<float4*>(out)[i] = make_float4(ninf, ninf, ninf, ninf);
+  if (f == 0)
+    for (long i = 4 * n4 + lane; i < n; i += kWave) out[i] = ninf;
 }
 
 // One wave per (64-centroid tile, RB rows): S[b][c] for the tile's
-// centroids; with `fill` (forward) the wave also fills its share of the
-// output rows with -inf.
+// centroids.  With `fill` (forward) the grid has more rows of workgroups
+// than row groups: those waves fill the output rows with -inf while the
+// others compute (a wave that did both would wait for its stores at every
+// load: stores and loads share one counter).
 //
 // With NORM, h holds the rows before the final RMSNorm: the wave normalises
 // its rows into LDS (dynamic, [RB][d]) and dots the tile with those; the
@@ -674,8 +669,13 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   const int c0 = blockIdx.x * kTileTokens;
   const int r0 = blockIdx.y * RB;
   const int nvalid = min(kTileTokens, Nc - c0);
+  const int ngroups = (B + RB - 1) / RB;
+  if ((int)blockIdx.y >= ngroups) {
+    fill_share(fill, (long)B * V, (long)(blockIdx.y - ngroups) * gridDim.x + blockIdx.x,
+               (long)(gridDim.y - ngroups) * gridDim.x);
+    return;
+  }
   const int nrows = min(RB, B - r0);
-  if (fill) fill_neg_inf(fill, V, r0, nrows);
   int rows[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) rows[r] = r0 + (r < nrows ? r : nrows - 1);
@@ -1305,18 +1305,27 @@ hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* t
   return hipGetLastError();
 }
 
+// Fill waves of the forward: about one per 64 KiB of output rows, at least
+// one row of the grid, at most 1024.
+static int fill_grid_rows(const PassArgs& a, int gx) {
+  if (!a.fill) return 0;
+  const long waves = std::min<long>(1024, std::max<long>(1, (long)a.B * a.V * 4 / 65536));
+  return (int)std::max<long>(1, (waves + gx - 1) / gx);
+}
+
 template <typename T, int RB, int NCH>
 static void launch_scores_n(const PassArgs& a, hipStream_t s) {
-  const dim3 grid((a.Nc + kTileTokens - 1) / kTileTokens, (a.B + RB - 1) / RB);
+  const int gx = (a.Nc + kTileTokens - 1) / kTileTokens;
+  const dim3 grid(gx, (a.B + RB - 1) / RB + fill_grid_rows(a, gx));
   NormArgs nm{a.norm_w, (double)a.norm_eps, a.h_out};
   if (a.norm_w)
     hipLaunchKernelGGL((scores_kernel<T, RB, NCH, true>), grid, dim3(64),
                        (size_t)RB * a.d * sizeof(T), s, static_cast<const v4u*>(a.t.CT), a.Nc,
-                       a.d, static_cast<const T*>(a.h), a.B, a.S, a.ldS, a.logits, a.V, nm);
+                       a.d, static_cast<const T*>(a.h), a.B, a.S, a.ldS, a.fill, a.V, nm);
   else
     hipLaunchKernelGGL((scores_kernel<T, RB, NCH, false>), grid, dim3(64), 0, s,
                        static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const T*>(a.h), a.B,
-                       a.S, a.ldS, a.logits, a.V, nm);
+                       a.S, a.ldS, a.fill, a.V, nm);
 }
 
 // Hidden sizes with a straight-line chunk pipeline; others take the generic one.
