@@ -10,8 +10,9 @@ host and device time than the four launches it replaces) and the device time
 per call with eight calls captured in one graph.  The line also carries every
 batch size of the sweep, the masked full-vocabulary output (forward), the
 fused top-m, the fused draft step and FP8 slabs at B in {1, 16, 64} (eager
-calls; forward also as graph replays), and the wide head with its dense
-comparison path.
+calls; forward also as graph replays), the skewed head (Zipf clusters,
+correlated rows) at B=64, and the wide head with its dense comparison
+path.
 
 Cold HBM: every step uses a different copy of the weights (``--copies``,
 default 8, about 1 GiB) and, for B < 64, a different group of hidden rows, so
@@ -305,6 +306,55 @@ def _fp8_section(torch, heads, groups, H, w, K, args, stream, log):
     return res
 
 
+def _skewed_section(torch, args, stream, log):
+    """The skewed head at B=64 (d=512, V=262144, Nc=2048 Zipf(1.1) clusters of
+    10 .. 44,286 tokens, K=32, rows around 8 anchor directions): top_tokens
+    through the C ABI, cold over two weight copies (512 MiB), with the
+    gather alone.  Stresses the dedup (overlapping row sets) and the load
+    balance (one cluster is 692 tiles)."""
+    from centroid_masked_sparse_amd import Head, OP_TOP_TOKENS, _ffi
+    from workloads import make_workload
+    w = make_workload(5)
+    d, Nc, K, B = w.d, w.Nc, w.K, 64
+    C0 = _to_device(w.C, w.dtype, torch)
+    E0 = _to_device(w.E, w.dtype, torch)
+    H = _to_device(w.h, w.dtype, torch)[:B].contiguous()
+    heads = [Head(C0 if m == 0 else C0.clone(), E0 if m == 0 else E0.clone(), w.tos, w.offsets,
+                  max_B=B, max_K=K) for m in range(2)]
+    topk = torch.empty((B, K), dtype=torch.int32, device="cuda:0")
+    heads[0].top_tokens(H, K, topk_out=topk)
+    torch.cuda.synchronize()
+    slab, clusters = _union_bytes(topk.cpu().numpy(), w.sizes, d, 2)
+    unique = Nc * d * 2 + slab
+    us = _eager_us_per_call(torch, heads, [H], K, B, args.steps, args.warmup, stream)
+    n = max(20, args.probe_calls // 4)
+    start_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    stop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in start_ev + stop_ev:
+        e.record()
+    torch.cuda.synchronize()
+    o = torch.empty((B,), dtype=torch.int32, device="cuda:0")
+    for i in range(n):
+        _ffi.check(heads[0]._lib.ce_probe_gather_events(start_ev[i].cuda_event, stop_ev[i].cuda_event),
+                   "ce_probe_gather_events")
+        heads[i % 2].top_tokens(H, K, out=o)
+    torch.cuda.synchronize()
+    g_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(start_ev, stop_ev)]))
+    out = {"workload": f"skewed head d={d} V={w.V} Nc={Nc} Zipf(1.1) CSR, K={K} bf16, B={B}, "
+                       f"correlated rows, cold (2 weight copies)",
+           "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
+           "union_clusters": clusters, "unique_MiB": round(unique / 2**20, 2),
+           "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
+           "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "gather_us": round(g_ms * 1e3, 3), "gather_GB_s": round(slab / (g_ms * 1e-3) / 1e9, 1)}
+    log(f"[bench] skewed: {out}")
+    for h in heads:
+        h.close()
+    del heads, E0, C0
+    torch.cuda.empty_cache()
+    return out
+
+
 def _wide_section(torch, args, stream, log):
     """The wide head at B=64: the sparse head at K=64 and at K=Nc (every
     centroid: the exact dense argmax), beside a dense comparison path, the
@@ -386,6 +436,7 @@ def main() -> int:
     ap.add_argument("--no-top-m", action="store_true")
     ap.add_argument("--no-draft", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-skewed", action="store_true")
     ap.add_argument("--probe-calls", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -579,6 +630,11 @@ def main() -> int:
     if not args.no_fp8:
         fp8 = _fp8_section(torch, heads, groups, H, w, K, args, stream, log)
 
+    # ------------------------------------------------------------ skewed clusters (config 5)
+    skewed = None
+    if not args.no_skewed:
+        skewed = _skewed_section(torch, args, stream, log)
+
     # ------------------------------------------------------------ wide head (d=1024, Nc=4096)
     wide = None
     if not args.no_wide:
@@ -634,6 +690,7 @@ def main() -> int:
         "top_m": top_m,
         "draft_step": draft,
         "fp8_slabs": fp8,
+        "skewed": skewed,
         "wide": wide,
     }
     print(json.dumps(line), flush=True)

@@ -64,6 +64,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kChunk = 64;       // hidden dims per LDS step
 constexpr int kGatherRows = 4;   // hidden rows dotted per pass over a gather tile
+constexpr int kGatherSplitShift = 1;   // log2 waves per gather tile for large batches
 
 // 16 bytes as a native vector (HIP's uint4 wraps a union, which keeps arrays
 // of it out of registers).
@@ -1022,6 +1023,7 @@ struct GatherArgs {
   const uint32_t* tiles;        // [n_tiles] (index in cluster << 13) | cluster
   int tpc;                      // tiles per cluster when all clusters hold as many, else 0
   const int32_t* ttok;          // [n_tiles][64] token of each slot, -1 past the cluster's end
+  int split_shift;              // 2^split_shift waves per tile share its passes
   const float* escale;          // FP8 slabs: [n_tiles][64] row scales
   unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
                                 // top-m: [64] packed (segments << 32 | keys) per row
@@ -1063,20 +1065,29 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
 template <typename T, int RB, int MODE, int NCH>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
-  const int t = blockIdx.x;
+  // 2^split_shift consecutive waves per tile; the tile's passes of RB rows
+  // are dealt to them in turn, so a tile many rows selected is not one
+  // long wave
+  const int nsplit = 1 << a.split_shift;
+  const int slot = blockIdx.x & (nsplit - 1);
+  const int t = blockIdx.x >> a.split_shift;
   const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
   // lane b reads row b's selection word of c's 64-centroid block
   const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
   unsigned long long mask = __ballot((word >> (c % kWave)) & 1ull);
-  if (!mask) return;   // no row selected this tile's cluster
+  auto skip_passes = [&](int n) {
+    for (int i = 0; i < n * RB && mask; ++i) mask &= mask - 1ull;
+  };
+  skip_passes(slot);
+  if (!mask) return;   // no row selected this tile's cluster, or no pass left for this wave
   // the token ids are needed only after the first batch is dotted: they
   // are waited for there, not before the tile loads go out
-  int tok = a.ttok[(long)blockIdx.x * kWave + lane];
+  int tok = a.ttok[(long)t * kWave + lane];
   // FP8 slabs: the slot's row scale, applied to the finished chain
   float sc = 1.0f;
-  if constexpr (std::is_same<T, uint8_t>::value) sc = a.escale[(long)blockIdx.x * kWave + lane];
+  if constexpr (std::is_same<T, uint8_t>::value) sc = a.escale[(long)t * kWave + lane];
   const long tile_vecs = (long)(a.d / Elem<T>::kPerVec) * kWave;
-  const v4u* wt = a.ET + (long)blockIdx.x * tile_vecs;
+  const v4u* wt = a.ET + (long)t * tile_vecs;
   const auto* h = reinterpret_cast<const typename Elem<T>::hidden*>(a.h);
 
   // argmax: wave maximum of the packed (ordered logit, ~token) per row,
@@ -1132,6 +1143,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     pin(tok);   // keep the loads out of the branches below
     pin(sc);
     finish(rows, nrows, acc);
+    skip_passes(nsplit - 1);
   }
 }
 
@@ -1382,6 +1394,9 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Waves per tile (log2) for a pass of B rows.
+static int gather_split_shift(int B) { return B >= 32 ? kGatherSplitShift : 0; }
+
 template <typename T, int MODE>
 static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   GatherArgs g;
@@ -1394,6 +1409,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tpc = a.t.tpc;
   g.ttok = a.t.ttok;
   g.escale = a.t.escale;
+  g.split_shift = gather_split_shift(a.B);
   g.best = a.best;
   g.out = a.logits;
   g.V = a.V;
@@ -1402,7 +1418,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tm_heads = a.tm_heads;
   g.tm_cap = a.tm_cap;
   g.tm_segcap = a.tm_segcap;
-  const dim3 grid(a.t.n_tiles > 0 ? a.t.n_tiles : 1);
+  const dim3 grid(a.t.n_tiles > 0 ? (unsigned)a.t.n_tiles << g.split_shift : 1u);
   auto go = [&](auto kern) {
     if (a.probe_start && a.probe_stop) {
       hipExtLaunchKernelGGL(kern, grid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);
