@@ -1024,6 +1024,7 @@ struct GatherArgs {
   int tpc;                      // tiles per cluster when all clusters hold as many, else 0
   const int32_t* ttok;          // [n_tiles][64] token of each slot, -1 past the cluster's end
   int split_shift;              // 2^split_shift waves per tile share its passes
+  int n_tiles;
   const float* escale;          // FP8 slabs: [n_tiles][64] row scales
   unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
                                 // top-m: [64] packed (segments << 32 | keys) per row
@@ -1057,6 +1058,13 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
   return n;
 }
 
+// Register stages of the gather's tile ring: bf16 keeps a whole 256-dim tile
+// (four 8 KiB chunks) in flight, so a wave waits on one round trip rather
+// than three; fp32 chunks are twice as large, and FP8 chunks measured no
+// better with four.
+template <typename T>
+constexpr int kGatherStages = std::is_same<T, uint16_t>::value ? 4 : 2;
+
 // One wave per packed tile.  Once the rows that selected the tile's
 // cluster are known, the tile, the hidden rows and the slots' token ids are
 // all requested at once: they are addressed by the tile index alone.  With
@@ -1065,12 +1073,15 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
 template <typename T, int RB, int MODE, int NCH>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
-  // 2^split_shift consecutive waves per tile; the tile's passes of RB rows
-  // are dealt to them in turn, so a tile many rows selected is not one
-  // long wave
+  // 2^split_shift waves per tile; the tile's passes of RB rows are dealt to
+  // them in turn, so a tile many rows selected is not one long wave.  The
+  // grid is slot-major (wave slot * n_tiles + t): workgroups are dealt to
+  // the XCDs round-robin by index, and most tiles have a single pass, so
+  // consecutive waves of one tile would leave every other XCD without work,
+  // and the first slot's waves, the ones with work, are dispatched first.
   const int nsplit = 1 << a.split_shift;
-  const int slot = blockIdx.x & (nsplit - 1);
-  const int t = blockIdx.x >> a.split_shift;
+  const int slot = (int)blockIdx.x / a.n_tiles;
+  const int t = (int)blockIdx.x - slot * a.n_tiles;
   const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
   // lane b reads row b's selection word of c's 64-centroid block
   const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
@@ -1139,7 +1150,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     int rows[RB];
     const int nrows = take_rows<RB>(mask, rows, 0);
     double acc[RB];
-    dot_tile<T, RB, NCH>(wtb, a.d, h, rows, nrows, acc);
+    dot_tile<T, RB, NCH, kGatherStages<T>>(wtb, a.d, h, rows, nrows, acc);
     pin(tok);   // keep the loads out of the branches below
     pin(sc);
     finish(rows, nrows, acc);
@@ -1395,7 +1406,10 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
 }
 
 // Waves per tile (log2) for a pass of B rows.
-static int gather_split_shift(int B) { return B >= 32 ? kGatherSplitShift : 0; }
+// Below 48 rows a tile of the sweep head almost never needs a second pass
+// (B=32: 33.3 µs per call split or not); at 64 rows the two-pass tiles set
+// the gather's tail and splitting them takes the call from 39.2 to 37.8 µs.
+static int gather_split_shift(int B) { return B >= 48 ? kGatherSplitShift : 0; }
 
 template <typename T, int MODE>
 static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
@@ -1418,6 +1432,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tm_heads = a.tm_heads;
   g.tm_cap = a.tm_cap;
   g.tm_segcap = a.tm_segcap;
+  g.n_tiles = a.t.n_tiles;
   const dim3 grid(a.t.n_tiles > 0 ? (unsigned)a.t.n_tiles << g.split_shift : 1u);
   auto go = [&](auto kern) {
     if (a.probe_start && a.probe_stop) {
