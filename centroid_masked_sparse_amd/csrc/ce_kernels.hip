@@ -828,10 +828,13 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* vals, int n, uin
 // of a set is the smallest of its values with fewer than K values strictly
 // above it, so it can be found by counting in parallel, without a serial
 // chain of steps:
-//  1. Threshold: each wave finds the K-th largest mu_w of its 64 thread
-//     maxima (K <= 64) by such counts.  Those are K distinct keys >= mu_w,
-//     so the K-th largest key T of the row is >= mu = max_w mu_w, and the
-//     top K lies among the keys >= mu (about a hundred on random rows).
+//  1. Threshold: each wave finds the Kw-th largest mu_w of its 64 thread
+//     maxima, Kw = ceil(K / 4) <= 64, by such counts.  Each wave then holds
+//     at least Kw distinct keys >= mu_w, so the four hold at least K keys
+//     >= mu = min_w mu_w: the K-th largest key T of the row is >= mu, and
+//     the top K lies among the keys >= mu (about fifty on random rows at
+//     K = 32 of 2048; the K-th largest of each wave's maxima, maxed over
+//     the waves, left about 140).
 //  2. The keys >= mu are gathered into LDS and T is found among them: one
 //     candidate per thread counted against all (up to 256 candidates), else
 //     by a radix select in each wave.
@@ -840,7 +843,7 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* vals, int n, uin
 //     lowest ids first), and every thread's position in the ascending id
 //     list; the kept bits are assembled into the row's 64-centroid
 //     selection words.
-// Rows with more than kCandCap keys >= mu (K > 64 on large rows, or masses
+// Rows with more than kCandCap keys >= mu (K > 256 on large rows, or masses
 // of equal scores) fall back to a bit-serial select over all keys with one
 // barrier per bit.  K >= Nc keeps every centroid.
 template <int EPT, int MODE>
@@ -888,16 +891,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   wmax[tid] = m;
   __syncthreads();
   uint32_t mu = 0;
-  if (!take_all && K <= (uint32_t)kWave) {
-    // smallest wave maximum with fewer than K wave maxima above it (0, a
-    // valid bound, when the wave holds fewer than K keys)
+  const uint32_t Kw = (K + kTopkWaves - 1) / kTopkWaves;
+  if (!take_all && Kw <= (uint32_t)kWave) {
+    // smallest wave maximum with fewer than Kw wave maxima above it (0, a
+    // valid bound, when the wave holds fewer than Kw keys)
     const uint32_t above = count_above(wmax + wv * kWave, kWave, m);
-    mu = __ockl_wfred_min_u32(above < K ? m : 0xFFFFFFFFu);
+    mu = __ockl_wfred_min_u32(above < Kw ? m : 0xFFFFFFFFu);
   }
   if (lane == 0) wred[wv] = mu;
   __syncthreads();
+  mu = wred[0];
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) mu = max(mu, wred[i]);
+  for (int i = 1; i < kTopkWaves; ++i) mu = min(mu, wred[i]);
 
   uint32_t sel = valid, pos = 0, tot;
   bool placed = false;   // pos already known
