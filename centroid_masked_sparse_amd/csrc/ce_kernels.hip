@@ -1030,6 +1030,11 @@ struct GatherArgs {
   const int32_t* ttok;          // [n_tiles][64] token of each slot, -1 past the cluster's end
   int split_shift;              // 2^split_shift waves per tile share its passes
   int n_tiles;
+  // by row (equal clusters, small batches): one wave per (row, selected
+  // centroid, tile of that cluster), the centroid read from the row's top-K
+  const int32_t* topk;          // [B][ldK] ascending ids
+  int ldK, K;
+  int by_row;
   const float* escale;          // FP8 slabs: [n_tiles][64] row scales
   unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
                                 // top-m: [64] packed (segments << 32 | keys) per row
@@ -1085,17 +1090,30 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   // consecutive waves of one tile would leave every other XCD without work,
   // and the first slot's waves, the ones with work, are dispatched first.
   const int nsplit = 1 << a.split_shift;
-  const int slot = (int)blockIdx.x / a.n_tiles;
-  const int t = (int)blockIdx.x - slot * a.n_tiles;
-  const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
-  // lane b reads row b's selection word of c's 64-centroid block
-  const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
-  unsigned long long mask = __ballot((word >> (c % kWave)) & 1ull);
+  int t;
+  unsigned long long mask;
   auto skip_passes = [&](int n) {
     for (int i = 0; i < n * RB && mask; ++i) mask &= mask - 1ull;
   };
-  skip_passes(slot);
-  if (!mask) return;   // no row selected this tile's cluster, or no pass left for this wave
+  if (a.by_row) {
+    // a tile two rows selected is dotted by two waves (rare at small
+    // batches), but no wave is launched for a tile nobody selected
+    const int per_row = a.K * a.tpc;
+    const int b = (int)blockIdx.x / per_row;
+    const int rem = (int)blockIdx.x - b * per_row;
+    const int k = rem / a.tpc;
+    t = a.topk[(long)b * a.ldK + k] * a.tpc + (rem - k * a.tpc);
+    mask = 1ull << b;
+  } else {
+    const int slot = (int)blockIdx.x / a.n_tiles;
+    t = (int)blockIdx.x - slot * a.n_tiles;
+    const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
+    // lane b reads row b's selection word of c's 64-centroid block
+    const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
+    mask = __ballot((word >> (c % kWave)) & 1ull);
+    skip_passes(slot);
+    if (!mask) return;   // no row selected this tile's cluster, or no pass left for this wave
+  }
   // the token ids are needed only after the first batch is dotted: they
   // are waited for there, not before the tile loads go out
   int tok = a.ttok[(long)t * kWave + lane];
@@ -1416,6 +1434,13 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
 // the gather's tail and splitting them takes the call from 39.2 to 37.8 µs.
 static int gather_split_shift(int B) { return B >= 48 ? kGatherSplitShift : 0; }
 
+// Largest batch whose gather runs by row (equal clusters only): up to it
+// the B·K·tpc waves of the selected (row, centroid, tile) triples cost less
+// than the static grid of every tile, most of whose waves find no row
+// (sweep head, µs per call: B=1 17.3 → 15.5, B=2 19.4 → 18.0, B=4 20.1 →
+// 19.6; B=8 22.8 → 23.2 and B=16 24.2 → 25.8 the other way).
+constexpr int kGatherByRowMaxB = 4;
+
 template <typename T, int MODE>
 static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   GatherArgs g;
@@ -1438,7 +1463,12 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tm_cap = a.tm_cap;
   g.tm_segcap = a.tm_segcap;
   g.n_tiles = a.t.n_tiles;
-  const dim3 grid(a.t.n_tiles > 0 ? (unsigned)a.t.n_tiles << g.split_shift : 1u);
+  g.topk = a.topk;
+  g.ldK = a.ldK;
+  g.K = a.K;
+  g.by_row = a.t.tpc > 0 && a.B <= kGatherByRowMaxB && g.split_shift == 0;
+  const dim3 grid(g.by_row ? (unsigned)(a.B * a.K * a.t.tpc)
+                           : a.t.n_tiles > 0 ? (unsigned)a.t.n_tiles << g.split_shift : 1u);
   auto go = [&](auto kern) {
     if (a.probe_start && a.probe_stop) {
       hipExtLaunchKernelGGL(kern, grid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);
