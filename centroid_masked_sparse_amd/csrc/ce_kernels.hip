@@ -22,12 +22,15 @@
 //            the waves' maxima, then parallel rank counts among the keys
 //            above it); writes the ids and the row's 64-centroid selection
 //            words
-//   gather   one wave per 64-token tile of the static tile list; a tile whose
+//   gather   one wave per 64-token tile of the static tile list (two from
+//            48 rows, sharing the tile's passes of 4 rows); a tile whose
 //            centroid no row selected exits at once, so each selected slab is
 //            read exactly once however many rows share it (cross-row dedup).
 //            The tile is dotted with every row that selected it, then reduced
 //            to a per-row packed argmax (64-bit atomicMax) or stored at the
-//            candidates' token columns of the forward rows
+//            candidates' token columns of the forward rows.  Up to 4 rows
+//            with equal clusters, one wave per selected (row, centroid, tile)
+//            instead, so no wave is launched for an unselected tile
 //   finalize (get_top_tokens) decode the packed argmax into token ids
 //
 // No kernel waits on another workgroup and none uses a device-scope fence:
@@ -62,14 +65,13 @@ namespace ce {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kChunk = 64;       // hidden dims per LDS step
+constexpr int kChunk = 64;       // hidden dims per register stage
 constexpr int kGatherRows = 4;   // hidden rows dotted per pass over a gather tile
 constexpr int kGatherSplitShift = 1;   // log2 waves per gather tile for large batches
 
 // 16 bytes as a native vector (HIP's uint4 wraps a union, which keeps arrays
 // of it out of registers).
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef double v2d __attribute__((ext_vector_type(2)));
 
 // Weight element types: fp32, bf16 bits, and OCP E4M3 codes (FP8 slabs,
 // whose hidden rows stay bf16).
@@ -1075,11 +1077,13 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
 template <typename T>
 constexpr int kGatherStages = std::is_same<T, uint16_t>::value ? 4 : 2;
 
-// One wave per packed tile.  Once the rows that selected the tile's
-// cluster are known, the tile, the hidden rows and the slots' token ids are
-// all requested at once: they are addressed by the tile index alone.  With
-// equal tile counts per cluster the cluster follows from the tile index
-// too, so the selection words are the only load before the tile's.
+// One wave per packed tile (2^split_shift waves from 48 rows), or, by row,
+// one wave per selected (row, centroid, tile).  Once the rows that selected
+// the tile's cluster are known, the tile, the hidden rows and the slots'
+// token ids are all requested at once: they are addressed by the tile index
+// alone.  With equal tile counts per cluster the cluster follows from the
+// tile index too, so the selection words (by row: the row's top-K id) are
+// the only load before the tile's.
 template <typename T, int RB, int MODE, int NCH>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
