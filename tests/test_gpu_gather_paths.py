@@ -47,3 +47,26 @@ def test_by_row_and_tile_grid_agree_with_oracle(seed, d, V, Nc, K, B):
     tm_o, vm_o = oracle.top_m(hb, w.C, w.E, w.offsets, w.tos, K, 6, "bf16")
     assert tm.cpu().numpy().tolist() == tm_o.tolist()
     assert np.array_equal(vm.cpu().numpy().view(np.uint32), vm_o.view(np.uint32))
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 5])
+def test_by_row_and_tile_grid_fp8(B):
+    """The same two launch shapes on FP8 slabs (bf16 rows, E4M3 codes with
+    row scales): tokens and masked rows equal the FP8 oracle's."""
+    from centroid_masked_sparse_amd import Head
+    from oracle import fp8_slabs as f8
+    torch = torch_mod()
+    w = make_random(84, d=128, V=8192, Nc=64, dtype="bf16", rows=64, ragged=False)
+    hb = rows(w, B).copy()
+    if B >= 2:
+        hb[1] = hb[0]
+    head = Head(to_device(w.C, "bf16"), to_device(w.E, "bf16"), w.tos, max_B=8, max_K=8, slabs="fp8")
+    h = to_device(hb, "bf16")
+    tok = head.top_tokens(h, 4)
+    masked = head.masked_logits(h, 4)
+    torch.cuda.synchronize()
+    codes, sc = f8.quantize_rows(w.E)
+    tok_o, _ = f8.top_tokens_fp8(hb, w.C, codes, sc, w.offsets, w.tos, 4)
+    assert tok.cpu().numpy().tolist() == tok_o.tolist()
+    M = f8.masked_logits_fp8(hb, w.C, codes, sc, w.offsets, w.tos, 4)
+    assert np.array_equal(masked.cpu().numpy().view(np.uint32), M.view(np.uint32))
