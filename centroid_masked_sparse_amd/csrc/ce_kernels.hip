@@ -1394,8 +1394,14 @@ static void launch_scores_t(const PassArgs& a, hipStream_t s) {
 #undef CE_SCORES
 }
 
+// One row per wave: the projection at small batches is a lone wave's fp64
+// chain per SIMD, so halving each wave's rows halves the critical path
+// (sweep head, µs per call: B=2 17.9 → 16.5, B=16 24.1 → 22.8, B=64 37.1 →
+// 36.7).  Two rows per wave (the tile widened once for both) only for the
+// forward at 48 rows or more, where the grid also holds the fill waves
+// (B=64: 55.2 with one row against 54.4).
 hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
-  const bool two = a.B >= 2;
+  const bool two = a.fill != nullptr && a.B >= 48;
   if (a.dtype == 1) {
     if (two) launch_scores_t<uint16_t, 2>(a, s); else launch_scores_t<uint16_t, 1>(a, s);
   } else {
