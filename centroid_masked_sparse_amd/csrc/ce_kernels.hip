@@ -1073,12 +1073,11 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
   return n;
 }
 
-// Register stages of the gather's tile ring: bf16 keeps a whole 256-dim tile
-// (four 8 KiB chunks) in flight, so a wave waits on one round trip rather
-// than three; fp32 chunks are twice as large, and FP8 chunks measured no
-// better with four.
+// Register stages of the gather's tile ring: bf16 and FP8 keep four chunks
+// in flight (a whole 256-dim tile), so a wave waits on one round trip
+// rather than three; fp32 chunks are twice as large and keep two.
 template <typename T>
-constexpr int kGatherStages = std::is_same<T, uint16_t>::value ? 4 : 2;
+constexpr int kGatherStages = std::is_same<T, float>::value ? 2 : 4;
 
 // One wave per packed tile (2^split_shift waves from 48 rows), or, by row,
 // one wave per selected (row, centroid, tile).  Once the rows that selected
