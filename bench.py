@@ -46,7 +46,7 @@ METRIC = "sparse-head draft rows/sec at B=1..64 + achieved HBM GB/s vs peak (1 M
 # write x1.00); see profiles/gather_kernel_sweep_B64.md.  Valid only for the
 # kernel source it was measured on: any other source reports null.
 TRAFFIC_RECORD = {
-    "kernels_sha256_prefix": "e216d6b20eb35c87",
+    "kernels_sha256_prefix": "5b1feb49ef2114b5",
     "fetch_kib": 41514, "fetch_scale": 2.00, "write_kib": 128, "write_scale": 1.00,
 }
 
@@ -184,6 +184,33 @@ def _device_us_per_call(torch, heads, hs, K, B, steps, warmup, per_graph=8):
 EMB_DIM = 2560   # backbone width of the embedding table (assumed: the pages give none)
 
 
+def _stream_read_probe(torch, lib, stream, log, nbytes=2 << 30, calls=20):
+    """Streaming read rate of this GPU: `ce_probe_stream_read` over a 2 GiB
+    buffer (8 times the Infinity Cache), each launch bracketed by events on the
+    stream it runs on; GB/s over the mean launch time."""
+    from centroid_masked_sparse_amd import _ffi
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for _ in range(3):
+        _ffi.check(lib.ce_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream),
+                   "ce_probe_stream_read")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record()
+        _ffi.check(lib.ce_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream),
+                   "ce_probe_stream_read")
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    out = {"GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "us_per_launch": round(ms * 1e3, 2),
+           "frac_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"[bench] streaming read probe: {out}")
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def _draft_section(torch, heads, groups, K, args, stream, log):
     """The fused draft step (final RMSNorm, head, next step's scaled embedding:
     four launches) against the same step unfused (PyTorch RMSNorm in float32,
@@ -310,8 +337,9 @@ def _skewed_section(torch, args, stream, log):
     """The skewed head at B=64 (d=512, V=262144, Nc=2048 Zipf(1.1) clusters of
     10 .. 44,286 tokens, K=32, rows around 8 anchor directions): top_tokens
     through the C ABI, cold over two weight copies (512 MiB), with the
-    gather alone.  Stresses the dedup (overlapping row sets) and the load
-    balance (one cluster is 692 tiles)."""
+    gather alone.  Stresses the dedup (overlapping row sets: the line gives
+    their mean pairwise Jaccard) and the load balance (tiles that many rows
+    selected; the line gives the largest selected cluster, in tokens)."""
     from centroid_masked_sparse_amd import Head, OP_TOP_TOKENS, _ffi
     from workloads import make_workload
     w = make_workload(5)
@@ -324,8 +352,14 @@ def _skewed_section(torch, args, stream, log):
     topk = torch.empty((B, K), dtype=torch.int32, device="cuda:0")
     heads[0].top_tokens(H, K, topk_out=topk)
     torch.cuda.synchronize()
-    slab, clusters = _union_bytes(topk.cpu().numpy(), w.sizes, d, 2)
+    sel = topk.cpu().numpy()
+    slab, clusters = _union_bytes(sel, w.sizes, d, 2)
     unique = Nc * d * 2 + slab
+    # overlap of the rows' selections: mean pairwise Jaccard, and the largest
+    # cluster any row selected
+    sets = [set(r.tolist()) for r in sel]
+    jac = [len(sets[i] & sets[j]) / len(sets[i] | sets[j]) for i in range(B) for j in range(i + 1, B)]
+    largest = int(max(w.sizes[c] for c in set().union(*sets)))
     us = _eager_us_per_call(torch, heads, [H], K, B, args.steps, args.warmup, stream)
     n = max(20, args.probe_calls // 4)
     start_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -343,7 +377,8 @@ def _skewed_section(torch, args, stream, log):
     out = {"workload": f"skewed head d={d} V={w.V} Nc={Nc} Zipf(1.1) CSR, K={K} bf16, B={B}, "
                        f"correlated rows, cold (2 weight copies)",
            "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
-           "union_clusters": clusters, "unique_MiB": round(unique / 2**20, 2),
+           "union_clusters": clusters, "mean_jaccard": round(float(np.mean(jac)), 4),
+           "largest_cluster_in_union": largest, "unique_MiB": round(unique / 2**20, 2),
            "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
            "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
            "gather_us": round(g_ms * 1e3, 3), "gather_GB_s": round(slab / (g_ms * 1e-3) / 1e9, 1)}
@@ -479,6 +514,8 @@ def main() -> int:
     def groups(B):
         return [H[s * B:(s + 1) * B].contiguous() for s in range(64 // B)]
 
+    probe = _stream_read_probe(torch, heads[0]._lib, stream, log)
+
     # ------------------------------------------------------------ sweep (top_tokens)
     sweep = []
     head_row = None
@@ -517,6 +554,7 @@ def main() -> int:
             "unique_MiB": round(unique / 2**20, 2), "union_clusters": round(clusters, 1),
             "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
             "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "frac_probe": round(unique / (us * 1e-6) / 1e9 / probe["GB_s"], 4),
             "graph_us_per_call": round(graph_us, 3),
             "graph_warm_us_per_call": round(ms_warm * 1e3, 3),
             "device_us_per_call": round(dev_us, 3),
@@ -656,7 +694,8 @@ def main() -> int:
         cpu = {"value": round(calls * Bp / secs, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
                "sample": f"{calls} oracle top_tokens call(s) of the first {Bp} rows of the sweep "
                          f"workload, {secs:.1f} s single-threaded numpy (float64 canonical dots); "
-                         f"host has {len(os.sched_getaffinity(0))} usable cores"}
+                         f"host has {len(os.sched_getaffinity(0))} usable of {os.cpu_count()} cores; "
+                         f"numpy {np.__version__}"}
         log(f"[bench] cpu oracle: {cpu}")
 
     us = head_row["us_per_call"]
@@ -683,7 +722,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "gather_kernel<bf16,argmax>",
                      "achieved": round(gather_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gather_gbs / PEAK_HBM_GBS, 4), "traffic": _traffic_bytes(),
-                     "bytes_per_launch": int(head_slab), "us_per_launch": round(gather_ms * 1e3, 3)},
+                     "bytes_per_launch": int(head_slab), "us_per_launch": round(gather_ms * 1e3, 3),
+                     "probe_GB_s": probe["GB_s"], "frac_probe": round(gather_gbs / probe["GB_s"], 4)},
+        "stream_read_probe": probe,
         "cpu_baseline": cpu,
         "sweep": sweep,
         "masked": masked,

@@ -52,6 +52,7 @@ SIGNATURES = {
     "ce_graph_launch": (_i32, [_vp, _vp]),
     "ce_graph_destroy": (_i32, [_vp]),
     "ce_probe_gather_events": (_i32, [_vp, _vp]),
+    "ce_probe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "ce_status_string": (ctypes.c_char_p, [_i32]),
     "ce_last_error": (ctypes.c_char_p, []),
 }

@@ -569,6 +569,15 @@ ce_status ce_probe_gather_events(hipEvent_t start, hipEvent_t stop) {
   return CE_SUCCESS;
 }
 
+ce_status ce_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return fail(CE_ERR_NULL_POINTER, "buf or sink is NULL");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || (bytes & 15u) != 0)
+    return fail(CE_ERR_MISALIGNED, "buf and bytes must be multiples of 16");
+  const hipError_t e = ce::launch_stream_read(buf, bytes, sink, stream);
+  if (e != hipSuccess) return fail(CE_ERR_HIP, hipGetErrorString(e));
+  return CE_SUCCESS;
+}
+
 const char* ce_status_string(ce_status status) {
   switch (status) {
     case CE_SUCCESS: return "CE_SUCCESS";

@@ -92,5 +92,7 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: T
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
 hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
+// Read every 16-byte vector of buf[0, bytes) once (measurement probe).
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace ce

@@ -1530,6 +1530,38 @@ hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Streaming-read probe: every 16-byte vector of the buffer is loaded once,
+// four independent loads per thread per step, grid-stride; the XOR of the
+// loaded words feeds a store that never happens for real data (sink is
+// written only if it equals an improbable pattern), so no load is dropped.
+__global__ __launch_bounds__(256) void stream_read_kernel(const v4u* __restrict__ p, long n,
+                                                          uint32_t* __restrict__ sink) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const v4u a = p[i], b = p[i + stride], c = p[i + 2 * stride], e = p[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^
+           (e.x ^ e.y ^ e.z ^ e.w);
+  }
+  for (; i < n; i += stride) {
+    const v4u a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const long n = (long)(bytes / sizeof(v4u));
+  if (n == 0) return hipSuccess;
+  // 16 workgroups of 256 threads per CU on the 256-CU part; fewer when the
+  // buffer is small, so every thread has at least one vector
+  const long blocks = std::min<long>(4096, (n + 255) / 256);
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const v4u*>(buf), n, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {
   if (a.emb_table) {
     EmbedArgs e{a.emb_table, a.emb_dim, a.emb_normalizer, a.emb_out};

@@ -212,3 +212,11 @@ def test_fp8_slab_sizes(lib):
     # bytes of codes plus 5 * 256 bytes of scales (each region 256-aligned)
     assert native[0] - fp8[0] == 5 * 8192 - 5 * 4096 - 5 * 256
     assert native[1] == fp8[1]
+
+
+def test_stream_read_probe_rejects_bad_arguments(lib):
+    """The probe's argument checks come before any HIP call."""
+    assert lib.ce_probe_stream_read(None, 1024, FAKE, None) == ERR["CE_ERR_NULL_POINTER"]
+    assert lib.ce_probe_stream_read(FAKE, 1024, None, None) == ERR["CE_ERR_NULL_POINTER"]
+    assert lib.ce_probe_stream_read(FAKE + 4, 1024, FAKE, None) == ERR["CE_ERR_MISALIGNED"]
+    assert lib.ce_probe_stream_read(FAKE, 1000, FAKE, None) == ERR["CE_ERR_MISALIGNED"]

@@ -201,6 +201,21 @@ def test_graph_replay_matches_eager():
     g2.close()
 
 
+def test_stream_read_probe_runs():
+    """The streaming-read probe completes on buffers from one vector to a few
+    MiB with ragged remainders; all-zero data never matches its store pattern."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import _ffi
+    lib = _ffi.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    for n in (16, 4096 + 16, 1 << 20, (3 << 20) + 48):
+        buf = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+        sink = torch.full((1,), 7, dtype=torch.int32, device="cuda:0")
+        _ffi.check(lib.ce_probe_stream_read(buf.data_ptr(), n, sink.data_ptr(), stream), "probe")
+        torch.cuda.synchronize()
+        assert sink.item() == 7
+
+
 def test_probe_events_bracket_gather():
     torch = torch_mod()
     from centroid_masked_sparse_amd import _ffi
