@@ -342,7 +342,7 @@ def _skewed_section(torch, args, stream, log):
     selected; the line gives the largest selected cluster, in tokens)."""
     from centroid_masked_sparse_amd import Head, OP_TOP_TOKENS, _ffi
     from workloads import make_workload
-    w = make_workload(5)
+    w = make_workload("skewed")
     d, Nc, K, B = w.d, w.Nc, w.K, 64
     C0 = _to_device(w.C, w.dtype, torch)
     E0 = _to_device(w.E, w.dtype, torch)
@@ -397,7 +397,7 @@ def _wide_section(torch, args, stream, log):
     Cold over two weight copies."""
     from centroid_masked_sparse_amd import OP_TOP_TOKENS, Head
     from workloads import make_workload
-    w = make_workload(4)
+    w = make_workload("wide")
     d, V, Nc, K, B = w.d, w.V, w.Nc, w.K, 64
     sizes = w.sizes
     ncopy = 2
@@ -489,7 +489,7 @@ def main() -> int:
     from centroid_masked_sparse_amd import OP_MASKED_LOGITS, OP_TOP_TOKENS, Head, _ffi
     from workloads import CONFIGS, make_workload
 
-    w = make_workload(2)
+    w = make_workload("sweep")
     d, V, Nc, K = w.d, w.V, w.Nc, w.K
     elem = 2
     sizes = w.sizes
@@ -592,7 +592,7 @@ def main() -> int:
     # ------------------------------------------------------------ masked logits (forward)
     masked = []
     if not args.no_masked:
-        for B in [b for b in CONFIGS[3].batches if b in (1, 16, 64)]:
+        for B in [b for b in CONFIGS["masked"].batches if b in (1, 16, 64)]:
             hs = groups(B)
             topk = torch.empty((B, K), dtype=torch.int32, device=dev)
             ub = []

@@ -26,14 +26,14 @@ def _run_tokens(head, w, B, K):
 
 @pytest.fixture(scope="module")
 def sweep():
-    w = make_workload(2)
+    w = make_workload("sweep")
     tok_o, sel_o, _ = oracle.top_tokens(rows(w, 64), w.C, w.E, w.offsets, w.tos, w.K, w.dtype)
     return w, make_head(w), tok_o, sel_o
 
 
 def test_sweep_every_batch_size(sweep):
     w, head, tok_o, sel_o = sweep
-    for B in CONFIGS[2].batches:
+    for B in CONFIGS["sweep"].batches:
         tok, tk = _run_tokens(head, w, B, w.K)
         assert tk.tolist() == sel_o[:B].tolist(), B
         assert tok.tolist() == tok_o[:B].tolist(), B
@@ -58,7 +58,7 @@ def test_sweep_graph_replay(sweep):
 def test_masked_config_full_rows(sweep):
     w, head, _, sel_o = sweep
     M_o, _ = oracle.masked_logits(rows(w, 64), w.C, w.E, w.offsets, w.tos, w.K, w.dtype)
-    for B in CONFIGS[3].batches:
+    for B in CONFIGS["masked"].batches:
         M = head.masked_logits(to_device(rows(w, B), w.dtype), w.K).cpu().numpy()
         assert np.array_equal(M.view(np.uint32), M_o[:B].view(np.uint32)), B
         assert np.all(np.isfinite(M).sum(axis=1) == w.K * (w.V // w.Nc))
@@ -69,7 +69,7 @@ WIDE_SAMPLE = [0, 17, 42, 63]
 
 @pytest.fixture(scope="module")
 def wide():
-    w = make_workload(4)
+    w = make_workload("wide")
     D = oracle.dense_logits(rows(w, 64)[WIDE_SAMPLE], w.E, w.tos, w.dtype)
     return w, D
 
@@ -119,7 +119,7 @@ def test_wide_dense_comparison_path(wide):
 
 
 def test_skewed_config():
-    w = make_workload(5)
+    w = make_workload("skewed")
     head = make_head(w)
     tok_o, sel_o, _ = oracle.top_tokens(rows(w, 64), w.C, w.E, w.offsets, w.tos, w.K, w.dtype)
     tok, tk = _run_tokens(head, w, 64, w.K)

@@ -59,7 +59,7 @@ def _check(head, w, x, nw, table, eps, normalizer, K):
 
 @pytest.mark.parametrize("K,B", [(4, 3), (64, 4)])
 def test_tiny_config_f32(K, B):
-    w = make_workload(1)
+    w = make_workload("tiny")
     x, nw, table = _inputs(1, B, w.d, w.V, 12, "f32")
     _check(make_head(w, max_B=4), w, x, nw, table, 1e-6, 2.5, K)
 
@@ -80,7 +80,7 @@ def test_random_shapes(seed, d, V, Nc, K, B, emb_dim, ragged):
 def test_sweep_config_full_size():
     """The sweep head (d=256, V=262144, Nc=2048, K=32, bf16) at B=64 as the
     bench runs it: every normalised row and token against the oracle."""
-    w = make_workload(2)
+    w = make_workload("sweep")
     x, nw, table = _inputs(60, 64, w.d, w.V, 128, "bf16")
     _check(make_head(w, max_B=64), w, x, nw, table, 1e-6, float(np.sqrt(2560.0)), w.K)
 
@@ -126,7 +126,7 @@ def test_draft_step_errors():
     import ctypes
     from centroid_masked_sparse_amd import _ffi
     torch = torch_mod()
-    w = make_workload(1)
+    w = make_workload("tiny")
     head = make_head(w, max_B=4)
     x, nw, table = _inputs(3, 2, w.d, w.V, 12, "f32")
     xd, nwd = to_device(x, "f32"), to_device(nw, "f32")

@@ -86,7 +86,7 @@ def test_sweep_config_full_size():
     selected clusters own (the selection does not depend on the slabs).
     Also reports how often the FP8 argmax equals the bf16 one."""
     torch = torch_mod()
-    w = make_workload(2)
+    w = make_workload("sweep")
     B, K = 64, w.K
     head = _head(w, max_B=B, max_K=K)
     hb = rows(w, B)

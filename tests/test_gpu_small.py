@@ -37,7 +37,7 @@ def _topk_ids(head, w, hB, K):
 
 
 def test_tiny_config_scores_topk_tokens_masked():
-    w = make_workload(1)
+    w = make_workload("tiny")
     head = make_head(w)
     hB = rows(w, 1)
     for K in (4, 64):
@@ -140,7 +140,7 @@ def test_empty_clusters_give_minus_one():
 
 def test_zero_batch_writes_nothing():
     torch = torch_mod()
-    w = make_workload(1)
+    w = make_workload("tiny")
     head = make_head(w)
     out = torch.full((4,), 12345, dtype=torch.int32, device="cuda:0")
     h0 = to_device(rows(w, 1), w.dtype)[:0]
@@ -152,7 +152,7 @@ def test_zero_batch_writes_nothing():
 def test_errors_from_device_calls():
     from centroid_masked_sparse_amd import CeError, _ffi
     torch = torch_mod()
-    w = make_workload(1)
+    w = make_workload("tiny")
     head = make_head(w, max_B=4, max_K=8)
     h = to_device(rows(w, 5), w.dtype)
     with pytest.raises(CeError) as e:
@@ -219,7 +219,7 @@ def test_stream_read_probe_runs():
 def test_probe_events_bracket_gather():
     torch = torch_mod()
     from centroid_masked_sparse_amd import _ffi
-    w = make_workload(1)
+    w = make_workload("tiny")
     head = make_head(w)
     h = to_device(rows(w, 1), w.dtype)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -28,7 +28,7 @@ def _check(head, w, B, K, m):
 
 @pytest.mark.parametrize("K,m", [(4, 1), (4, 5), (4, 32), (64, 32), (1, 32)])
 def test_tiny_config(K, m):
-    w = make_workload(1)
+    w = make_workload("tiny")
     _check(make_head(w, max_B=4), w, 3, K, m)
 
 
@@ -67,14 +67,14 @@ def test_empty_clusters_pad():
 
 
 def test_sweep_config_top8():
-    w = make_workload(2)
+    w = make_workload("sweep")
     _check(make_head(w), w, 64, w.K, 8)
 
 
 def test_bad_m_rejected():
     torch = torch_mod()
     from centroid_masked_sparse_amd import CeError
-    w = make_workload(1)
+    w = make_workload("tiny")
     head = make_head(w, max_B=2)
     h = to_device(rows(w, 1), w.dtype)
     for m in (0, 33):

@@ -132,7 +132,7 @@ def test_canonical_dot_against_exact_rationals(dtype):
 
 
 def test_tiny_config_dense_sample_against_exact_rationals():
-    w = make_workload(1)
+    w = make_workload("tiny")
     D = oracle.dense_logits(w.h[:2], w.E, w.tos, "f32")
     rng = np.random.default_rng(5)
     tok_of_slot = w.tos.astype(np.int64)
@@ -236,7 +236,7 @@ def _selected_tokens(sel, offsets, tos):
 @pytest.mark.parametrize("case", ["tiny4", "tiny64", "ragged"])
 def test_masked_equals_dense_on_candidates(case):
     if case.startswith("tiny"):
-        w = make_workload(1)
+        w = make_workload("tiny")
         K = int(case[4:])
         h = w.h[:3]
     else:
@@ -255,7 +255,7 @@ def test_masked_equals_dense_on_candidates(case):
 
 
 def test_full_K_gives_dense_argmax():
-    for w, h in ((make_workload(1), make_workload(1).h[:4]),
+    for w, h in ((make_workload("tiny"), make_workload("tiny").h[:4]),
                  (make_random(7, d=64, V=600, Nc=30, dtype="bf16", rows=4, ragged=True), None)):
         h = w.h[:4] if h is None else h
         tok, sel, _ = oracle.top_tokens(h, w.C, w.E, w.offsets, w.tos, w.Nc, w.dtype)

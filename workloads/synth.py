@@ -3,14 +3,14 @@
 The real assistant checkpoints (trained centroids, token ordering, embedding
 table) are not available, so every workload here is drawn from a seeded
 ``numpy.random.default_rng`` (PCG64) stream with the shapes, dtypes and value
-scales of the five benchmark configurations:
+scales of the five benchmark workloads, named:
 
-1. ``tiny``    d=64,   V=4096,   Nc=64,   K=4 (also K=64), all fp32, h,C,E ~ N(0,1/d)
-2. ``sweep``   d=256,  V=262144, Nc=2048, K=32, bf16, h ~ N(0,1), C,E ~ N(0,1/d)
-3. ``masked``  the arrays of ``sweep`` (same seed), run at B in {1,16,64}
-4. ``wide``    d=1024, V=262144, Nc=4096, K=64 (also K=4096), bf16, as ``sweep``
-5. ``skewed``  d=512,  V=262144, Nc=2048, K=32, bf16, Zipf(1.1) cluster sizes,
-               rows drawn around 8 anchor centroid directions
+* ``tiny``    d=64,   V=4096,   Nc=64,   K=4 (also K=64), all fp32, h,C,E ~ N(0,1/d)
+* ``sweep``   d=256,  V=262144, Nc=2048, K=32, bf16, h ~ N(0,1), C,E ~ N(0,1/d)
+* ``masked``  the arrays of ``sweep`` (same seed), run at B in {1,16,64}
+* ``wide``    d=1024, V=262144, Nc=4096, K=64 (also K=4096), bf16, as ``sweep``
+* ``skewed``  d=512,  V=262144, Nc=2048, K=32, bf16, Zipf(1.1) cluster sizes,
+              rows drawn around 8 anchor centroid directions
 
 Recipe (fixed, so that any implementation can regenerate the bytes):
 
@@ -41,7 +41,6 @@ _CHUNK_ELEMS = 1 << 24
 
 @dataclass(frozen=True)
 class ConfigSpec:
-    key: int
     name: str
     seed: int
     d: int
@@ -58,15 +57,15 @@ class ConfigSpec:
 
 
 CONFIGS = {
-    1: ConfigSpec(1, "tiny", 1, 64, 4096, 64, 4, "f32", "inv_d", (1,), (64,)),
-    2: ConfigSpec(2, "sweep", 2, 256, 262144, 2048, 32, "bf16", "unit",
-                  (1, 2, 4, 8, 16, 32, 64)),
-    3: ConfigSpec(3, "masked", 2, 256, 262144, 2048, 32, "bf16", "unit",
-                  (1, 16, 64)),
-    4: ConfigSpec(4, "wide", 4, 1024, 262144, 4096, 64, "bf16", "unit",
-                  (64,), (4096,)),
-    5: ConfigSpec(5, "skewed", 5, 512, 262144, 2048, 32, "bf16", "anchored",
-                  (64,), (), zipf_s=1.1, anchors=8, noise_var=0.1),
+    "tiny": ConfigSpec("tiny", 1, 64, 4096, 64, 4, "f32", "inv_d", (1,), (64,)),
+    "sweep": ConfigSpec("sweep", 2, 256, 262144, 2048, 32, "bf16", "unit",
+                        (1, 2, 4, 8, 16, 32, 64)),
+    "masked": ConfigSpec("masked", 2, 256, 262144, 2048, 32, "bf16", "unit",
+                         (1, 16, 64)),
+    "wide": ConfigSpec("wide", 4, 1024, 262144, 4096, 64, "bf16", "unit",
+                       (64,), (4096,)),
+    "skewed": ConfigSpec("skewed", 5, 512, 262144, 2048, 32, "bf16", "anchored",
+                         (64,), (), zipf_s=1.1, anchors=8, noise_var=0.1),
 }
 
 
@@ -171,11 +170,12 @@ def _offsets_from_sizes(sizes: np.ndarray) -> np.ndarray:
 
 
 @lru_cache(maxsize=4)
-def make_workload(key: int) -> Workload:
-    """Draw configuration ``key`` (1..5); configs 2 and 3 share arrays."""
-    spec = CONFIGS[key]
-    if key == 3:
-        w = make_workload(2)
+def make_workload(name: str) -> Workload:
+    """Draw the workload called ``name`` (a key of CONFIGS); ``masked`` shares
+    the arrays of ``sweep``."""
+    spec = CONFIGS[name]
+    if name == "masked":
+        w = make_workload("sweep")
         return Workload(spec.name, w.seed, w.d, w.V, w.Nc, spec.K, w.dtype, w.h, w.C,
                         w.E, w.offsets, w.tos)
     rng = np.random.default_rng(spec.seed)
