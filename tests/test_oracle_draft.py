@@ -208,3 +208,38 @@ def test_draft_step_uses_normalised_rows():
     tok2, sel2, _ = top_tokens(h, C, E, offsets, tos, 3, "bf16")
     assert np.array_equal(tok, tok2) and np.array_equal(sel, sel2)
     assert np.array_equal(emb, ds.embed_rows(table, tok, 2.0, "bf16"))
+
+
+def test_draft_step_hand_derived_end_to_end():
+    """A whole draft step whose every output follows by hand.
+
+    A constant row of 2.0 has mean square 4, so with a negligible eps its
+    RMSNorm is exactly the weight w.  One-hot centroids make the scores the
+    first coordinates of w, so the top-2 set is {2, 4}.  Every candidate
+    embedding is zero except coordinate 2, where w is 1.0, so a logit is that
+    coordinate's value.  Slots 9 (cluster 2) and 17 (cluster 4) tie at the
+    maximum 0.9375; token_of_slot maps slot 17 to the lower token id, so it
+    wins.  The normalizer 4 is a power of two, so the embedding row is the
+    table row with every exponent raised by 2.
+    """
+    d, Nc, vpc, K = 64, 8, 4, 2
+    V = Nc * vpc
+    x = to_bf16_bits(np.full((1, d), 2.0))
+    wv = np.zeros(d)
+    wv[:8] = [0.5, 0.25, 1.0, 0.125, 0.75, 0.0, -1.0, 0.375]
+    w = to_bf16_bits(wv)
+    C = to_bf16_bits(np.eye(Nc, d))
+    Ev = np.zeros((V, d))
+    Ev[8:12, 2] = [0.5, 0.9375, 0.25, 0.125]       # cluster 2
+    Ev[16:20, 2] = [0.375, 0.9375, 0.0, 0.5]       # cluster 4
+    Ev[0:8, 5] = 7.0                                # clusters 0 and 1: not selected
+    E = to_bf16_bits(Ev)
+    offsets = np.arange(Nc + 1) * vpc
+    tos = np.arange(V)[::-1].copy()                 # slot s holds token V-1-s
+    table = to_bf16_bits(np.arange(V * 16).reshape(V, 16) / 64.0 + 1.0)
+    h, tok, emb, sel = ds.draft_step(x, w, 1e-30, C, E, offsets, tos, K, table, 4.0, "bf16")
+    assert np.array_equal(h[0], w)
+    assert sel.tolist() == [[2, 4]]
+    assert tok.tolist() == [V - 1 - 17]             # token 14 beats token 22 (slot 9)
+    want = to_bf16_bits((np.arange(16) + (V - 1 - 17) * 16) / 64.0 * 4.0 + 4.0)
+    assert np.array_equal(emb[0], want)
