@@ -1,7 +1,8 @@
 """GPU parity at the size limits of the boundary: the largest hidden size
 (d = 8192, where every kernel takes its generic chunk loop and the fp32
 draft step stages 64 KiB of normalised rows in LDS), the largest centroid
-count (Nc = 8192) with K = Nc, and batches of several 64-row passes."""
+count (Nc = 8192) with K = Nc, batches of several 64-row passes, and a
+vocabulary of 2^23 tokens."""
 
 import numpy as np
 import pytest
@@ -108,3 +109,40 @@ def test_three_passes_of_rows():
     got = tok.cpu().numpy()
     assert got[:64].tolist() == tok_o.tolist()
     assert got[64:128].tolist() == tok_o.tolist() and got[128:].tolist() == tok_o[:22].tolist()
+
+
+@pytest.mark.parametrize("B", [2, 6])
+def test_largest_vocabulary(B):
+    """A vocabulary of 2^23 tokens (d = 64, Nc = 8192 clusters of 1024, 16
+    tiles each, 131072 tiles in all): token ids, tile indices and the
+    forward's row offsets all pass 2^22.  B = 2 runs the by-row gather, B = 6
+    the tile grid.  The bf16 values are drawn directly as bit patterns (one
+    seeded integer draw: random sign and mantissa, exponents 2^-7 .. 2^0),
+    which keeps the 8M x 64 draw to seconds."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import Head
+    d, V, Nc, K = 64, 1 << 23, 8192, 4
+    rng = np.random.default_rng(77)
+
+    def bf16_bits(n):
+        r = np.frombuffer(rng.bytes(2 * n), dtype=np.uint16)
+        exp = (np.uint16(120) + ((r >> np.uint16(7)) & np.uint16(7))) << np.uint16(7)
+        return (r & np.uint16(0x807F)) | exp
+
+    E = bf16_bits(V * d).reshape(V, d)
+    C = bf16_bits(Nc * d).reshape(Nc, d)
+    h = bf16_bits(B * d).reshape(B, d)
+    tos = rng.permutation(V).astype(np.int32)
+    offsets = (np.arange(Nc + 1) * (V // Nc)).astype(np.int32)
+    head = Head(to_device(C, "bf16"), to_device(E, "bf16"), tos, max_B=B, max_K=K)
+    hd = to_device(h, "bf16")
+    tk = torch.full((B, K), -7, dtype=torch.int32, device="cuda:0")
+    tok = head.top_tokens(hd, K, topk_out=tk)
+    masked = head.masked_logits(hd, K)
+    torch.cuda.synchronize()
+    tok_o, sel_o, _ = oracle.top_tokens(h, C, E, offsets, tos, K, "bf16")
+    assert tk.cpu().numpy().tolist() == sel_o.tolist()
+    assert tok.cpu().numpy().tolist() == tok_o.tolist()
+    M, _ = oracle.masked_logits(h, C, E, offsets, tos, K, "bf16")
+    assert np.array_equal(masked.cpu().numpy().view(np.uint32), M.view(np.uint32))
+    head.close()
