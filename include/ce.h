@@ -19,7 +19,9 @@
  *   - Top-K ties go to the lowest centroid id; argmax ties to the lowest token
  *     id.  Top-K ids are returned as an ascending set.
  *   - The fill value of the full-vocabulary row is -inf (fp32 0xFF800000).
- *   - NaN inputs are not supported.
+ *   - Inputs must be finite: with a NaN or an infinity in h, the centroids
+ *     or the embeddings (an infinity can make a NaN product), scores, ids
+ *     and tokens are unspecified.  No call checks for this or fails on it.
  *
  * Layout: the embedding table is in the ordered layout: row j holds the
  * embedding of token token_of_slot[j], and cluster c owns the contiguous slots
