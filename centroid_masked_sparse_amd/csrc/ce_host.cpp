@@ -64,7 +64,8 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
-  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, tm_keys = 0, tm_heads = 0, total = 0;
+  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, tm_keys = 0, tm_heads = 0, tm_rank = 0, total = 0;
+  bool has_rank = false;
   int tm_segcap = 0;
 };
 
@@ -89,6 +90,10 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
     L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);
     L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kMaxTopM * sizeof(unsigned long long));
     L.tm_heads = take(nb * (size_t)L.tm_segcap * sizeof(unsigned long long));
+    if (h->tpc > 0) {   // equal clusters: fixed segment places
+      L.tm_rank = take(nb * (size_t)h->Nc * sizeof(int16_t));
+      L.has_rank = true;
+    }
   }
   L.total = off;
   return L;
@@ -153,6 +158,8 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.tm_keys = reinterpret_cast<unsigned long long*>(ws + L.tm_keys);
   a.tm_heads = reinterpret_cast<unsigned long long*>(ws + L.tm_heads);
   a.tm_segcap = L.tm_segcap;
+  a.tm_rank = L.has_rank ? reinterpret_cast<int16_t*>(ws + L.tm_rank) : nullptr;
+  a.ldR = a.Nc;
 }
 
 // The draft step's extra operands (ce_draft_step).

@@ -59,6 +59,8 @@ struct PassArgs {
   unsigned long long* tm_keys;   // [B][tm_cap]
   unsigned long long* tm_heads;  // [B][tm_segcap]
   int tm_cap, tm_segcap;
+  int16_t* tm_rank;       // equal clusters: [B][ldR] output position of each selected
+  int ldR;                // centroid (top-K writes it, the gather's fixed segments read it)
   int32_t* tm_tokens;     // [B][m]
   float* tm_logits;       // [B][m]
   // fused draft step: h holds the rows before the final RMSNorm when norm_w

@@ -805,6 +805,8 @@ struct TopkArgs {
   int ldK;
   unsigned long long* cl_sel;      // [ceil(Nc/64)][64]: bit i of word (w, b) = row b selected 64w+i
   unsigned long long* best;        // [64] argmax slots, cleared per row (or null)
+  int16_t* rank;                   // [rows][ldR] output position of each selected id (or null)
+  int ldR;
 };
 
 // Number of the values vals[0..n) (LDS, read as broadcasts; n a multiple
@@ -1012,7 +1014,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   int32_t* out = a.out + (long)b * a.ldK;
 #pragma unroll
   for (int i = 0; i < EPT; ++i)
-    if (sel & (1u << i)) out[pos++] = first + i;
+    if (sel & (1u << i)) {
+      if (a.rank) a.rank[(long)b * a.ldR + first + i] = (int16_t)pos;
+      out[pos++] = first + i;
+    }
 
   if (MODE >= kSelMark) {
     if (sel) atomicOr(&words[first / kWave], (unsigned long long)sel << (first % kWave));
@@ -1049,6 +1054,11 @@ struct GatherArgs {
   unsigned long long* tm_keys;  // top-m: [B][tm_cap] tile segments of keys
   unsigned long long* tm_heads; // top-m: [B][tm_segcap] each segment's first key
   int tm_cap, tm_segcap;
+  // top-m with equal clusters: each (row, tile) segment has a fixed place,
+  // (rank of the cluster in the row's selection) * tpc + tile in cluster,
+  // so no counter is claimed; null otherwise
+  const int16_t* tm_rank;       // [B][ldR]
+  int ldR;
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -1097,6 +1107,8 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   // and the first slot's waves, the ones with work, are dispatched first.
   const int nsplit = 1 << a.split_shift;
   int t;
+  int cl = 0;          // the tile's cluster (tile grid)
+  int fixed_seg = 0;   // by row: the wave's fixed top-m segment
   unsigned long long mask;
   auto skip_passes = [&](int n) {
     for (int i = 0; i < n * RB && mask; ++i) mask &= mask - 1ull;
@@ -1109,11 +1121,13 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     const int rem = (int)blockIdx.x - b * per_row;
     const int k = rem / a.tpc;
     t = a.topk[(long)b * a.ldK + k] * a.tpc + (rem - k * a.tpc);
+    fixed_seg = rem;
     mask = 1ull << b;
   } else {
     const int slot = (int)blockIdx.x / a.n_tiles;
     t = (int)blockIdx.x - slot * a.n_tiles;
     const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
+    cl = c;
     // lane b reads row b's selection word of c's 64-centroid block
     const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
     mask = __ballot((word >> (c % kWave)) & 1ull);
@@ -1134,6 +1148,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   // max-ed into the row's slot; forward: each candidate logit stored at its
   // token's column; top-m: the tile's m largest packed keys for the row, in
   // descending order, appended as one segment of the row's list
+  int rk[RB];   // top-m on the tile grid: each pass row's rank of the cluster
   auto finish = [&](const int (&rows)[RB], int nrows, const double (&acc)[RB]) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -1152,10 +1167,18 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
           if (tok >= 0)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           const int mm = min(a.m, (int)__builtin_popcountll(__ballot(tok >= 0)));
-          unsigned long long at = 0ull;
-          if (lane == 0) at = atomicAdd(&a.best[rows[r]], (1ull << 32) | (unsigned long long)mm);
-          const uint32_t seg = __builtin_amdgcn_readfirstlane((uint32_t)(at >> 32));
-          const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)at);
+          uint32_t seg, base;
+          if (a.tm_rank) {
+            // fixed place; a short tile's missing keys are zeros (no key is 0)
+            seg = (uint32_t)(a.by_row ? fixed_seg : rk[r] * a.tpc + (t - cl * a.tpc));
+            base = seg * (uint32_t)a.m;
+            if (lane < a.m - mm) a.tm_keys[(long)rows[r] * a.tm_cap + base + mm + lane] = 0ull;
+          } else {
+            unsigned long long at = 0ull;
+            if (lane == 0) at = atomicAdd(&a.best[rows[r]], (1ull << 32) | (unsigned long long)mm);
+            seg = __builtin_amdgcn_readfirstlane((uint32_t)(at >> 32));
+            base = __builtin_amdgcn_readfirstlane((uint32_t)at);
+          }
           unsigned long long* keys = a.tm_keys + (long)rows[r] * a.tm_cap + base;
           for (int i = 0; i < mm; ++i) {
             const unsigned long long mx = wave_max_u64(k);
@@ -1178,6 +1201,15 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     const v4u* wtb = wt + zero;
     int rows[RB];
     const int nrows = take_rows<RB>(mask, rows, 0);
+    if constexpr (MODE == kTopM) {
+      // issued before the tile loads, so waiting for the first stage covers
+      // them; unconditional (unused slots repeat a selecting row, and
+      // without a table the load reads the row's own counter)
+      const int16_t* rp = a.tm_rank ? a.tm_rank : reinterpret_cast<const int16_t*>(a.best);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        rk[r] = rp[a.tm_rank && !a.by_row ? (long)rows[r] * a.ldR + cl : 0];
+    }
     double acc[RB];
     dot_tile<T, RB, NCH, kGatherStages<T>>(wtb, a.d, h, rows, nrows, acc);
     pin(tok);   // keep the loads out of the branches below
@@ -1250,6 +1282,7 @@ struct TopmArgs {
   const unsigned long long* keys;   // [B][cap]
   const unsigned long long* heads;  // [B][segcap]
   int cap, segcap, m;
+  int fixed_segs;                   // > 0: every row has this many segments of m keys (zeros pad)
   int32_t* tokens;                  // [B][m]
   float* logits;                    // [B][m]
 };
@@ -1275,9 +1308,9 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int m = a.m;
-  const unsigned long long c = a.cnt[b];
-  const int segs = (int)(c >> 32);
-  const int n = (int)(uint32_t)c;
+  const unsigned long long c = a.fixed_segs > 0 ? 0ull : a.cnt[b];
+  const int segs = a.fixed_segs > 0 ? a.fixed_segs : (int)(c >> 32);
+  const int n = a.fixed_segs > 0 ? a.fixed_segs * m : (int)(uint32_t)c;
   unsigned long long* heads = tm_lds;
   unsigned long long* cand = tm_lds + a.segcap;
   const unsigned long long* hsrc = a.heads + (long)b * a.segcap;
@@ -1304,7 +1337,7 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
   }
   for (int i = tid; i < n; i += kTopkThreads) {
     const unsigned long long k = ksrc[i];
-    if (k >= mu) {
+    if (k >= mu && k != 0ull) {
       const uint32_t at = atomicAdd(&ncand, 1u);
       if (at < (uint32_t)kTopMCand) cand[at] = k;
     }
@@ -1322,7 +1355,7 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
       val[above] = key_value((uint32_t)(x >> 32));
     }
   }
-  for (int p = min(n, m) + tid; p < m; p += kTopkThreads) {
+  for (int p = min(nc, m) + tid; p < m; p += kTopkThreads) {
     tok[p] = -1;
     val[p] = -__builtin_inff();
   }
@@ -1430,6 +1463,8 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.ldK = a.ldK;
   t.cl_sel = a.cl_sel;
   t.best = a.best;
+  t.rank = a.tm_rank;
+  t.ldR = a.ldR;
   const int ept = (a.Nc + kTopkThreads - 1) / kTopkThreads;
   if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, s);
   else if (ept <= 2) launch_topk_ept<2>(t, a.B, mode, s);
@@ -1474,6 +1509,8 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tm_heads = a.tm_heads;
   g.tm_cap = a.tm_cap;
   g.tm_segcap = a.tm_segcap;
+  g.tm_rank = MODE == kTopM ? a.tm_rank : nullptr;
+  g.ldR = a.ldR;
   g.n_tiles = a.t.n_tiles;
   g.topk = a.topk;
   g.ldK = a.ldK;
@@ -1523,6 +1560,7 @@ hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s) {
   t.cap = a.tm_cap;
   t.segcap = a.tm_segcap;
   t.m = a.m;
+  t.fixed_segs = a.tm_rank ? a.K * a.t.tpc : 0;
   t.tokens = a.tm_tokens;
   t.logits = a.tm_logits;
   const size_t lds = ((size_t)a.tm_segcap + kTopMCand) * sizeof(unsigned long long);
