@@ -88,7 +88,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
   if (op == CE_OP_TOP_M) {
     L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);
-    L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kMaxTopM * sizeof(unsigned long long));
+    L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kTileTokens * sizeof(unsigned long long));
     L.tm_heads = take(nb * (size_t)L.tm_segcap * sizeof(unsigned long long));
     if (h->tpc > 0) {   // equal clusters: fixed segment places
       L.tm_rank = take(nb * (size_t)h->Nc * sizeof(int16_t));
@@ -211,7 +211,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
     return fail(CE_ERR_NULL_POINTER, "output pointer is NULL");
   if (op == CE_OP_TOP_M) {
     if (m < 1 || m > ce::kMaxTopM) return fail(CE_ERR_BAD_SHAPE, "m must lie in [1, CE_MAX_TOP_M]");
-    if (h->tiles_top[K] > ce::kTopMMaxSegs)
+    if (h->tiles_top[K] + (long long)m * ce::kTileTokens > ce::kTopMLdsWords)
       return fail(CE_ERR_UNSUPPORTED, "the K largest clusters hold too many tiles for the top-m merge");
   }
   if (B == 0) return CE_SUCCESS;
@@ -243,7 +243,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.tokens = static_cast<int32_t*>(out) + b0;
     } else if (op == CE_OP_TOP_M) {
       a.m = m;
-      a.tm_cap = L.tm_segcap * m;
+      a.tm_cap = L.tm_segcap * ce::kTileTokens;
       a.tm_tokens = static_cast<int32_t*>(out) + (size_t)b0 * m;
       a.tm_logits = out2 + (size_t)b0 * m;
     } else {

@@ -31,8 +31,9 @@ struct Tables {
 
 enum GatherMode { kArgmax = 0, kMasked = 1, kTopM = 2 };
 constexpr int kMaxTopM = 32;        // m of the fused top-m
-constexpr int kTopMCand = kMaxTopM * kMaxTopM;   // merge candidates per row (at most m*m)
-constexpr int kTopMMaxSegs = 6144;  // per-row tile segments the merge keeps in LDS
+// 64-bit LDS words of the top-m merge (under 64 KiB with its static part):
+// the row's segment heads, then up to m * 64 candidate keys
+constexpr int kTopMLdsWords = (65536 - 256) / 8;
 // What the top-K kernel writes besides the ids: nothing, or the rows'
 // selection words (and, given `best`, cleared argmax slots).
 enum TopkMode { kTopkOnly = 1, kTopkMark = 2 };

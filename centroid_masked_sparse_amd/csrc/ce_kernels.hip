@@ -1146,8 +1146,8 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 
   // argmax: wave maximum of the packed (ordered logit, ~token) per row,
   // max-ed into the row's slot; forward: each candidate logit stored at its
-  // token's column; top-m: the tile's m largest packed keys for the row, in
-  // descending order, appended as one segment of the row's list
+  // token's column; top-m: the tile's 64 packed keys for the row stored as
+  // one segment of the row's list, with the segment's maximum as its head
   int rk[RB];   // top-m on the tile grid: each pass row's rank of the cluster
   auto finish = [&](const int (&rows)[RB], int nrows, const double (&acc)[RB]) {
 #pragma unroll
@@ -1166,28 +1166,21 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
           unsigned long long k = 0ull;
           if (tok >= 0)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
-          const int mm = min(a.m, (int)__builtin_popcountll(__ballot(tok >= 0)));
+          // the segment is the tile's 64 keys as they are (zero where the
+          // slot holds no token; no key is 0) and its head the largest
           uint32_t seg, base;
           if (a.tm_rank) {
-            // fixed place; a short tile's missing keys are zeros (no key is 0)
             seg = (uint32_t)(a.by_row ? fixed_seg : rk[r] * a.tpc + (t - cl * a.tpc));
-            base = seg * (uint32_t)a.m;
-            if (lane < a.m - mm) a.tm_keys[(long)rows[r] * a.tm_cap + base + mm + lane] = 0ull;
+            base = seg * (uint32_t)kTileTokens;
           } else {
             unsigned long long at = 0ull;
-            if (lane == 0) at = atomicAdd(&a.best[rows[r]], (1ull << 32) | (unsigned long long)mm);
+            if (lane == 0) at = atomicAdd(&a.best[rows[r]], (1ull << 32) | (unsigned long long)kTileTokens);
             seg = __builtin_amdgcn_readfirstlane((uint32_t)(at >> 32));
             base = __builtin_amdgcn_readfirstlane((uint32_t)at);
           }
-          unsigned long long* keys = a.tm_keys + (long)rows[r] * a.tm_cap + base;
-          for (int i = 0; i < mm; ++i) {
-            const unsigned long long mx = wave_max_u64(k);
-            if (k == mx) k = 0ull;   // keys are unique (they hold the token)
-            if (lane == 0) {
-              keys[i] = mx;
-              if (i == 0) a.tm_heads[(long)rows[r] * a.tm_segcap + seg] = mx;
-            }
-          }
+          a.tm_keys[(long)rows[r] * a.tm_cap + base + lane] = k;
+          const unsigned long long mx = wave_max_u64(k);
+          if (lane == 0) a.tm_heads[(long)rows[r] * a.tm_segcap + seg] = mx;
         }
       }
     }
@@ -1292,13 +1285,14 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// One workgroup of kTopkThreads per row.  Each gather segment (one tile's keys
-// for the row) is sorted descending, so the m-th largest segment head mu is
-// a lower bound of the row's m-th largest key (m heads are keys >= mu), and
-// at most m segments reach it: the keys >= mu number at most m*m.  Each of
-// those counts the candidates above it; a count below m is its output
-// position.  With fewer than m segments every key is a candidate (fewer
-// than m*m of them).
+// One workgroup of kTopkThreads per row.  Each gather segment holds one
+// tile's keys for the row (zeros where a slot has no token) and its head is
+// their maximum, so the m-th largest head mu is a lower bound of the row's
+// m-th largest key (m heads are keys >= mu), and only the m segments whose
+// heads are the m largest (heads are distinct) hold keys >= mu: at most
+// m*64 candidates.  Each of those counts the candidates above it; a count
+// below m is its output position.  With fewer than m segments every key is
+// a candidate.
 __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
   extern __shared__ unsigned long long tm_lds[];   // heads [segcap], then candidates
   __shared__ uint32_t ncand;
@@ -1310,7 +1304,10 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
   const int m = a.m;
   const unsigned long long c = a.fixed_segs > 0 ? 0ull : a.cnt[b];
   const int segs = a.fixed_segs > 0 ? a.fixed_segs : (int)(c >> 32);
-  const int n = a.fixed_segs > 0 ? a.fixed_segs * m : (int)(uint32_t)c;
+  const int n = a.fixed_segs > 0 ? a.fixed_segs * kTileTokens : (int)(uint32_t)c;
+  // keys >= mu come from the m segments whose heads are the m largest
+  // (heads are distinct), so at most m * 64 of them
+  const int cap_c = m * kTileTokens;
   unsigned long long* heads = tm_lds;
   unsigned long long* cand = tm_lds + a.segcap;
   const unsigned long long* hsrc = a.heads + (long)b * a.segcap;
@@ -1335,15 +1332,24 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
 #pragma unroll
     for (int i = 1; i < kTopkWaves; ++i) mu = min(mu, wred[i]);
   }
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const unsigned long long k = ksrc[i];
-    if (k >= mu && k != 0ull) {
-      const uint32_t at = atomicAdd(&ncand, 1u);
-      if (at < (uint32_t)kTopMCand) cand[at] = k;
+  // eight loads in flight per thread before any is tested (clamped, so
+  // unconditional; a clamped repeat of the last key is dropped by i < n)
+  constexpr int kScan = 8;
+  for (int i0 = 0; i0 < n; i0 += kScan * kTopkThreads) {
+    unsigned long long kk[kScan];
+#pragma unroll
+    for (int u = 0; u < kScan; ++u) kk[u] = ksrc[min(i0 + u * kTopkThreads + tid, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kScan; ++u) {
+      const unsigned long long k = kk[u];
+      if (i0 + u * kTopkThreads + tid < n && k >= mu && k != 0ull) {
+        const uint32_t at = atomicAdd(&ncand, 1u);
+        if (at < (uint32_t)cap_c) cand[at] = k;
+      }
     }
   }
   __syncthreads();
-  const int nc = min((int)ncand, kTopMCand);
+  const int nc = min((int)ncand, cap_c);
   int32_t* tok = a.tokens + (long)b * m;
   float* val = a.logits + (long)b * m;
   for (int i = tid; i < nc; i += kTopkThreads) {
@@ -1563,7 +1569,7 @@ hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s) {
   t.fixed_segs = a.tm_rank ? a.K * a.t.tpc : 0;
   t.tokens = a.tm_tokens;
   t.logits = a.tm_logits;
-  const size_t lds = ((size_t)a.tm_segcap + kTopMCand) * sizeof(unsigned long long);
+  const size_t lds = ((size_t)a.tm_segcap + (size_t)a.m * kTileTokens) * sizeof(unsigned long long);
   hipLaunchKernelGGL(topm_merge_kernel, dim3(a.B), dim3(kTopkThreads), lds, s, t);
   return hipGetLastError();
 }

@@ -228,7 +228,8 @@ ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K,
  *            (sized for m = CE_MAX_TOP_M), 256-byte aligned
  * Other arguments and errors as ce_top_tokens, plus BAD_SHAPE for m out of
  * range and UNSUPPORTED when a row's K largest clusters hold too many tiles
- * for the merge (more than 6144 64-token tiles). */
+ * for the merge (more than 8160 - 64*m tiles of 64 tokens: 6112 at m = 32,
+ * 7648 at m = 8). */
 #define CE_MAX_TOP_M 32
 ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m,
                    int32_t* tokens, float* logits, int32_t* topk_ids_or_null,
