@@ -805,7 +805,7 @@ struct TopkArgs {
   int ldK;
   unsigned long long* cl_sel;      // [ceil(Nc/64)][64]: bit i of word (w, b) = row b selected 64w+i
   unsigned long long* best;        // [64] argmax slots, cleared per row (or null)
-  int16_t* rank;                   // [rows][ldR] output position of each selected id (or null)
+  int16_t* rank;                   // [rows][ldR] output position of each selected id (RANK)
   int ldR;
 };
 
@@ -853,7 +853,7 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* vals, int n, uin
 // Rows with more than kCandCap keys >= mu (K > 512 on large rows, or masses
 // of equal scores) fall back to a bit-serial select over all keys with one
 // barrier per bit.  K >= Nc keeps every centroid.
-template <int EPT, int MODE>
+template <int EPT, int MODE, bool RANK = false>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   static_assert(EPT >= 1 && EPT <= 32 && kWave % EPT == 0, "per-thread keys");
   __shared__ __attribute__((aligned(16))) uint32_t cand[kCandCap + kCountBlock];
@@ -1015,7 +1015,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int i = 0; i < EPT; ++i)
     if (sel & (1u << i)) {
-      if (a.rank) a.rank[(long)b * a.ldR + first + i] = (int16_t)pos;
+      if constexpr (RANK) a.rank[(long)b * a.ldR + first + i] = (int16_t)pos;
       out[pos++] = first + i;
     }
 
@@ -1453,8 +1453,12 @@ hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
 
 template <int EPT>
 static void launch_topk_ept(const TopkArgs& t, int B, int mode, hipStream_t s) {
+  // the ranks (top-m on equal clusters) come from their own instantiation,
+  // so the other calls' kernel carries none of their stores
   if (mode == kTopkOnly)
     hipLaunchKernelGGL((topk_kernel<EPT, kSelIds>), dim3(B), dim3(kTopkThreads), 0, s, t);
+  else if (t.rank)
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true>), dim3(B), dim3(kTopkThreads), 0, s, t);
   else
     hipLaunchKernelGGL((topk_kernel<EPT, kSelMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
 }
