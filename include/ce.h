@@ -225,7 +225,7 @@ ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K,
  *   tokens   DEVICE [B][m] int32
  *   logits   DEVICE [B][m] fp32
  *   ws       DEVICE workspace of ce_workspace_bytes(head, B, K, CE_OP_TOP_M)
- *            (sized for m = CE_MAX_TOP_M), 256-byte aligned
+ *            (the same for every m), 256-byte aligned
  * Other arguments and errors as ce_top_tokens, plus BAD_SHAPE for m out of
  * range and UNSUPPORTED when a row's K largest clusters hold too many tiles
  * for the merge (more than 8160 - 64*m tiles of 64 tokens: 6112 at m = 32,

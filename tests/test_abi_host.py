@@ -139,9 +139,9 @@ def test_create_ragged_and_sizes(lib):
         assert lib.ce_workspace_bytes(h, 8, 0, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
         assert lib.ce_workspace_bytes(h, 8, 1, 9, ctypes.byref(n)) == ERR["CE_ERR_UNSUPPORTED"]
         # top-m: the masked sizes plus its segment lists (tiles of the K
-        # largest clusters: 2 + 2 for K=2, for m = CE_MAX_TOP_M keys each)
+        # largest clusters: 2 + 2 for K=2, of one 64-token tile's keys each)
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_M, ctypes.byref(n)) == 0
-        assert n.value >= sizes[_ffi.CE_OP_TOP_TOKENS] + 8 * 4 * _ffi.CE_MAX_TOP_M * 8
+        assert n.value >= sizes[_ffi.CE_OP_TOP_TOKENS] + 8 * 4 * 64 * 8
     finally:
         lib.ce_head_destroy(h)
 
