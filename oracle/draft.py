@@ -18,13 +18,14 @@ backbone hidden size, a float32 buffer).  This module composes
 Readings where the page leaves a step open (also listed in the design notes):
 
 * RMSNorm is the plain one: ``y_k = x_k * w_k / sqrt(mean_j x_j^2 + eps)``.
-  Its canonical rounding ("canonical norm"): squares are exact in float64;
-  each 64-element chunk of the row is summed by a balanced pairwise tree
-  (adjacent pairs, then adjacent pairs of those, six levels), the chunk sums
-  are added in chunk order from +0.0; then ``v = ss / d + eps`` (eps widened
-  from float32), ``r = 1 / sqrt(v)``, ``y_k = (x_k * r) * w_k``, every step
-  one correctly rounded float64 operation; ``y`` is rounded to float32
-  (nearest-even) and, for bf16 heads, that float32 to bf16 (nearest-even).
+  Its canonical rounding ("canonical norm"): the sum of squares is the same
+  sequential float64 chain as every dot product of the head, applied to x
+  with itself: ``ss_0 = +0.0``, ``ss_{k+1} = fl64(ss_k + x_k * x_k)`` for
+  k = 0 .. d-1 in order (each square is exact in float64), kept in float64;
+  then ``v = ss / d + eps`` (eps widened from float32), ``r = 1 / sqrt(v)``,
+  ``y_k = (x_k * r) * w_k``, every step one correctly rounded float64
+  operation; ``y`` is rounded to float32 (nearest-even) and, for bf16 heads,
+  that float32 to bf16 (nearest-even).
 * The embedding product follows the model's dtype rule: the bf16 (or fp32)
   table element times the float32 ``normalizer`` in float32 (one rounding),
   then, for bf16, rounded to bf16 (nearest-even).  A row with no candidate
@@ -37,7 +38,7 @@ import numpy as np
 
 from .masked_head import top_tokens, upcast
 
-__all__ = ["f32_to_bf16_bits", "rms_norm", "embed_rows", "draft_step"]
+__all__ = ["f32_to_bf16_bits", "sum_of_squares", "rms_norm", "embed_rows", "draft_step"]
 
 CHUNK = 64
 
@@ -55,13 +56,15 @@ def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
     return out.astype(np.uint16)
 
 
-def _chunk_tree_sums(q: np.ndarray) -> np.ndarray:
-    """Balanced pairwise sums of each 64-element chunk of the last axis."""
-    n, d = q.shape
-    t = q.reshape(n, d // CHUNK, CHUNK)
-    while t.shape[-1] > 1:
-        t = t[..., 0::2] + t[..., 1::2]
-    return t[..., 0]
+def sum_of_squares(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Float64 sum of squares of each row of x ``[B,d]``, the canonical
+    chain: from +0.0, one square (exact in float64) added per step in
+    hidden-dimension order, one rounding per step, no final rounding."""
+    X = upcast(x, dtype)
+    ss = np.zeros(X.shape[0], dtype=np.float64)   # +0.0
+    for k in range(X.shape[1]):                   # hidden-dimension order
+        ss = ss + X[:, k] * X[:, k]
+    return ss
 
 
 def rms_norm(x: np.ndarray, w: np.ndarray, eps: float, dtype: str) -> np.ndarray:
@@ -75,10 +78,7 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float, dtype: str) -> np.ndarray
     n, d = X.shape
     if d % CHUNK:
         raise ValueError("d must be a multiple of 64")
-    ts = _chunk_tree_sums(X * X)            # [n, d/64], squares exact
-    ss = np.zeros(n, dtype=np.float64)
-    for g in range(d // CHUNK):             # chunk order, from +0.0
-        ss = ss + ts[:, g]
+    ss = sum_of_squares(x, dtype)
     v = ss / np.float64(d) + np.float64(np.float32(eps))
     r = np.float64(1.0) / np.sqrt(v)
     y = (X * r[:, None]) * W[None, :]

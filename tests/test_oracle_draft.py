@@ -34,34 +34,70 @@ def golden():
         return json.load(f)
 
 
+def _hex_array(c, key, rest_key, d, dt):
+    """A golden vector: "<key>_fill", a "<key>" string of repeated bit
+    patterns, or a sparse "<key>" dict with the other entries "<rest_key>"."""
+    if key + "_fill" in c:
+        return np.full(d, int(c[key + "_fill"], 16), dtype=dt)
+    v = c[key]
+    if isinstance(v, dict):
+        out = np.full(d, int(c.get(rest_key, "0x0"), 16), dtype=dt)
+        for k, b in v.items():
+            out[int(k)] = int(b, 16)
+        return out
+    return np.tile(np.array([int(t, 16) for t in v.split()], dtype=dt), c[key + "_repeat"])
+
+
 def _case_arrays(c):
+    """(x, w, expected) of a golden norm case: bf16 bit patterns, or float32
+    values for "dtype": "f32"."""
     d = c["d"]
-    if "x_fill" in c:
-        x = np.full(d, int(c["x_fill"], 16), dtype=np.uint16)
-    else:
-        x = np.zeros(d, dtype=np.uint16)
-        for k, v in c["x"].items():
-            x[int(k)] = int(v, 16)
-    if "w_fill" in c:
-        w = np.full(d, int(c["w_fill"], 16), dtype=np.uint16)
-    else:
-        w = np.tile(_bits(c["w"]), c["w_repeat"])
-    return x, w
+    f32 = c.get("dtype", "bf16") == "f32"
+    dt = np.uint32 if f32 else np.uint16
+    x = _hex_array(c, "x", "x_rest", d, dt)
+    w = _hex_array(c, "w", "w_rest", d, dt)
+    want = w.copy() if c["expect"] == "same as w" else _hex_array(c, "expect", "expect_rest", d, dt)
+    if f32:
+        x, w, want = x.view(np.float32), w.view(np.float32), want.view(np.float32)
+    return x, w, want
 
 
 def test_golden_rms_norm(golden):
     for c in golden["rms_norm"]:
-        x, w = _case_arrays(c)
-        got = ds.rms_norm(x[None, :], w, c["eps"], "bf16")[0]
-        if c["expect"] == "same as w":
-            want = w
-        elif isinstance(c["expect"], dict):
-            want = np.full(c["d"], int(c["expect_rest"], 16), dtype=np.uint16)
-            for k, v in c["expect"].items():
-                want[int(k)] = int(v, 16)
-        else:
-            want = np.tile(_bits(c["expect"]), c["expect_repeat"])
+        x, w, want = _case_arrays(c)
+        dtype = c.get("dtype", "bf16")
+        got = ds.rms_norm(x[None, :], w, c["eps"], dtype)[0]
+        if dtype == "f32":
+            got, want = got.view(np.uint32), want.view(np.uint32)
         assert np.array_equal(got, want), c["name"]
+
+
+def test_sum_of_squares_is_sequential():
+    """The absorbed-squares golden row: its sequential sum of squares is
+    exactly 2^54 (every later square is below half a float64 spacing there),
+    while the exact sum is 2^54 + 63 (1 + 2^-22 + 2^-46)."""
+    x = np.full((1, 64), np.float32(1.0 + 2.0 ** -23), dtype=np.float32)
+    x[0, 0] = np.float32(2.0 ** 27)
+    assert ds.sum_of_squares(x, "f32")[0] == 2.0 ** 54
+    # the same squares in the opposite order: the 63 small ones first
+    # (63 + 63 (2^-22 + 2^-46), exact below 2^54), then 2^54 added once:
+    # the exact sum rounded once, the float64 multiple of 4 nearest 2^54 + 63.000015
+    assert ds.sum_of_squares(x[:, ::-1].copy(), "f32")[0] == 2.0 ** 54 + 64
+
+
+@pytest.mark.parametrize("seed,d,scale", [(1, 64, 1.0), (2, 256, 1e3), (3, 192, 1e-3)])
+def test_sum_of_squares_within_sequential_bound(seed, d, scale):
+    """Against exact rationals: every partial sum of positive terms rounds
+    once, so |ss - exact| <= (d - 1) 2^-53 exact (to first order).  Exponent-
+    spread rows (a few entries 2^20 larger) exercise absorption."""
+    rng = np.random.default_rng(seed)
+    X = (rng.standard_normal((4, d)) * scale).astype(np.float32)
+    X[:, ::17] *= np.float32(2.0 ** 20)
+    got = ds.sum_of_squares(X, "f32")
+    for b in range(4):
+        exact = sum(Fraction(float(v)) ** 2 for v in X[b])
+        err = abs(Fraction(float(got[b])) - exact)
+        assert err <= Fraction(d, 2 ** 53) * exact, b
 
 
 def test_golden_embedding(golden):
