@@ -20,7 +20,7 @@ import numpy as np
 
 from . import _ffi
 from ._ffi import (CE_BF16, CE_F32, CE_MAX_TOP_M, CE_OP_DRAFT_STEP, CE_OP_MASKED_LOGITS,
-                   CE_OP_TOP_M, CE_OP_TOP_TOKENS, CeError, check)
+                   CE_OP_SCORE, CE_OP_TOP_M, CE_OP_TOP_TOKENS, CE_OP_TOPK, CeError, check)
 
 __all__ = ["Head", "Graph", "CeError", "load_library"]
 
@@ -55,7 +55,7 @@ def _host_i32(a) -> np.ndarray:
 
 
 class Graph:
-    """An instantiated HIP graph of one ``top_tokens`` or ``masked_logits`` call."""
+    """An instantiated HIP graph of one captured call."""
 
     def __init__(self, lib, handle, keep):
         self._lib = lib
@@ -263,24 +263,43 @@ class Head:
               "ce_draft_step")
         return h_out, out, (emb_out if emb_table is not None else None)
 
-    def capture(self, op: int, h, K: int | None, out, topk_out=None, stream=None) -> Graph:
-        """Capture one call into a HIP graph with its own workspace.
+    def capture(self, op: int, h, K: int | None, out, topk_out=None, stream=None, *, m: int = 0,
+                logits_out=None, norm_weight=None, eps: float = 0.0, h_out=None, emb_table=None,
+                normalizer: float = 1.0, emb_out=None) -> Graph:
+        """Capture one call of any op into a HIP graph (with its own workspace).
 
-        ``op`` is ``CE_OP_TOP_TOKENS`` or ``CE_OP_MASKED_LOGITS``; ``h``, ``out``
-        and ``topk_out`` are read/written at the same addresses on every launch.
-        ``stream`` (a torch stream, not the null stream) is used for capture.
+        ``op`` is one of the ``OP_*`` codes; ``h`` is the op's input (the rows,
+        the ``[B, Nc]`` scores for ``OP_TOPK``, the rows before the norm for
+        ``OP_DRAFT_STEP``) and ``out`` its first output (scores, top-K ids,
+        tokens or logits).  ``OP_TOP_M`` also takes ``m`` and ``logits_out``;
+        ``OP_DRAFT_STEP`` takes ``norm_weight``, ``eps``, ``h_out`` and
+        optionally ``emb_table``, ``normalizer`` and ``emb_out``.  Every tensor
+        is read or written at the same address on every launch.  ``stream``
+        (a torch stream, not the null stream) is used for capture.
         """
         torch = _torch()
-        B = self._check_h(h)
-        K = self._k(K)
-        ws = self.new_workspace(B, K, op)
+        B = h.shape[0]
+        if op == CE_OP_TOPK:
+            if h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] != self.Nc or not h.is_contiguous():
+                raise ValueError(f"scores must be a contiguous fp32 [B, {self.Nc}] tensor")
+        else:
+            self._check_h(h)
+        K = 1 if op == CE_OP_SCORE else self._k(K)
+        ws = self.new_workspace(B, K, op) if op not in (CE_OP_SCORE, CE_OP_TOPK) else None
+        ptr = (lambda t: 0 if t is None else t.data_ptr())
+        call = _ffi.CeCall(
+            op=op, in_=h.data_ptr(), B=B, K=K, m=int(m), out=out.data_ptr(),
+            out_logits=ptr(logits_out), topk_ids=ptr(topk_out), ws=ptr(ws),
+            ws_bytes=0 if ws is None else ws.numel(), norm_weight=ptr(norm_weight),
+            eps=float(eps), h_out=ptr(h_out), emb_table=ptr(emb_table),
+            emb_dim=0 if emb_table is None else int(emb_table.shape[1]),
+            normalizer=float(normalizer), emb_out=ptr(emb_out))
         s = stream if stream is not None else torch.cuda.Stream(self.device)
         g = ctypes.c_void_p()
-        check(self._lib.ce_graph_capture(self._handle, op, h.data_ptr(), B, K, out.data_ptr(),
-                                         0 if topk_out is None else topk_out.data_ptr(),
-                                         ws.data_ptr(), ws.numel(), s.cuda_stream,
-                                         ctypes.byref(g)), "ce_graph_capture")
-        return Graph(self._lib, g, (h, out, topk_out, ws, self))
+        check(self._lib.ce_graph_capture_call(self._handle, ctypes.byref(call), s.cuda_stream,
+                                              ctypes.byref(g)), "ce_graph_capture_call")
+        keep = (h, out, topk_out, ws, logits_out, norm_weight, h_out, emb_table, emb_out, self)
+        return Graph(self._lib, g, keep)
 
     def close(self) -> None:
         if getattr(self, "_handle", None):
@@ -294,6 +313,8 @@ class Head:
             pass
 
 
+OP_SCORE = CE_OP_SCORE
+OP_TOPK = CE_OP_TOPK
 OP_TOP_TOKENS = CE_OP_TOP_TOKENS
 OP_MASKED_LOGITS = CE_OP_MASKED_LOGITS
 OP_TOP_M = CE_OP_TOP_M

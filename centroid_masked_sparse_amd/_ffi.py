@@ -34,6 +34,16 @@ class HeadDesc(ctypes.Structure):
     ]
 
 
+class CeCall(ctypes.Structure):
+    """``ce_call``: one call of any op, for ``ce_graph_capture_call``."""
+    _fields_ = [
+        ("op", _i32), ("in_", _vp), ("B", _i32), ("K", _i32), ("m", _i32), ("out", _vp),
+        ("out_logits", _vp), ("topk_ids", _vp), ("ws", _vp), ("ws_bytes", _sz),
+        ("norm_weight", _vp), ("eps", ctypes.c_float), ("h_out", _vp), ("emb_table", _vp),
+        ("emb_dim", _i32), ("normalizer", ctypes.c_float), ("emb_out", _vp),
+    ]
+
+
 SIGNATURES = {
     "ce_head_create": (_i32, [ctypes.POINTER(HeadDesc), ctypes.POINTER(_vp)]),
     "ce_head_destroy": (_i32, [_vp]),
@@ -49,6 +59,7 @@ SIGNATURES = {
                              ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
     "ce_graph_capture": (_i32, [_vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp,
                                 ctypes.POINTER(_vp)]),
+    "ce_graph_capture_call": (_i32, [_vp, ctypes.POINTER(CeCall), _vp, ctypes.POINTER(_vp)]),
     "ce_graph_launch": (_i32, [_vp, _vp]),
     "ce_graph_destroy": (_i32, [_vp]),
     "ce_probe_gather_events": (_i32, [_vp, _vp]),

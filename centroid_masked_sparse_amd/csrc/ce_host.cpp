@@ -200,7 +200,8 @@ ce_status check_draft(const ce_head* h, const void* x, int B, const DraftArgs& d
 // ce_draft_step, in passes of at most kPassRows rows.
 ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* out,
                      int32_t* topk_ids, void* ws, size_t ws_bytes, hipStream_t stream,
-                     int m = 0, float* out2 = nullptr, const DraftArgs* draft = nullptr) {
+                     int m = 0, float* out2 = nullptr, const DraftArgs* draft = nullptr,
+                     bool dry = false) {
   ce_status st = check_call(h, hin, B, K, true);
   if (st != CE_SUCCESS) return st;
   if (op == CE_OP_DRAFT_STEP) {
@@ -221,6 +222,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
     return fail(CE_ERR_MISALIGNED, "h and logits need 16-byte, ws 256-byte alignment");
   const Layout L = make_layout(h, B, K, op);
   if (ws_bytes < L.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than ce_workspace_bytes");
+  if (dry) return CE_SUCCESS;   // arguments checked, nothing enqueued
 
   hipEvent_t pstart = g_probe_start, pstop = g_probe_stop;
   g_probe_start = g_probe_stop = nullptr;
@@ -455,13 +457,18 @@ ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op, s
   return CE_SUCCESS;
 }
 
-ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* scores,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ce_status score_impl(ce_head_t head, const void* h, int32_t B, float* scores, hipStream_t stream,
+                     bool dry) {
   ce_status st = check_call(head, h, B, 1, false);
   if (st != CE_SUCCESS) return st;
   if (B == 0) return CE_SUCCESS;
   if (!scores) return fail(CE_ERR_NULL_POINTER, "scores is NULL");
   if (!aligned(h, 16) || !aligned(scores, 4)) return fail(CE_ERR_MISALIGNED, "h needs 16-byte alignment");
+  if (dry) return CE_SUCCESS;
   for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
     ce::PassArgs a = base_args(head, 1);
     a.B = std::min(ce::kPassRows, B - b0);
@@ -474,13 +481,14 @@ ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* sc
   return CE_SUCCESS;
 }
 
-ce_status ce_topk(ce_head_t head, const float* scores, int32_t B, int32_t K, int32_t* topk_ids,
-                  hipStream_t stream) {
+ce_status topk_impl(ce_head_t head, const float* scores, int32_t B, int32_t K, int32_t* topk_ids,
+                    hipStream_t stream, bool dry) {
   ce_status st = check_call(head, scores, B, K, true);
   if (st != CE_SUCCESS) return st;
   if (B == 0) return CE_SUCCESS;
   if (!topk_ids) return fail(CE_ERR_NULL_POINTER, "topk_ids is NULL");
   if (!aligned(scores, 4) || !aligned(topk_ids, 4)) return fail(CE_ERR_MISALIGNED, "scores and ids need 4-byte alignment");
+  if (dry) return CE_SUCCESS;
   for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
     ce::PassArgs a = base_args(head, K);
     a.B = std::min(ce::kPassRows, B - b0);
@@ -492,6 +500,20 @@ ce_status ce_topk(ce_head_t head, const float* scores, int32_t B, int32_t K, int
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
   }
   return CE_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+ce_status ce_score_centroids(ce_head_t head, const void* h, int32_t B, float* scores,
+                             hipStream_t stream) {
+  return score_impl(head, h, B, scores, stream, false);
+}
+
+ce_status ce_topk(ce_head_t head, const float* scores, int32_t B, int32_t K, int32_t* topk_ids,
+                  hipStream_t stream) {
+  return topk_impl(head, scores, B, K, topk_ids, stream, false);
 }
 
 ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t* tokens,
@@ -519,25 +541,52 @@ ce_status ce_draft_step(ce_head_t head, const void* x, const void* norm_weight, 
                     stream, 0, nullptr, &dr);
 }
 
-ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B, int32_t K, void* out,
-                           int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream,
-                           ce_graph_t* graph) {
-  if (!graph) return fail(CE_ERR_NULL_POINTER, "graph is NULL");
-  *graph = nullptr;
-  if (op != CE_OP_TOP_TOKENS && op != CE_OP_MASKED_LOGITS)
-    return fail(CE_ERR_UNSUPPORTED, "only CE_OP_TOP_TOKENS and CE_OP_MASKED_LOGITS are captured");
+}  // extern "C"
+
+namespace {
+
+// Enqueue one described call, or with `dry` only check its arguments (no
+// HIP call is made then).
+ce_status enqueue_call(ce_head_t head, const ce_call& c, hipStream_t stream, bool dry) {
+  switch (c.op) {
+    case CE_OP_SCORE:
+      return score_impl(head, c.in, c.B, static_cast<float*>(c.out), stream, dry);
+    case CE_OP_TOPK:
+      return topk_impl(head, static_cast<const float*>(c.in), c.B, c.K,
+                       static_cast<int32_t*>(c.out), stream, dry);
+    case CE_OP_TOP_TOKENS:
+    case CE_OP_MASKED_LOGITS:
+      return run_sparse(head, c.op, c.in, c.B, c.K, c.out, c.topk_ids, c.ws, c.ws_bytes, stream, 0,
+                        nullptr, nullptr, dry);
+    case CE_OP_TOP_M:
+      return run_sparse(head, c.op, c.in, c.B, c.K, c.out, c.topk_ids, c.ws, c.ws_bytes, stream,
+                        c.m, c.out_logits, nullptr, dry);
+    case CE_OP_DRAFT_STEP: {
+      const DraftArgs dr{c.norm_weight, c.eps, c.h_out, c.emb_table, c.emb_dim, c.normalizer,
+                         c.emb_out};
+      return run_sparse(head, c.op, c.in, c.B, c.K, c.out, c.topk_ids, c.ws, c.ws_bytes, stream, 0,
+                        nullptr, &dr, dry);
+    }
+    default:
+      return fail(CE_ERR_UNSUPPORTED, "unknown op");
+  }
+}
+
+ce_status capture(ce_head_t head, const ce_call& c, hipStream_t stream, ce_graph_t* graph) {
+  if (c.op < CE_OP_SCORE || c.op > CE_OP_DRAFT_STEP) return fail(CE_ERR_UNSUPPORTED, "unknown op");
   if (!stream) return fail(CE_ERR_UNSUPPORTED, "capture needs a non-null stream");
-  // validate before capturing so that a bad call leaves no capture behind
-  ce_status st = check_call(head, h, B, K, true);
+  // check the call before capturing, so that a bad call leaves no capture
+  ce_status st = enqueue_call(head, c, stream, true);
   if (st != CE_SUCCESS) return st;
   hipError_t e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) return fail_hip(e, "hipStreamBeginCapture");
-  st = run_sparse(head, op, h, B, K, out, topk_ids_or_null, ws, ws_bytes, stream);
+  st = enqueue_call(head, c, stream, false);
+  const std::string call_error = g_last_error;
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(stream, &g);
   if (st != CE_SUCCESS) {
     if (g) (void)hipGraphDestroy(g);
-    return st;
+    return fail(st, call_error);
   }
   if (e != hipSuccess) return fail_hip(e, "hipStreamEndCapture");
   ce_graph* out_g = new (std::nothrow) ce_graph;
@@ -553,6 +602,39 @@ ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B,
   }
   *graph = out_g;
   return CE_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B, int32_t K, void* out,
+                           int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream,
+                           ce_graph_t* graph) {
+  if (!graph) return fail(CE_ERR_NULL_POINTER, "graph is NULL");
+  *graph = nullptr;
+  if (op != CE_OP_SCORE && op != CE_OP_TOPK && op != CE_OP_TOP_TOKENS && op != CE_OP_MASKED_LOGITS)
+    return fail(CE_ERR_UNSUPPORTED,
+                "ce_graph_capture takes CE_OP_SCORE, TOPK, TOP_TOKENS and MASKED_LOGITS; "
+                "use ce_graph_capture_call for the others");
+  ce_call c;
+  std::memset(&c, 0, sizeof(c));
+  c.op = op;
+  c.in = h;
+  c.B = B;
+  c.K = K;
+  c.out = out;
+  c.topk_ids = topk_ids_or_null;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return capture(head, c, stream, graph);
+}
+
+ce_status ce_graph_capture_call(ce_head_t head, const ce_call* call, hipStream_t stream,
+                                ce_graph_t* graph) {
+  if (!graph || !call) return fail(CE_ERR_NULL_POINTER, "call or graph is NULL");
+  *graph = nullptr;
+  return capture(head, *call, stream, graph);
 }
 
 ce_status ce_graph_launch(ce_graph_t graph, hipStream_t stream) {

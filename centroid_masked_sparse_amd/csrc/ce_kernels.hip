@@ -483,56 +483,66 @@ __device__ __forceinline__ v4u pack_norm(const double (&y)[4], float) {
   return o;
 }
 
-// A double from another lane of the same 16-lane row (DPP on both halves).
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // lane i of 8 <- lane 7-i
-constexpr int kDppMirror = 0x140;      // lane i of 16 <- lane 15-i
-
-// Sum of t over each 16-lane row as a balanced tree over lane order (lanes
-// 2m and 2m+1 first, then pairs of pairs, ...); every lane of the row ends
-// with the row's sum.  After each level the lanes of a group hold equal
-// values, so the mirrors pair whole groups.
-__device__ __forceinline__ double row16_tree_sum(double t) {
-  t = t + dpp_f64<kDppXor1>(t);
-  t = t + dpp_f64<kDppXor2>(t);
-  t = t + dpp_f64<kDppHalfMirror>(t);
-  t = t + dpp_f64<kDppMirror>(t);
-  return t;
-}
-
-__device__ __forceinline__ double read_lane_f64(double v, int lane) {
-  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-
 struct NormArgs {
   const void* w;       // [d] norm weight, head dtype
   double eps;          // widened from float32
   void* out;           // [B][d] normalised rows, head dtype
 };
 
+// ss = fl64(ss + q_k) for the four squares q[0..3] held by lane J of this
+// lane's 16-lane row, in order: a 64-bit DPP row broadcast fused into
+// v_fmac_f64 with src1 = 1.0, so each step is the sum's single rounding
+// (q * 1 is exact).  The two wait states a DPP read needs after the VALU
+// write of its source open the block.
+template <int J>
+__device__ __forceinline__ void sq_add4(double& ss, const double (&q)[4], const double& one) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f64_dpp %0, %1, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %2, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %3, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf"
+      : "+v"(ss)
+      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(one), "n"(J));
+}
+
+// Add the 64 squares of one chunk to ss in element order.  Every 16-lane
+// row of the wave holds the same chunk (lane l: elements 4(l%16) .. +3), so
+// every lane runs the same chain and ends with the same sum.
+template <typename HR>
+__device__ __forceinline__ void sq_chunk(double& ss, const HR xr) {
+  double x[4], q[4];
+  widen4(xr, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = x[i] * x[i];   // exact in float64
+  const double one = 1.0;
+  static_for<0, 16>([&](auto j) { sq_add4<decltype(j)::value>(ss, q, one); });
+}
+
+// y = (x r) w for four elements, stored to LDS and (given out) to out.
+template <typename T, typename HR>
+__device__ __forceinline__ void norm_store(const HR xr, const HR wr, double rr, T* lds,
+                                           T* __restrict__ out) {
+  double xv[4], wv[4], y[4];
+  widen4(xr, xv);
+  widen4(wr, wv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = (xv[i] * rr) * wv[i];
+  const HR o = pack_norm(y, T());
+  *reinterpret_cast<HR*>(lds) = o;
+  if (out) *reinterpret_cast<HR*>(out) = o;
+}
+
 // The final RMSNorm of the rows rows[0..RB) of x ([*][d]), written to
 // lds ([RB][d], slot r for rows[r]) and, given `out`, to out[rows[r]] for
-// r < nrows.  Canonical rounding: squares are exact in float64; each chunk
-// of 64 elements is summed by a balanced pairwise tree, the chunk sums in
-// chunk order from +0.0; v = ss / d + eps, r = 1 / sqrt(v), y = (x r) w, each
-// one correctly rounded float64 operation; y is rounded to float32 and then
-// to the head's element type (nearest, ties to even).
+// r < nrows.  Canonical rounding: the sum of squares is the sequential
+// float64 chain ss = fl64(ss + x_k^2) over k in order from +0.0 (squares
+// exact); v = ss / d + eps, r = 1 / sqrt(v), y = (x r) w, each one correctly
+// rounded float64 operation; y is rounded to float32 and then to the head's
+// element type (nearest, ties to even).
 //
-// Lane l works on chunk 4j + l/16 of each group of four chunks, elements
-// 4(l%16) .. 4(l%16)+3: its four squares make the tree's first two levels,
-// a butterfly over its 16-lane row the other four.
+// The chain runs in every lane (see sq_chunk); lane l then writes chunks
+// c = l/16 (mod 4), elements 4(l%16) .. +3.
 template <typename T, int RB>
 __device__ __forceinline__ void normalize_rows(const T* __restrict__ x, const int (&rows)[RB],
                                                int nrows, int d, const NormArgs& nm,
@@ -543,96 +553,77 @@ __device__ __forceinline__ void normalize_rows(const T* __restrict__ x, const in
   const int e4 = 4 * (lane & 15);
   const int nch = d / kChunk;
   const T* w = static_cast<const T*>(nm.w);
-  double rr[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const T* xr = x + (long)rows[r] * d;
     double ss = 0.0;
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-      const int ch = min(c0 + g, nch - 1);   // clamped: lanes past the end are not read back
-      double q[4];
-      widen4(*reinterpret_cast<const HR*>(xr + ch * kChunk + e4), q);
-      const double t = row16_tree_sum((q[0] * q[0] + q[1] * q[1]) + (q[2] * q[2] + q[3] * q[3]));
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        if (c0 + gg < nch) ss = ss + read_lane_f64(t, 16 * gg);
-    }
-    rr[r] = 1.0 / sqrt(ss / (double)d + nm.eps);
-  }
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const T* xr = x + (long)rows[r] * d;
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-      const int ch = c0 + g;
-      if (ch < nch) {
-        const int k = ch * kChunk + e4;
-        double xv[4], wv[4], y[4];
-        widen4(*reinterpret_cast<const HR*>(xr + k), xv);
-        widen4(*reinterpret_cast<const HR*>(w + k), wv);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = (xv[i] * rr[r]) * wv[i];
-        const HR o = pack_norm(y, T());
-        *reinterpret_cast<HR*>(lds + r * d + k) = o;
-        if (out && r < nrows) *reinterpret_cast<HR*>(out + (long)rows[r] * d + k) = o;
-      }
+    for (int c = 0; c < nch; ++c) sq_chunk(ss, *reinterpret_cast<const HR*>(xr + c * kChunk + e4));
+    const double rr = 1.0 / sqrt(ss / (double)d + nm.eps);
+    for (int c = g; c < nch; c += 4) {
+      const int k = c * kChunk + e4;
+      norm_store<T>(*reinterpret_cast<const HR*>(xr + k), *reinterpret_cast<const HR*>(w + k), rr,
+                    lds + r * d + k, out && r < nrows ? out + (long)rows[r] * d + k : nullptr);
     }
   }
 }
 
-// The same norm with its loads split from its arithmetic: norm_load issues
-// the rows' and the weight's loads (NG groups of four chunks, d = 256 NG),
-// norm_finish does the rest, so that other loads can go out in between.
-template <typename T, int RB, int NG>
+// The same norm with its loads split from its arithmetic, for a chunk
+// count NCH known at compile time: norm_load issues the rows' loads (every
+// chunk, as the chain reads them) and the weight's (the chunks this lane
+// writes), norm_finish does the rest, so that other loads go out in between.
+template <typename T, int RB, int NCH>
 struct NormRegs {
-  typename HQuad<T>::raw x[RB][NG];
-  typename HQuad<T>::raw w[NG];
+  static constexpr int NW = (NCH + 3) / 4;
+  typename HQuad<T>::raw x[RB][NCH];   // every chunk, as the chain reads them
+  typename HQuad<T>::raw xs[RB][NW];   // the chunks 4q + l/16 this lane writes
+  typename HQuad<T>::raw w[NW];
 };
 
-template <typename T, int RB, int NG>
-__device__ __forceinline__ void norm_load(NormRegs<T, RB, NG>& nr, const T* __restrict__ x,
+template <typename T, int RB, int NCH>
+__device__ __forceinline__ void norm_load(NormRegs<T, RB, NCH>& nr, const T* __restrict__ x,
                                           const int (&rows)[RB], int d, const NormArgs& nm) {
   using HR = typename HQuad<T>::raw;
   const int lane = threadIdx.x;
-  const int k = (lane >> 4) * kChunk + 4 * (lane & 15);
+  const int g = lane >> 4;
+  const int e4 = 4 * (lane & 15);
   const T* w = static_cast<const T*>(nm.w);
 #pragma unroll
-  for (int q = 0; q < NG; ++q) {
+  for (int c = 0; c < NCH; ++c)
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-      nr.x[r][q] = *reinterpret_cast<const HR*>(x + (long)rows[r] * d + q * 4 * kChunk + k);
-    nr.w[q] = *reinterpret_cast<const HR*>(w + q * 4 * kChunk + k);
+      nr.x[r][c] = *reinterpret_cast<const HR*>(x + (long)rows[r] * d + c * kChunk + e4);
+  // the lane's own chunks are loaded once more (cache hits) rather than
+  // picked out of nr.x by a lane-dependent index, which would go to scratch
+#pragma unroll
+  for (int q = 0; q < NormRegs<T, RB, NCH>::NW; ++q) {   // clamped: unconditional loads
+    const int k = min(4 * q + g, NCH - 1) * kChunk + e4;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) nr.xs[r][q] = *reinterpret_cast<const HR*>(x + (long)rows[r] * d + k);
+    nr.w[q] = *reinterpret_cast<const HR*>(w + k);
   }
 }
 
-template <typename T, int RB, int NG>
-__device__ __forceinline__ void norm_finish(const NormRegs<T, RB, NG>& nr, const int (&rows)[RB],
+template <typename T, int RB, int NCH>
+__device__ __forceinline__ void norm_finish(const NormRegs<T, RB, NCH>& nr, const int (&rows)[RB],
                                             int nrows, int d, const NormArgs& nm, T* lds,
                                             T* __restrict__ out) {
   using HR = typename HQuad<T>::raw;
   const int lane = threadIdx.x;
-  const int k = (lane >> 4) * kChunk + 4 * (lane & 15);
+  const int g = lane >> 4;
+  const int e4 = 4 * (lane & 15);
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     double ss = 0.0;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      double v[4];
-      widen4(nr.x[r][q], v);
-      const double t = row16_tree_sum((v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]));
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) ss = ss + read_lane_f64(t, 16 * gg);
-    }
+    static_for<0, NCH>([&](auto c) { sq_chunk(ss, nr.x[r][decltype(c)::value]); });
     const double rr = 1.0 / sqrt(ss / (double)d + nm.eps);
 #pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      double xv[4], wv[4], y[4];
-      widen4(nr.x[r][q], xv);
-      widen4(nr.w[q], wv);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = (xv[i] * rr) * wv[i];
-      const HR o = pack_norm(y, T());
-      *reinterpret_cast<HR*>(lds + r * d + q * 4 * kChunk + k) = o;
-      if (out && r < nrows) *reinterpret_cast<HR*>(out + (long)rows[r] * d + q * 4 * kChunk + k) = o;
+    for (int q = 0; q < NormRegs<T, RB, NCH>::NW; ++q) {
+      const int c = 4 * q + g;
+      if (c < NCH) {
+        const int k = c * kChunk + e4;
+        norm_store<T>(nr.xs[r][q], nr.w[q], rr, lds + r * d + k,
+                      out && r < nrows ? out + (long)rows[r] * d + k : nullptr);
+      }
     }
   }
 }
@@ -690,14 +681,14 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
     int lrows[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) lrows[r] = r < nrows ? r : 0;
-    if constexpr (NCH > 0 && NCH % 4 == 0) {
+    if constexpr (NCH > 0) {
       // row and weight loads first, then the tile's first stages; the norm
       // is computed while those are in flight
-      NormRegs<T, RB, NCH / 4> nr;
-      norm_load<T, RB, NCH / 4>(nr, h, rows, d, nm);
+      NormRegs<T, RB, NCH> nr;
+      norm_load<T, RB, NCH>(nr, h, rows, d, nm);
       __builtin_amdgcn_sched_barrier(0);
       dot_tile<T, RB, NCH, 2, true>(CT + blockIdx.x * tile_vecs, d, hn, lrows, nrows, acc, [&] {
-        norm_finish<T, RB, NCH / 4>(nr, rows, nrows, d, nm, hn, out);
+        norm_finish<T, RB, NCH>(nr, rows, nrows, d, nm, hn, out);
         __syncthreads();
       });
     } else {

@@ -242,9 +242,9 @@ ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t 
  * embedding times the float32 `normalizer` buffer.  For every row b < B:
  *   h_out[b]  = RMSNorm(x[b]) with weight norm_weight and epsilon eps:
  *               x_k w_k / sqrt(mean_j x_j^2 + eps) in the canonical norm
- *               rounding: squares exact in float64, each 64-element chunk
- *               summed by a balanced pairwise tree and the chunk sums in
- *               order from +0.0, then v = ss/d + eps, r = 1/sqrt(v),
+ *               rounding: the sum of squares is the float64 chain
+ *               ss = fl64(ss + x_k^2) over k in order from +0.0 (squares
+ *               exact), then v = ss/d + eps, r = 1/sqrt(v),
  *               y = (x_k r) w_k in correctly rounded float64 steps, y rounded
  *               to float32 and then to the head's dtype (nearest, ties even);
  *   tokens[b] = get_top_tokens of h_out[b], exactly as ce_top_tokens;
@@ -271,17 +271,64 @@ ce_status ce_draft_step(ce_head_t head, const void* x, const void* norm_weight, 
                         void* emb_out, int32_t* topk_ids_or_null, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
-/* Capture one call of ce_top_tokens (op CE_OP_TOP_TOKENS, out = tokens) or
- * ce_masked_logits (op CE_OP_MASKED_LOGITS, out = logits) into an
- * instantiated HIP graph, the counterpart of the page's per-batch-size CUDA
- * graphs.  The graph reads h and writes out/topk_ids/ws at the addresses given
- * here on every launch.  `stream` must not be the null stream; it is used only
- * for capture.  Errors: as the captured call, plus UNSUPPORTED for another
- * op, HIP for a capture failure. */
+/* Capture one call into an instantiated HIP graph, the counterpart of the
+ * page's per-batch-size CUDA graphs (Gemma4Proposer._setup_centroids_cuda_graphs
+ * in the vLLM compare view, diff of spec_decode/gemma4.py).  The graph reads
+ * its inputs and writes its outputs and workspace at the addresses given here
+ * on every launch; new inputs written there are picked up by the next launch.
+ * `stream` must not be the null stream; it is used only for capture.
+ * This form covers the ops whose call these arguments describe:
+ *   CE_OP_SCORE          h -> out = scores [B][Nc] fp32 (K, topk_ids, ws unused)
+ *   CE_OP_TOPK           h = scores [B][Nc] fp32 -> out = topk ids [B][K]
+ *                        (topk_ids, ws unused)
+ *   CE_OP_TOP_TOKENS     h -> out = tokens [B]
+ *   CE_OP_MASKED_LOGITS  h -> out = logits [B][V]
+ * and ce_graph_capture_call every op, CE_OP_TOP_M and CE_OP_DRAFT_STEP
+ * included.  Errors: as the captured call (checked before anything is
+ * enqueued, so a failed call leaves no capture behind), plus UNSUPPORTED for
+ * another op or the null stream, HIP for a capture failure. */
 ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B,
                            int32_t K, void* out, int32_t* topk_ids_or_null,
                            void* ws, size_t ws_bytes, hipStream_t stream,
                            ce_graph_t* graph);
+
+/* One call of any compute op, as ce_graph_capture_call takes it.  Each field
+ * has the meaning of the same argument of the op's own entry point; fields an
+ * op does not take are ignored.
+ *   op          ce_op
+ *   in          h (SCORE, TOP_TOKENS, MASKED_LOGITS, TOP_M), the scores (TOPK)
+ *               or the rows before the norm, x (DRAFT_STEP)
+ *   out         scores (SCORE), topk ids (TOPK), tokens (TOP_TOKENS, TOP_M,
+ *               DRAFT_STEP) or logits (MASKED_LOGITS)
+ *   out_logits  the [B][m] logits of TOP_M
+ *   topk_ids    topk_ids_or_null of the fused ops
+ *   norm_weight, eps, h_out, emb_table, emb_dim, normalizer, emb_out
+ *               the DRAFT_STEP operands */
+typedef struct ce_call {
+  int32_t op;
+  const void* in;
+  int32_t B;
+  int32_t K;
+  int32_t m;
+  void* out;
+  float* out_logits;
+  int32_t* topk_ids;
+  void* ws;
+  size_t ws_bytes;
+  const void* norm_weight;
+  float eps;
+  void* h_out;
+  const void* emb_table;
+  int32_t emb_dim;
+  float normalizer;
+  void* emb_out;
+} ce_call;
+
+/* Capture the call `*call` of any op into an instantiated HIP graph, as
+ * ce_graph_capture does.  Errors: NULL_POINTER for call or graph, otherwise
+ * as ce_graph_capture. */
+ce_status ce_graph_capture_call(ce_head_t head, const ce_call* call, hipStream_t stream,
+                                ce_graph_t* graph);
 
 /* Launch a captured graph on `stream`.  Errors: NULL_POINTER, HIP. */
 ce_status ce_graph_launch(ce_graph_t graph, hipStream_t stream);

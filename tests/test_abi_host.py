@@ -160,8 +160,23 @@ def test_compute_calls_before_prepare_fail_on_host(lib):
         assert "prepare" in lib.ce_last_error().decode()
         assert lib.ce_top_tokens(None, FAKE, 1, 2, FAKE, None, FAKE, 1, None) == ERR["CE_ERR_NULL_POINTER"]
         g = ctypes.c_void_p()
-        assert lib.ce_graph_capture(h, 0, FAKE, 1, 2, FAKE, None, FAKE, 1, FAKE,
+        # every check runs before the capture starts: these make no HIP call
+        assert lib.ce_graph_capture(h, _ffi.CE_OP_SCORE, FAKE, 1, 2, FAKE, None, FAKE, 1, FAKE,
+                                    ctypes.byref(g)) == NP
+        assert lib.ce_graph_capture(h, _ffi.CE_OP_TOP_M, FAKE, 1, 2, FAKE, None, FAKE, 1, FAKE,
                                     ctypes.byref(g)) == ERR["CE_ERR_UNSUPPORTED"]
+        assert lib.ce_graph_capture(h, 17, FAKE, 1, 2, FAKE, None, FAKE, 1, FAKE,
+                                    ctypes.byref(g)) == ERR["CE_ERR_UNSUPPORTED"]
+        call = _ffi.CeCall(op=_ffi.CE_OP_TOP_M, in_=FAKE, B=1, K=2, m=4, out=FAKE, out_logits=FAKE,
+                           ws=FAKE, ws_bytes=1 << 20)
+        assert lib.ce_graph_capture_call(h, None, FAKE, ctypes.byref(g)) == ERR["CE_ERR_NULL_POINTER"]
+        assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE, None) == ERR["CE_ERR_NULL_POINTER"]
+        assert lib.ce_graph_capture_call(h, ctypes.byref(call), None,
+                                         ctypes.byref(g)) == ERR["CE_ERR_UNSUPPORTED"]
+        assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE, ctypes.byref(g)) == NP
+        call.op = _ffi.CE_OP_DRAFT_STEP
+        assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE, ctypes.byref(g)) == NP
+        assert not g.value
         assert lib.ce_graph_launch(None, None) == ERR["CE_ERR_NULL_POINTER"]
         assert lib.ce_graph_destroy(None) == 0
         assert lib.ce_head_prepare(h, None, 0, None) == ERR["CE_ERR_NULL_POINTER"]

@@ -85,6 +85,39 @@ def test_sweep_config_full_size():
     _check(make_head(w, max_B=64), w, x, nw, table, 1e-6, float(np.sqrt(2560.0)), w.K)
 
 
+def test_sum_of_squares_in_element_order():
+    """The absorbed-squares row of tests/golden/draft_step.json on a float32
+    head, with the oracle's value and the hand-derived bits: the outputs are
+    0x33c00002 only when the squares are summed in element order (a pairwise
+    or any other order keeps some of the small squares and gives 0x33c00001).
+    The norm's arithmetic is one template for both element types, so this
+    pins the order of the bf16 heads' chain as well."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "draft_step.json")))
+    case = next(c for c in gold["rms_norm"] if c["name"] == "absorbed_squares_f32")
+    d = case["d"]
+    x = np.full(d, int(case["x_rest"], 16), dtype=np.uint32)
+    x[0] = int(case["x"]["0"], 16)
+    nw = np.full(d, int(case["w_rest"], 16), dtype=np.uint32)
+    nw[0] = int(case["w"]["0"], 16)
+    want = np.full(d, int(case["expect_rest"], 16), dtype=np.uint32)
+    want[0] = int(case["expect"]["0"], 16)
+    w = make_random(61, d=d, V=1024, Nc=16, dtype="f32", rows=64, ragged=False)
+    # the row three times (by itself, and between random rows), so that the
+    # chain runs in rows of every position of a pass
+    xs = np.stack([x.view(np.float32)] * 3)
+    xs[1] = np.random.default_rng(5).standard_normal(d).astype(np.float32)
+    head = make_head(w, max_B=3)
+    h, _, _ = head.draft_step(to_device(xs, "f32"), to_device(nw.view(np.float32), "f32"),
+                              float(case["eps"]) or 1e-30, 4)
+    torch_mod().cuda.synchronize()
+    got = _bits(h, "f32")
+    assert np.array_equal(got[0], want) and np.array_equal(got[2], want)
+    h_o = od.rms_norm(xs, nw.view(np.float32), float(case["eps"]) or 1e-30, "f32")
+    assert np.array_equal(got, _np_bits(h_o, "f32"))
+
+
 def test_zero_rows_large_eps_and_identity_scale():
     """A zero row normalises to signed zeros; eps = 4 dominates; normalizer 1
     returns the table rows unchanged."""
