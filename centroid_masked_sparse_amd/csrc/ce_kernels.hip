@@ -1266,7 +1266,7 @@ struct TopmArgs {
   const unsigned long long* keys;   // [B][cap]
   const unsigned long long* heads;  // [B][segcap]
   int cap, segcap, m;
-  int fixed_segs;                   // > 0: every row has this many segments of m keys (zeros pad)
+  int fixed_segs;                   // > 0: every row has this many segments of 64 keys (zeros pad)
   int32_t* tokens;                  // [B][m]
   float* logits;                    // [B][m]
 };
