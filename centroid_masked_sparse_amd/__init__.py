@@ -196,6 +196,20 @@ class Head:
               "ce_top_tokens")
         return out
 
+    def top_tokens_static(self, h, K: int | None = None, out=None, topk_out=None):
+        """``top_tokens`` through ``ce_top_tokens_static``: no workspace is
+        allocated (the library's static per-GPU scratch is used), so calls on
+        one GPU must not overlap."""
+        torch = _torch()
+        B = self._check_h(h)
+        K = self._k(K)
+        if out is None:
+            out = torch.empty((B,), dtype=torch.int32, device=self.device)
+        check(self._lib.ce_top_tokens_static(self._handle, h.data_ptr(), B, K, out.data_ptr(),
+                                             0 if topk_out is None else topk_out.data_ptr(),
+                                             _stream_handle(self.device)), "ce_top_tokens_static")
+        return out
+
     def masked_logits(self, h, K: int | None = None, out=None, topk_out=None):
         """``[B, V]`` fp32 logits, -inf outside the candidates (forward)."""
         torch = _torch()

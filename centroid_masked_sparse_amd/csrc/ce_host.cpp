@@ -22,6 +22,9 @@
 #include "../../include/ce.h"
 #include "ce_internal.h"
 
+static_assert(CE_STATIC_SCRATCH_BYTES == ce::kStaticScratchBytes,
+              "the header's static scratch size is the library's");
+
 struct ce_head {
   int32_t d = 0, V = 0, Nc = 0, max_B = 0, max_K = 0, dtype = 0, slab = CE_SLAB_NATIVE;
   const void* C = nullptr;
@@ -519,6 +522,24 @@ ce_status ce_topk(ce_head_t head, const float* scores, int32_t B, int32_t K, int
 ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t* tokens,
                         int32_t* topk_ids_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_sparse(head, CE_OP_TOP_TOKENS, h, B, K, tokens, topk_ids_or_null, ws, ws_bytes, stream);
+}
+
+ce_status ce_top_tokens_static(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t* tokens,
+                               int32_t* topk_ids_or_null, hipStream_t stream) {
+  ce_status st = check_call(head, h, B, K, true);
+  if (st != CE_SUCCESS) return st;
+  const size_t need = make_layout(head, B, K, CE_OP_TOP_TOKENS).total;
+  if (need > ce::kStaticScratchBytes)
+    return fail(CE_ERR_UNSUPPORTED, "this call needs " + std::to_string(need) +
+                                        " bytes of workspace; the static scratch holds " +
+                                        std::to_string(ce::kStaticScratchBytes) +
+                                        " (use ce_top_tokens with a workspace)");
+  if (B == 0) return CE_SUCCESS;
+  void* ws = nullptr;
+  const hipError_t e = ce::static_scratch(&ws);
+  if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+  return run_sparse(head, CE_OP_TOP_TOKENS, h, B, K, tokens, topk_ids_or_null, ws,
+                    ce::kStaticScratchBytes, stream);
 }
 
 ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K, float* logits,

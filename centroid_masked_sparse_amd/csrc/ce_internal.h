@@ -95,6 +95,11 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: T
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
 hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
+// Size of the static scratch array of ce_top_tokens_static (bytes).
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+// Device address of the static scratch array on the current device (looked
+// up with hipGetSymbolAddress on the first call per device).
+hipError_t static_scratch(void** ptr);
 // Read every 16-byte vector of buf[0, bytes) once (measurement probe).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 

@@ -206,6 +206,23 @@ ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K,
                         int32_t* tokens, int32_t* topk_ids_or_null, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/* ce_top_tokens for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * same call and results without the workspace arguments.  Its workspace is a
+ * static array of the library, CE_STATIC_SCRATCH_BYTES on each GPU, held
+ * until the process ends; the call allocates nothing.  Every call on one GPU
+ * shares that GPU's array, so calls that may overlap on one GPU (on several
+ * streams, or from several threads without ordering) race and must not be
+ * issued; calls ordered on one stream are safe.  The array's content is not
+ * needed from one call to the next (every region is written before it is
+ * read).  Errors: as ce_top_tokens, plus UNSUPPORTED when the call's
+ * workspace (ce_workspace_bytes(head, B, K, CE_OP_TOP_TOKENS)) exceeds
+ * CE_STATIC_SCRATCH_BYTES, HIP if the array's address cannot be found. */
+#define CE_STATIC_SCRATCH_BYTES (4u << 20)
+ce_status ce_top_tokens_static(ce_head_t head, const void* h, int32_t B, int32_t K,
+                               int32_t* tokens, int32_t* topk_ids_or_null,
+                               hipStream_t stream);
+
 /* forward: logits[b][t] = canonical logit of token t if t is owned by one of
  * row b's K selected centroids, else -inf.  Every entry of [B][V] is written.
  *   logits  DEVICE [B][V] fp32, 16-byte aligned
