@@ -88,10 +88,15 @@ class Head:
     float32 scale per row (bf16 heads only; logits change accordingly).
     """
 
+    _PROJ = {"auto": _ffi.CE_PROJ_AUTO, "exact": _ffi.CE_PROJ_EXACT, "mfma": _ffi.CE_PROJ_MFMA}
+
     def __init__(self, centroids, emb_ordered, token_of_slot, cluster_offsets=None,
-                 max_B: int = 64, max_K: int | None = None, slabs: str = "native"):
+                 max_B: int = 64, max_K: int | None = None, slabs: str = "native",
+                 projection: str = "auto"):
         if slabs not in ("native", "fp8"):
             raise ValueError("slabs must be 'native' or 'fp8'")
+        if projection not in self._PROJ:
+            raise ValueError("projection must be 'auto', 'exact' or 'mfma'")
         torch = _torch()
         self._lib = _ffi.load()
         for name, t in (("centroids", centroids), ("emb_ordered", emb_ordered)):
@@ -115,7 +120,8 @@ class Head:
             cluster_offsets=None if self._off is None else
             self._off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
             token_of_slot=self._tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-            slab_format=_ffi.CE_SLAB_FP8_E4M3 if slabs == "fp8" else _ffi.CE_SLAB_NATIVE)
+            slab_format=_ffi.CE_SLAB_FP8_E4M3 if slabs == "fp8" else _ffi.CE_SLAB_NATIVE,
+            projection=self._PROJ[projection])
         self.slabs = slabs
         handle = ctypes.c_void_p()
         check(self._lib.ce_head_create(ctypes.byref(desc), ctypes.byref(handle)), "ce_head_create")
@@ -157,6 +163,24 @@ class Head:
 
     def _k(self, K):
         return self.max_K if K is None else int(K)
+
+    def repair_counts(self) -> tuple[int, int]:
+        """(rows whose top-K boundary took recomputed canonical keys, rows
+        recomputed whole) since prepare, for the MFMA projection.  Synchronises."""
+        c = (ctypes.c_uint64 * 2)()
+        check(self._lib.ce_head_repair_counts(self._handle, c), "ce_head_repair_counts")
+        return int(c[0]), int(c[1])
+
+    def approx_scores(self, h, out=None):
+        """``[B, Nc]`` fp32 scores of the MFMA projection alone (bf16 heads), the
+        approximate values the certified top-K starts from."""
+        torch = _torch()
+        B = self._check_h(h)
+        if out is None:
+            out = torch.empty((B, self.Nc), dtype=torch.float32, device=self.device)
+        check(self._lib.ce_probe_approx_scores(self._handle, h.data_ptr(), B, out.data_ptr(),
+                                               _stream_handle(self.device)), "ce_probe_approx_scores")
+        return out
 
     # ------------------------------------------------------------------ calls
     def score_centroids(self, h, out=None):

@@ -19,6 +19,7 @@ CE_OP_DRAFT_STEP = 5
 CE_MAX_TOP_M = 32
 CE_STATIC_SCRATCH_BYTES = 4 << 20
 CE_SLAB_NATIVE, CE_SLAB_FP8_E4M3 = 0, 1
+CE_PROJ_AUTO, CE_PROJ_EXACT, CE_PROJ_MFMA = 0, 1, 2
 
 # Every symbol the header declares, with (restype, argtypes).
 _vp = ctypes.c_void_p
@@ -31,7 +32,7 @@ class HeadDesc(ctypes.Structure):
         ("d", _i32), ("V", _i32), ("Nc", _i32), ("max_B", _i32), ("max_K", _i32),
         ("dtype", _i32), ("centroids", _vp), ("emb_ordered", _vp),
         ("cluster_offsets", ctypes.POINTER(_i32)), ("token_of_slot", ctypes.POINTER(_i32)),
-        ("slab_format", _i32),
+        ("slab_format", _i32), ("projection", _i32),
     ]
 
 
@@ -66,6 +67,8 @@ SIGNATURES = {
     "ce_graph_destroy": (_i32, [_vp]),
     "ce_probe_gather_events": (_i32, [_vp, _vp]),
     "ce_probe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "ce_head_repair_counts": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint64)]),
+    "ce_probe_approx_scores": (_i32, [_vp, _vp, _i32, _vp, _vp]),
     "ce_status_string": (ctypes.c_char_p, [_i32]),
     "ce_last_error": (ctypes.c_char_p, []),
 }

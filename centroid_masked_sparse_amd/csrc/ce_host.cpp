@@ -27,6 +27,8 @@ static_assert(CE_STATIC_SCRATCH_BYTES == ce::kStaticScratchBytes,
 
 struct ce_head {
   int32_t d = 0, V = 0, Nc = 0, max_B = 0, max_K = 0, dtype = 0, slab = CE_SLAB_NATIVE;
+  int32_t proj = CE_PROJ_AUTO;
+  unsigned long long* stats = nullptr;   // device: [cmax bits, repaired rows, recomputed rows]
   const void* C = nullptr;
   const void* E = nullptr;
   std::vector<int32_t> offsets;       // [Nc+1]
@@ -67,10 +69,19 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
-  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, tm_keys = 0, tm_heads = 0, tm_rank = 0, total = 0;
+  size_t scores = 0, topk = 0, cl_sel = 0, best = 0, amax = 0, tm_keys = 0, tm_heads = 0, tm_rank = 0,
+         total = 0;
   bool has_rank = false;
   int tm_segcap = 0;
 };
+
+// CE_PROJ_AUTO takes the MFMA projection for a pass of at least this many
+// multiply-adds (B Nc d).  The exact projection costs in proportion to them;
+// the certified top-K adds a few microseconds whatever their number (its
+// band recomputation included), measured as the break-even on the wide head
+// (d = 1024, Nc = 4096: MFMA from B = 32) while the sweep head (d = 256,
+// Nc = 2048) stays exact up to B = 64.
+constexpr long long kMfmaMinMacs = 1ll << 27;
 
 Layout make_layout(const ce_head* h, int B, int K, int op) {
   Layout L;
@@ -89,6 +100,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   L.topk = take(nb * (size_t)K * sizeof(int32_t));
   L.cl_sel = take(((size_t)h->Nc + 63) / 64 * ce::kPassRows * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
+  L.amax = take(ce::kArgWords * sizeof(unsigned long long));
   if (op == CE_OP_TOP_M) {
     L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);
     L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kTileTokens * sizeof(unsigned long long));
@@ -104,7 +116,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
 
 // Offsets of the device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t offsets, tos, tiles, ttok, et, escale, ct, total;
+  size_t stats, offsets, tos, tiles, ttok, et, escale, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -115,6 +127,7 @@ PersistLayout persist_layout(const ce_head* h) {
     off = round_up(off + bytes, 256);
     return at;
   };
+  p.stats = take(4 * sizeof(unsigned long long));
   p.offsets = take(((size_t)h->Nc + 1) * sizeof(int32_t));
   p.tos = take((size_t)h->V * sizeof(int32_t));
   p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
@@ -158,6 +171,7 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.ldK = a.K;
   a.cl_sel = reinterpret_cast<unsigned long long*>(ws + L.cl_sel);
   a.best = reinterpret_cast<unsigned long long*>(ws + L.best);
+  a.amax = reinterpret_cast<unsigned long long*>(ws + L.amax);
   a.tm_keys = reinterpret_cast<unsigned long long*>(ws + L.tm_keys);
   a.tm_heads = reinterpret_cast<unsigned long long*>(ws + L.tm_heads);
   a.tm_segcap = L.tm_segcap;
@@ -239,6 +253,9 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
     ce::PassArgs a = base_args(h, K);
     a.B = nb;
     a.h = static_cast<const char*>(hin) + (size_t)b0 * in_row;
+    a.approx = op != CE_OP_DRAFT_STEP &&
+               (h->proj == CE_PROJ_MFMA ||
+                (h->proj == CE_PROJ_AUTO && (long long)nb * h->Nc * h->d >= kMfmaMinMacs));
     bind_workspace(a, L, static_cast<char*>(ws));
     if (topk_ids) {
       a.topk = topk_ids + (size_t)b0 * K;
@@ -303,6 +320,10 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
     return fail(CE_ERR_BAD_DTYPE, "slab_format must be CE_SLAB_NATIVE or CE_SLAB_FP8_E4M3");
   if (desc->slab_format == CE_SLAB_FP8_E4M3 && desc->dtype != CE_BF16)
     return fail(CE_ERR_BAD_DTYPE, "FP8 slabs are quantised from bf16 heads only");
+  if (desc->projection < CE_PROJ_AUTO || desc->projection > CE_PROJ_MFMA)
+    return fail(CE_ERR_BAD_DTYPE, "projection must be CE_PROJ_AUTO, CE_PROJ_EXACT or CE_PROJ_MFMA");
+  if (desc->projection == CE_PROJ_MFMA && desc->dtype != CE_BF16)
+    return fail(CE_ERR_BAD_DTYPE, "the MFMA projection takes bf16 heads only");
   const int d = desc->d, V = desc->V, Nc = desc->Nc;
   if (d < 64 || d > ce::kMaxD || d % 64) return fail(CE_ERR_BAD_SHAPE, "d must be a multiple of 64 in [64, 8192]");
   if (V < 1) return fail(CE_ERR_BAD_SHAPE, "V must be >= 1");
@@ -321,6 +342,7 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
   h->max_K = desc->max_K;
   h->dtype = desc->dtype;
   h->slab = desc->slab_format;
+  h->proj = desc->dtype == CE_BF16 ? desc->projection : CE_PROJ_EXACT;
   h->C = desc->centroids;
   h->E = desc->emb_ordered;
   try {
@@ -415,8 +437,12 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
                                   hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
   }
-  hipError_t e =
-      head->slab == CE_SLAB_FP8_E4M3
+  hipError_t e = hipMemsetAsync(base + p.stats, 0, 4 * sizeof(unsigned long long), stream);
+  if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
+  e = ce::launch_cnorm_max(head->C, head->dtype, head->Nc, head->d,
+                           reinterpret_cast<unsigned long long*>(base + p.stats), stream);
+  if (e != hipSuccess) return fail_hip(e, "norm kernel launch");
+  e = head->slab == CE_SLAB_FP8_E4M3
           ? ce::launch_pack_fp8(head->E, head->d, (long)head->tiles.size(),
                                 reinterpret_cast<const uint32_t*>(base + p.tiles),
                                 reinterpret_cast<const int32_t*>(base + p.offsets), base + p.et,
@@ -443,6 +469,8 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   head->tables.escale = head->slab == CE_SLAB_FP8_E4M3 ? reinterpret_cast<const float*>(base + p.escale)
                                                         : nullptr;
   head->tables.CT = base + p.ct;
+  head->stats = reinterpret_cast<unsigned long long*>(base + p.stats);
+  head->tables.stats = head->stats;
   head->prepared = true;
   return CE_SUCCESS;
 }
@@ -685,6 +713,38 @@ ce_status ce_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hi
     return fail(CE_ERR_MISALIGNED, "buf and bytes must be multiples of 16");
   const hipError_t e = ce::launch_stream_read(buf, bytes, sink, stream);
   if (e != hipSuccess) return fail(CE_ERR_HIP, hipGetErrorString(e));
+  return CE_SUCCESS;
+}
+
+ce_status ce_head_repair_counts(ce_head_t head, uint64_t counts[2]) {
+  if (!head || !counts) return fail(CE_ERR_NULL_POINTER, "head or counts is NULL");
+  if (!head->prepared) return fail(CE_ERR_NOT_PREPARED, "ce_head_prepare has not been called");
+  unsigned long long c[2] = {0, 0};
+  const hipError_t e = hipMemcpy(c, head->stats + 1, sizeof(c), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpy");
+  counts[0] = c[0];
+  counts[1] = c[1];
+  return CE_SUCCESS;
+}
+
+ce_status ce_probe_approx_scores(ce_head_t head, const void* h, int32_t B, float* scores,
+                                 hipStream_t stream) {
+  ce_status st = check_call(head, h, B, 1, false);
+  if (st != CE_SUCCESS) return st;
+  if (head->dtype != CE_BF16) return fail(CE_ERR_BAD_DTYPE, "the MFMA projection takes bf16 heads only");
+  if (B == 0) return CE_SUCCESS;
+  if (!scores) return fail(CE_ERR_NULL_POINTER, "scores is NULL");
+  if (!aligned(h, 16) || !aligned(scores, 4)) return fail(CE_ERR_MISALIGNED, "h needs 16-byte alignment");
+  for (int b0 = 0; b0 < B; b0 += ce::kPassRows) {
+    ce::PassArgs a = base_args(head, 1);
+    a.B = std::min(ce::kPassRows, B - b0);
+    a.h = static_cast<const char*>(h) + (size_t)b0 * (size_t)head->d * elem_bytes(head->dtype);
+    a.S = scores + (size_t)b0 * head->Nc;
+    a.ldS = head->Nc;
+    a.approx = true;
+    hipError_t e = ce::launch_scores(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  }
   return CE_SUCCESS;
 }
 

@@ -27,7 +27,24 @@ struct Tables {
   int slab;                    // 0: the head's dtype; 1: E4M3 codes (16 per vector)
   const float* escale;         // E4M3 slabs: [n_tiles][64] row scales
   const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
+  // [0] the largest centroid row norm (bits of a double, rounded up);
+  // [1] rows whose top-K band was recomputed in canonical keys,
+  // [2] rows recomputed whole (both counted since prepare, atomically)
+  unsigned long long* stats;
 };
+
+// Argmax slots: a row's packed (ordered logit, ~token) maxima sit in
+// kArgSlots words kArgSlotStride words (16 KiB) apart, rows kArgRowStride
+// words (256 B) apart inside a slot's block; a gather wave max-es into the
+// slot of its index mod kArgSlots and the finalize takes the largest.
+// Device-scope atomics on one address serialise, and on neighbouring words
+// share a memory channel; the spread slots keep thousands of them per call
+// from queueing on one.
+constexpr int kArgSlots = 8;
+constexpr int kArgRowStride = 32;
+constexpr int kArgSlotStride = kPassRows * kArgRowStride;
+constexpr size_t kArgWords = (size_t)(kPassRows - 1) * kArgRowStride +
+                             (size_t)(kArgSlots - 1) * kArgSlotStride + 1;
 
 enum GatherMode { kArgmax = 0, kMasked = 1, kTopM = 2 };
 constexpr int kMaxTopM = 32;        // m of the fused top-m
@@ -47,13 +64,15 @@ struct PassArgs {
   const void* E;          // [V][d] ordered layout
   Tables t;
   const void* h;          // [B][d] rows of this pass
+  bool approx;            // bf16 MFMA projection + certified top-K (else canonical scores)
   // workspace regions
   float* S;               // [B][ldS] centroid scores
   int ldS;
   int32_t* topk;          // [B][ldK] selected centroids
   int ldK;
   unsigned long long* cl_sel;   // [ceil(Nc/64)][kPassRows] bit i of word (w, b): row b selected 64w+i
-  unsigned long long* best;     // [kPassRows] packed (ordered logit, ~token)
+  unsigned long long* best;     // [kPassRows] top-m counters (segments << 32 | keys)
+  unsigned long long* amax;     // [kArgWords] argmax slots (see kArgSlots)
   // fused top-m: per row, a packed count (segments << 32 | keys) in `best`,
   // the tiles' local top-m keys and each tile segment's head key
   int m;
@@ -90,6 +109,9 @@ hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint
 // Quantise bf16 rows to E4M3 with row scales and pack them the same way.
 hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* tiles,
                            const int32_t* offsets, void* out, float* scale, hipStream_t s);
+// Largest row norm of C [Nc][d] into *out (zeroed by the caller).
+hipError_t launch_cnorm_max(const void* C, int dtype, int Nc, int d, unsigned long long* out,
+                            hipStream_t s);
 hipError_t launch_scores(const PassArgs& a, hipStream_t s);
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: TopkMode
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);

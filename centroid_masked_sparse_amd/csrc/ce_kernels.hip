@@ -129,6 +129,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (a key of -0 does not occur: order_key maps it to +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // ------------------------------------------------------------------ packing
 
 // Pack rows of W ([rows][d] row-major) into 64-row tiles [t][v][lane].
@@ -707,6 +712,125 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   }
 }
 
+// ------------------------------------------------------------------ approximate scores (MFMA)
+
+// bf16 operands of v_mfma_f32_16x16x32_bf16 and its fp32 accumulator.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Approximate centroid scores of a bf16 head, for the certified top-K:
+// S~[b][c] = sum_k h[b][k] C[c][k] accumulated by the matrix cores in fp32,
+// whatever their internal order.  One wave per (16 MB centroids, 16 rows):
+// per k-step of 32 the A operands are MB blocks of 16 centroid rows (lane l:
+// row l%16, elements 8(l/16) .. +7, one 16-byte vector of the packed tile)
+// and the B operand 16 hidden rows the same way; lane l ends with
+// D[4(l/16) + i][l%16], the scores of centroids 4(l/16) + i of each block
+// for hidden row l%16.  With `fill` (forward) the extra grid rows stream
+// -inf over the output rows, as in scores_kernel.
+template <int MB, int NKS>
+__global__ __launch_bounds__(64) void proj_mfma_kernel(const v4u* __restrict__ CT, int Nc, int d,
+                                                       const uint16_t* __restrict__ h, int B,
+                                                       float* __restrict__ S, int ldS,
+                                                       float* __restrict__ fill, int V) {
+  const int lane = threadIdx.x;
+  const int ngroups = (B + 15) / 16;
+  if ((int)blockIdx.y >= ngroups) {
+    fill_share(fill, (long)B * V, (long)(blockIdx.y - ngroups) * gridDim.x + blockIdx.x,
+               (long)(gridDim.y - ngroups) * gridDim.x);
+    return;
+  }
+  const int r = lane & 15, kq = lane >> 4;
+  const int c0 = blockIdx.x * 16 * MB;
+  const int row0 = blockIdx.y * 16;
+  const int nks = NKS > 0 ? NKS : d / 32;
+  const int nvec = d / 8;
+  // unconditional loads: hidden rows past B repeat row B-1, and centroid
+  // rows past Nc read the packed tiles' zero padding
+  const v4u* hp = reinterpret_cast<const v4u*>(h + (long)min(row0 + r, B - 1) * d) + kq;
+  const v4u* cp[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int c = c0 + 16 * m + r;
+    cp[m] = CT + ((long)(c / kTileTokens) * nvec + kq) * kWave + (c % kTileTokens);
+  }
+  v4f acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+  // groups of G k-steps in a ring of two register stages: the next group's
+  // loads are in flight while a group's MFMAs run (clamped, so
+  // unconditional; the MFMAs of steps past the end are skipped)
+  constexpr int G = 4;
+  struct Stage {
+    v4u b[G], a[G][MB];
+  };
+  auto load = [&](Stage& st, int s0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int s = min(s0 + j, nks - 1);
+      st.b[j] = hp[4 * s];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) st.a[j][m] = cp[m][(long)4 * s * kWave];
+    }
+  };
+  auto run = [&](const Stage& st, int s0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (s0 + j < nks) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, st.a[j][m]),
+                                                           __builtin_bit_cast(v8bf, st.b[j]),
+                                                           acc[m], 0, 0, 0);
+      }
+    }
+  };
+  Stage st0, st1;
+  load(st0, 0);
+  if (nks > G) load(st1, G);
+#pragma unroll
+  for (int s0 = 0; s0 < nks; s0 += 2 * G) {
+    run(st0, s0);
+    if (s0 + 2 * G < nks) load(st0, s0 + 2 * G);
+    if (s0 + G < nks) {
+      run(st1, s0 + G);
+      if (s0 + 3 * G < nks) load(st1, s0 + 3 * G);
+    }
+  }
+  const int row = row0 + r;
+  if (row < B) {
+    float* out = S + (long)row * ldS;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int c = c0 + 16 * m + 4 * kq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (c + i < Nc) out[c + i] = acc[m][i];
+    }
+  }
+}
+
+// Largest row norm of the centroids, rounded up, max-ed into *out as the
+// bits of a positive double (ordered like unsigned integers); *out starts
+// at 0.  The row's sum of squares is a float64 chain (relative error below
+// d 2^-53), and the square root is scaled by 1 + 2^-40, which covers it.
+template <typename T>
+__global__ __launch_bounds__(256) void cnorm_max_kernel(const T* __restrict__ C, int Nc, int d,
+                                                        unsigned long long* __restrict__ out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  double ss = 0.0;
+  if (c < Nc) {
+    for (int k = 0; k < d; ++k) {
+      double x;
+      if constexpr (std::is_same<T, uint16_t>::value) x = (double)__uint_as_float((uint32_t)C[(long)c * d + k] << 16);
+      else x = (double)C[(long)c * d + k];
+      ss = fma(x, x, ss);
+    }
+  }
+  const double n = sqrt(ss) * (1.0 + 0x1p-40);
+  const unsigned long long bits = __ockl_wfred_max_u64((unsigned long long)__double_as_longlong(n));
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(out, bits);
+}
+
 // ------------------------------------------------------------------ top-K
 
 // Threads of a top-K (and top-m merge) workgroup: 512 measured faster than
@@ -714,6 +838,7 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
 // 38.4): more waves shorten the per-thread passes until barriers dominate.
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
+static_assert(kMaxNc <= 16 * kTopkThreads, "a top-K thread holds at most 16 keys");
 constexpr int kCandCap = 1024;   // candidate keys kept for the exact select
 
 // Lanes of the wave below this one whose bit is set in `m`.
@@ -796,9 +921,19 @@ struct TopkArgs {
   int32_t* out;                    // [rows][ldK] ascending ids
   int ldK;
   unsigned long long* cl_sel;      // [ceil(Nc/64)][64]: bit i of word (w, b) = row b selected 64w+i
-  unsigned long long* best;        // [64] argmax slots, cleared per row (or null)
+  unsigned long long* best;        // [64] top-m counters, cleared per row (or null)
+  unsigned long long* amax;        // argmax slots (kArgSlots per row), cleared per row (or null)
   int16_t* rank;                   // [rows][ldR] output position of each selected id (RANK)
   int ldR;
+  // approximate scores (APPROX): S holds the matrix cores' fp32 sums, each
+  // within E of its canonical key (E from the row's norm and the largest
+  // centroid norm); canonical keys are recomputed from h and the packed
+  // centroids where the bound leaves the selection open
+  const uint16_t* h;               // [rows][d] bf16 hidden rows
+  const v4u* CT;                   // packed centroids [ceil(Nc/64)][d/8][64]
+  int d;
+  const unsigned long long* cmax;  // largest centroid row norm (bits of a double)
+  unsigned long long* stats;       // [0] rows whose band was recomputed, [1] rows recomputed whole
 };
 
 // Number of the values vals[0..n) (LDS, read as broadcasts; n a multiple
@@ -821,6 +956,124 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* vals, int n, uin
   }
   return (c0 + c1) + (c2 + c3);
 }
+
+// Exponent of the last significant bit of a bf16 value (nonzero): its
+// integer significand is a multiple of 2^this.
+__device__ __forceinline__ int bf16_lsb_exp(uint32_t bits) {
+  const int e = (int)((bits >> 7) & 0xFFu);
+  return e == 0 ? -133 : e - 134;
+}
+
+// The canonical key of centroid c (order_key of the canonical dot with the
+// bf16 row in LDS), by one whole wave; every lane returns it.  Lane l takes
+// the row's 16-byte vectors l and l + 64 of each pass of 128 (one load round
+// trip per pass; a single pass up to d = 1024).  Every product is exact in
+// float64 and a multiple of 2^q, q the smallest exponent of a product's last
+// significant bit; when the sum of their magnitudes is below 2^(q+53),
+// every partial sum in any order is a multiple of 2^q below 2^(q+53), so
+// exact: the sequential chain then equals the exact sum, which the wave adds
+// in parallel.  Otherwise the chain runs in hidden-dimension order, each
+// vector broadcast from its lane.
+__device__ uint32_t wave_canonical_key(int c, const uint16_t* hl, const v4u* __restrict__ CT, int d) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nvec = d / 8;
+  const v4u* row = CT + (long)(c / kTileTokens) * nvec * kWave + (c % kTileTokens);
+  auto prod = [&](const v4u& hv, const v4u& cv, int e) {
+    const uint32_t hb = (hv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    const uint32_t cb = (cv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    return (double)__uint_as_float(hb << 16) * (double)__uint_as_float(cb << 16);
+  };
+  double part = 0.0, mag = 0.0;
+  int q = 0x7FFFFFFF;
+#pragma unroll 1
+  for (int v0 = 0; v0 < nvec; v0 += 2 * kWave) {
+    v4u cv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) cv[j] = row[(long)min(v0 + lane + kWave * j, nvec - 1) * kWave];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int v = v0 + lane + kWave * j;
+      if (v < nvec) {
+        const v4u hv = *reinterpret_cast<const v4u*>(hl + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double p = prod(hv, cv[j], e);
+          if (p != 0.0) {
+            const uint32_t hb = (hv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t cb = (cv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            part += p;
+            mag += fabs(p);
+            q = min(q, bf16_lsb_exp(hb) + bf16_lsb_exp(cb));
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    part += __shfl_xor(part, o);
+    mag += __shfl_xor(mag, o);
+    q = min(q, __shfl_xor(q, o));
+  }
+  // every lane holds the same sums now (a butterfly), so the test is uniform
+  if (q == 0x7FFFFFFF || mag * (1.0 + 0x1p-30) < ldexp(1.0, q + 53)) return order_key(canon(part));
+  double acc = 0.0;
+#pragma unroll 4
+  for (int v = 0; v < nvec; ++v) {
+    const v4u cv = row[(long)v * kWave];   // the same address in every lane
+    const v4u hv = *reinterpret_cast<const v4u*>(hl + 8 * v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fma((double)__uint_as_float(((hv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16),
+                                          (double)__uint_as_float(((cv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16), acc);
+  }
+  return order_key(canon(acc));
+}
+
+// Canonical keys of this thread's centroids first + i for the bits i of
+// `mask`: the float64 chain over k in order from +0.0 (every product exact),
+// rounded once to fp32; the masked chains run interleaved, with 16 vectors
+// in flight.  For recomputing a whole row.
+template <int EPT>
+__device__ __forceinline__ void canonical_keys(uint32_t (&key)[EPT], uint32_t mask, int first,
+                                               const uint16_t* hrow, const v4u* __restrict__ CT,
+                                               int d) {
+  if (!mask) return;
+  const int nvec = d / 8;
+  const v4u* base = CT + (long)(first / kTileTokens) * nvec * kWave + (first % kTileTokens);
+  double acc[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) acc[i] = 0.0;
+  // 16 vectors in flight per thread (64 VGPRs); nvec is a multiple of 8
+  constexpr int kAhead = EPT >= 16 ? 1 : EPT >= 8 ? 2 : EPT >= 4 ? 4 : 8;
+  for (int v0 = 0; v0 < nvec; v0 += kAhead) {
+    v4u w[EPT][kAhead];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u)
+        if (mask & (1u << i)) w[i][u] = base[(long)(v0 + u) * kWave + i];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const v4u hv = *reinterpret_cast<const v4u*>(hrow + 8 * (v0 + u));
+      double hx[8];
+      widen(hv, hx, uint16_t());
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        if (mask & (1u << i)) {
+          double x[8];
+          widen(w[i][u], x, uint16_t());
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i] = fma(hx[j], x[j], acc[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i)
+    if (mask & (1u << i)) key[i] = order_key(canon(acc[i]));
+}
+
+constexpr int kRepairCap = 512;   // band keys recomputed in one row (else the whole row)
 
 // One workgroup of kTopkThreads (8 waves) per row; thread t holds centroids
 // [t*EPT, t*EPT+EPT), so thread order is id order.  The K-th largest value
@@ -845,7 +1098,20 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* vals, int n, uin
 // Rows with more than kCandCap keys >= mu (K > 512 on large rows, or masses
 // of equal scores) fall back to a bit-serial select over all keys with one
 // barrier per bit.  K >= Nc keeps every centroid.
-template <int EPT, int MODE, bool RANK = false>
+//
+// APPROX: the scores are the matrix cores' fp32 sums S~, each within E of
+// its canonical key (E = beta A (1 + 2^-8) + 2^-23 (max|S~| + beta A) +
+// d 2^-125, A = |h| max_c |C_c| >= sum_k |h_k C_ck|, beta = d 2^-23: each
+// instruction adds 32 exact products and the accumulator with at most 32
+// roundings or truncations of fp32 precision).  With T~ the K-th largest S~,
+// every centroid with S~ > T~ + 2E is in the top K (at most K - 2 others
+// can reach its key) and every one with S~ < T~ - 2E is out (K centroids
+// have keys above it); the band between them fills the remaining places by
+// canonical keys, recomputed in this workgroup only when the band holds more
+// centroids than places.  A non-finite S~ or E, more than kCandCap keys >= mu,
+// or more than kRepairCap keys in the band recompute the whole row's keys
+// and select on them.
+template <int EPT, int MODE, bool RANK = false, bool APPROX = false>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   static_assert(EPT >= 1 && EPT <= 32 && kWave % EPT == 0, "per-thread keys");
   __shared__ __attribute__((aligned(16))) uint32_t cand[kCandCap + kCountBlock];
@@ -855,6 +1121,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t part[2][kTopkWaves];
   __shared__ uint32_t scan_sh[kTopkWaves];
   __shared__ uint32_t ncand;
+  extern __shared__ __attribute__((aligned(16))) unsigned char topk_dyn[];   // APPROX: h row, band list
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -870,42 +1137,118 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const int c = first + i;
     v[i] = row[c < Nc ? c : Nc - 1];   // unconditional (clamped) loads
   }
+  // APPROX: the largest centroid norm and the hidden row (into LDS, with
+  // its squared norm), loaded beside the scores
+  unsigned long long cmax_bits = 0;
+  double ss = 0.0;
+  uint16_t* hrow = reinterpret_cast<uint16_t*>(topk_dyn);
+  if constexpr (APPROX) {
+    cmax_bits = *a.cmax;
+#pragma unroll 1
+    for (int k = tid; k < a.d; k += kTopkThreads) {
+      const uint16_t x = a.h[(long)b * a.d + k];
+      hrow[k] = x;
+      const double f = (double)__uint_as_float((uint32_t)x << 16);
+      ss = fma(f, f, ss);
+    }
+  }
   const int nwords = (Nc + kWave - 1) / kWave;
   if (MODE >= kSelMark)
     for (int w = tid; w < nwords; w += kTopkThreads) words[w] = 0ull;
-  if (tid == 0) ncand = 0;
 
   uint32_t key[EPT];
-  uint32_t valid = 0, m = 0;
+  uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const int c = first + i;
     pin(v[i]);
     key[i] = c < Nc ? order_key(v[i]) : 0u;
     valid |= (c < Nc ? 1u : 0u) << i;
-    m = max(m, key[i]);
   }
 
-  const bool take_all = K >= (uint32_t)Nc;
-  wmax[tid] = m;
-  __syncthreads();
-  uint32_t mu = 0;
-  const uint32_t Kw = (K + kTopkWaves - 1) / kTopkWaves;
-  if (!take_all && Kw <= (uint32_t)kWave) {
-    // smallest wave maximum with fewer than Kw wave maxima above it (0, a
-    // valid bound, when the wave holds fewer than Kw keys)
-    const uint32_t above = count_above(wmax + wv * kWave, kWave, m);
-    mu = __ockl_wfred_min_u32(above < Kw ? m : 0xFFFFFFFFu);
-  }
-  if (lane == 0) wred[wv] = mu;
-  __syncthreads();
-  mu = wred[0];
+  bool exact = !APPROX;   // keys are canonical
+  bool recompute = false;  // recompute every key of the row (next round)
+  double E = 0.0;
+  unsigned long long* band = reinterpret_cast<unsigned long long*>(topk_dyn + 2 * (size_t)a.d);
+  __shared__ double dsh[kTopkWaves];
+  if constexpr (APPROX) {
+    // per wave: the row's squared norm, the largest |S~| and whether an S~
+    // is not finite; the waves' values are combined after the first barrier
+    // of the selection
 #pragma unroll
-  for (int i = 1; i < kTopkWaves; ++i) mu = min(mu, wred[i]);
+    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    uint32_t mx = 0, bad = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if (valid & (1u << i)) {
+        const uint32_t u = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+        bad |= u >= 0x7F800000u ? 1u : 0u;
+        mx = max(mx, u);
+      }
+    mx = __ockl_wfred_max_u32(mx);
+    bad = __ockl_wfred_max_u32(bad);
+    if (lane == 0) {
+      dsh[wv] = ss;
+      part[0][wv] = mx;
+      part[1][wv] = bad;
+    }
+  }
 
   uint32_t sel = valid, pos = 0, tot;
   bool placed = false;   // pos already known
-  if (!take_all) {
+  const bool take_all = K >= (uint32_t)Nc;
+  for (int round = 0; round < 2 && !take_all; ++round) {
+    if (APPROX && recompute) {
+      // the one place that recomputes a whole row's keys (rare: a
+      // non-finite sum, masses of near-equal scores)
+      canonical_keys<EPT>(key, valid, first, hrow, a.CT, a.d);
+      exact = true;
+      recompute = false;
+      if (tid == 0) atomicAdd(&a.stats[1], 1ull);
+    }
+    // 1. threshold
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) m = max(m, key[i]);
+    if (tid == 0) ncand = 0;
+    wmax[tid] = m;
+    __syncthreads();
+    uint32_t mu = 0;
+    const uint32_t Kw = (K + kTopkWaves - 1) / kTopkWaves;
+    if (Kw <= (uint32_t)kWave) {
+      // smallest wave maximum with fewer than Kw wave maxima above it (0, a
+      // valid bound, when the wave holds fewer than Kw keys)
+      const uint32_t above = count_above(wmax + wv * kWave, kWave, m);
+      mu = __ockl_wfred_min_u32(above < Kw ? m : 0xFFFFFFFFu);
+    }
+    if (lane == 0) wred[wv] = mu;
+    __syncthreads();
+    mu = wred[0];
+#pragma unroll
+    for (int i = 1; i < kTopkWaves; ++i) mu = min(mu, wred[i]);
+    if (APPROX && round == 0) {
+      // E from the waves' values (published by the barriers above); a
+      // non-finite S~ or E recomputes the row's keys
+      double ss = 0.0;
+      uint32_t mxa = 0, bada = 0;
+#pragma unroll
+      for (int i = 0; i < kTopkWaves; ++i) {
+        ss += dsh[i];
+        mxa = max(mxa, part[0][i]);
+        bada |= part[1][i];
+      }
+      const double cmax = __longlong_as_double((long long)cmax_bits);
+      const double beta = (double)a.d * 0x1p-23;
+      const double A = sqrt(ss) * (1.0 + 0x1p-40) * cmax;
+      E = beta * A * (1.0 + 0x1p-8) + 0x1p-23 * ((double)__uint_as_float(mxa) + beta * A) +
+          (double)a.d * 0x1p-125;
+      if (bada || !(E < 1e300)) {
+        recompute = true;
+        __syncthreads();
+        continue;
+      }
+    }
+
     // 2. candidates: the keys >= mu, in any order
     uint32_t wtotal = 0;
 #pragma unroll
@@ -923,6 +1266,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
     __syncthreads();
     const int n = (int)ncand;
+    if (n > kCandCap && !exact) {
+      recompute = true;
+      __syncthreads();
+      continue;
+    }
     if (n <= kCandCap) {
       uint32_t T;
       if (n <= kTopkThreads) {
@@ -942,6 +1290,61 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         uint32_t quota, copies;
         if (n <= 8 * kWave) T = cand_kth<8>(cand, n, K, &quota, &copies);
         else T = cand_kth<16>(cand, n, K, &quota, &copies);
+      }
+      if (!exact) {
+        // 3'. the band [T~ - 2E, T~ + 2E], rounded outward to fp32 keys
+        const double tv = (double)key_value(T);
+        float lo = (float)(tv - 2.0 * E), hi = (float)(tv + 2.0 * E);
+        if ((double)lo > tv - 2.0 * E) lo = nextafterf(lo, -__builtin_inff());
+        if ((double)hi < tv + 2.0 * E) hi = nextafterf(hi, __builtin_inff());
+        const uint32_t klo = order_key(lo), khi = order_key(hi);
+        uint32_t gt = 0, inb = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          gt |= (key[i] > khi ? 1u : 0u) << i;
+          inb |= (key[i] != 0u && key[i] >= klo && key[i] <= khi ? 1u : 0u) << i;
+        }
+        const uint32_t ex =
+            block_excl_scan(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(inb), scan_sh, &tot);
+        const uint32_t need = K - (tot >> 16), nb = tot & 0xFFFFu;
+        if (nb == need) {
+          // the band holds exactly the open places: no key is recomputed
+          sel = gt | inb;
+          pos = (ex >> 16) + (ex & 0xFFFFu);
+          placed = true;
+          break;
+        }
+        if (nb > (uint32_t)kRepairCap) {
+          recompute = true;
+          __syncthreads();
+          continue;
+        }
+        // canonical keys of the band (one wave per centroid), ranked by
+        // (key desc, id asc); the `need` best take the open places
+        uint32_t at = ex & 0xFFFFu;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+          if (inb & (1u << i)) band[at++] = (unsigned long long)(first + i);
+        __syncthreads();
+        for (uint32_t j = wv; j < nb; j += kTopkWaves) {
+          const int c = (int)band[j];
+          const uint32_t ck = wave_canonical_key(c, hrow, a.CT, a.d);
+          if (lane == 0) band[j] = ((unsigned long long)ck << 32) | (0xFFFFFFFFu - (uint32_t)c);
+        }
+        __syncthreads();
+        uint32_t keep = 0;
+        at = ex & 0xFFFFu;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+          if (inb & (1u << i)) {
+            const unsigned long long pk = band[at++];
+            uint32_t above = 0;
+            for (uint32_t j = 0; j < nb; ++j) above += band[j] > pk ? 1u : 0u;
+            if (above < need) keep |= 1u << i;
+          }
+        sel = gt | keep;
+        if (tid == 0) atomicAdd(&a.stats[0], 1ull);
+        break;
       }
       // 3. keys > T, then copies of T up to K in id order
       uint32_t gt = 0, eq = 0;
@@ -999,6 +1402,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       }
       sel = s;
     }
+    break;
   }
   if (!placed) pos = block_excl_scan((uint32_t)__popc(sel), scan_sh, &tot);
 
@@ -1012,11 +1416,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
 
   if (MODE >= kSelMark) {
+    if (take_all) __syncthreads();   // words[] cleared before any bit is set (else the rounds' barriers order it)
     if (sel) atomicOr(&words[first / kWave], (unsigned long long)sel << (first % kWave));
     __syncthreads();
     for (int w = tid; w < nwords; w += kTopkThreads) a.cl_sel[(long)w * kWave + b] = words[w];
   }
   if (MODE == kSelMark && a.best && tid == 0) a.best[b] = 0ull;
+  if (MODE == kSelMark && a.amax && tid < kArgSlots) a.amax[b * kArgRowStride + tid * kArgSlotStride] = 0ull;
 }
 
 // ------------------------------------------------------------------ gather
@@ -1038,8 +1444,8 @@ struct GatherArgs {
   int ldK, K;
   int by_row;
   const float* escale;          // FP8 slabs: [n_tiles][64] row scales
-  unsigned long long* best;     // argmax: [64] packed (ordered logit, ~token) per row;
-                                // top-m: [64] packed (segments << 32 | keys) per row
+  unsigned long long* best;     // top-m: [64] packed (segments << 32 | keys) per row
+  unsigned long long* amax;     // argmax: packed (ordered logit, ~token) slots (kArgSlots per row)
   float* out;                   // forward: [B][V] output rows (already -inf)
   int V;
   int m;                        // top-m
@@ -1151,7 +1557,9 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
           if (tok >= 0)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           k = wave_max_u64(k);
-          if (lane == 0) atomicMax(&a.best[rows[r]], k);   // result unused: no stall
+          // result unused: no stall; one of the row's slots, by wave index
+          if (lane == 0)
+            atomicMax(&a.amax[rows[r] * kArgRowStride + (int)(blockIdx.x % kArgSlots) * kArgSlotStride], k);
         } else if (MODE == kMasked) {
           if (tok >= 0) a.out[(long)rows[r] * a.V + tok] = f;
         } else {
@@ -1204,13 +1612,24 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   }
 }
 
+// A row's packed (ordered logit, ~token) maximum over its argmax slots.
+__device__ __forceinline__ unsigned long long row_best(const unsigned long long* __restrict__ amax, int b) {
+  unsigned long long v[kArgSlots];
+#pragma unroll
+  for (int s = 0; s < kArgSlots; ++s) v[s] = amax[b * kArgRowStride + s * kArgSlotStride];
+  unsigned long long m = v[0];
+#pragma unroll
+  for (int s = 1; s < kArgSlots; ++s) m = max(m, v[s]);
+  return m;
+}
+
 // Decode each row's packed (ordered logit, ~token) maximum; 0 means no
 // candidate at all.
-__global__ __launch_bounds__(64) void finalize_kernel(const unsigned long long* __restrict__ best,
+__global__ __launch_bounds__(64) void finalize_kernel(const unsigned long long* __restrict__ amax,
                                                       int B, int32_t* __restrict__ tokens) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) {
-    const unsigned long long v = best[b];
+    const unsigned long long v = row_best(amax, b);
     tokens[b] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
   }
 }
@@ -1245,9 +1664,9 @@ __device__ __forceinline__ v4u scale_vec(v4u v, float n, float) {
 
 template <typename T>
 __global__ __launch_bounds__(kEmbedThreads) void finalize_embed_kernel(
-    const unsigned long long* __restrict__ best, int32_t* __restrict__ tokens, EmbedArgs e) {
+    const unsigned long long* __restrict__ amax, int32_t* __restrict__ tokens, EmbedArgs e) {
   const int b = blockIdx.x;
-  const unsigned long long v = best[b];
+  const unsigned long long v = row_best(amax, b);
   const int tok = v ? (int)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull)) : -1;
   if (threadIdx.x == 0) tokens[b] = tok;
   const int nvec = e.dim / Elem<T>::kPerVec;
@@ -1272,10 +1691,6 @@ struct TopmArgs {
   float* logits;                    // [B][m]
 };
 
-// Inverse of order_key (the canonical logits carry no -0).
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 // One workgroup of kTopkThreads per row.  Each gather segment holds one
 // tile's keys for the row (zeros where a slot has no token) and its head is
@@ -1376,6 +1791,18 @@ hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint
   return hipGetLastError();
 }
 
+hipError_t launch_cnorm_max(const void* C, int dtype, int Nc, int d, unsigned long long* out,
+                            hipStream_t s) {
+  const dim3 grid((Nc + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(cnorm_max_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(C), Nc, d, out);
+  else
+    hipLaunchKernelGGL(cnorm_max_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(C),
+                       Nc, d, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* tiles,
                            const int32_t* offsets, void* out, float* scale, hipStream_t s) {
   const long n_rows_out = n_tiles * kTileTokens;
@@ -1433,7 +1860,28 @@ static void launch_scores_t(const PassArgs& a, hipStream_t s) {
 // 36.7).  Two rows per wave (the tile widened once for both) only for the
 // forward at 48 rows or more, where the grid also holds the fill waves
 // (B=64: 55.2 with one row against 54.4).
+// MFMA blocks of 16 centroids per wave of the approximate projection.
+constexpr int kProjMB = 1;
+
+template <int NKS>
+static void launch_proj_n(const PassArgs& a, hipStream_t s) {
+  const int gx = (a.Nc + 16 * kProjMB - 1) / (16 * kProjMB);
+  const dim3 grid(gx, (a.B + 15) / 16 + fill_grid_rows(a, gx));
+  hipLaunchKernelGGL((proj_mfma_kernel<kProjMB, NKS>), grid, dim3(64), 0, s,
+                     static_cast<const v4u*>(a.t.CT), a.Nc, a.d, static_cast<const uint16_t*>(a.h),
+                     a.B, a.S, a.ldS, a.fill, a.V);
+}
+
 hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
+  if (a.approx) {
+    switch (a.d / 32) {
+      case 8: launch_proj_n<8>(a, s); break;
+      case 16: launch_proj_n<16>(a, s); break;
+      case 32: launch_proj_n<32>(a, s); break;
+      default: launch_proj_n<0>(a, s); break;
+    }
+    return hipGetLastError();
+  }
   const bool two = a.fill != nullptr && a.B >= 48;
   if (a.dtype == 1) {
     if (two) launch_scores_t<uint16_t, 2>(a, s); else launch_scores_t<uint16_t, 1>(a, s);
@@ -1444,11 +1892,16 @@ hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
 }
 
 template <int EPT>
-static void launch_topk_ept(const TopkArgs& t, int B, int mode, hipStream_t s) {
+static void launch_topk_ept(const TopkArgs& t, int B, int mode, bool approx, hipStream_t s) {
   // the ranks (top-m on equal clusters) come from their own instantiation,
   // so the other calls' kernel carries none of their stores
+  const size_t lds = (size_t)2 * t.d + sizeof(unsigned long long) * kRepairCap;
   if (mode == kTopkOnly)
     hipLaunchKernelGGL((topk_kernel<EPT, kSelIds>), dim3(B), dim3(kTopkThreads), 0, s, t);
+  else if (approx && t.rank)
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true, true>), dim3(B), dim3(kTopkThreads), lds, s, t);
+  else if (approx)
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, false, true>), dim3(B), dim3(kTopkThreads), lds, s, t);
   else if (t.rank)
     hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true>), dim3(B), dim3(kTopkThreads), 0, s, t);
   else
@@ -1465,15 +1918,21 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.ldK = a.ldK;
   t.cl_sel = a.cl_sel;
   t.best = a.best;
+  t.amax = a.amax;
   t.rank = a.tm_rank;
   t.ldR = a.ldR;
+  t.h = static_cast<const uint16_t*>(a.h);
+  t.CT = static_cast<const v4u*>(a.t.CT);
+  t.d = a.d;
+  t.cmax = a.t.stats;
+  t.stats = a.t.stats + 1;
+  const bool approx = a.approx && mode != kTopkOnly;
   const int ept = (a.Nc + kTopkThreads - 1) / kTopkThreads;
-  if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, s);
-  else if (ept <= 2) launch_topk_ept<2>(t, a.B, mode, s);
-  else if (ept <= 4) launch_topk_ept<4>(t, a.B, mode, s);
-  else if (ept <= 8) launch_topk_ept<8>(t, a.B, mode, s);
-  else if (ept <= 16) launch_topk_ept<16>(t, a.B, mode, s);
-  else launch_topk_ept<32>(t, a.B, mode, s);
+  if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, approx, s);
+  else if (ept <= 2) launch_topk_ept<2>(t, a.B, mode, approx, s);
+  else if (ept <= 4) launch_topk_ept<4>(t, a.B, mode, approx, s);
+  else if (ept <= 8) launch_topk_ept<8>(t, a.B, mode, approx, s);
+  else launch_topk_ept<16>(t, a.B, mode, approx, s);   // Nc <= kMaxNc: at most 16 keys a thread
   return hipGetLastError();
 }
 
@@ -1504,6 +1963,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.escale = a.t.escale;
   g.split_shift = gather_split_shift(a.B);
   g.best = a.best;
+  g.amax = a.amax;
   g.out = a.logits;
   g.V = a.V;
   g.m = a.m;
@@ -1607,12 +2067,12 @@ hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {
     EmbedArgs e{a.emb_table, a.emb_dim, a.emb_normalizer, a.emb_out};
     if (a.dtype == 1)
       hipLaunchKernelGGL(finalize_embed_kernel<uint16_t>, dim3(a.B), dim3(kEmbedThreads), 0, s,
-                         a.best, a.tokens, e);
+                         a.amax, a.tokens, e);
     else
       hipLaunchKernelGGL(finalize_embed_kernel<float>, dim3(a.B), dim3(kEmbedThreads), 0, s,
-                         a.best, a.tokens, e);
+                         a.amax, a.tokens, e);
   } else {
-    hipLaunchKernelGGL(finalize_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.best, a.B, a.tokens);
+    hipLaunchKernelGGL(finalize_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.amax, a.B, a.tokens);
   }
   return hipGetLastError();
 }

@@ -92,6 +92,26 @@ typedef enum ce_slab {
   CE_SLAB_FP8_E4M3 = 1
 } ce_slab;
 
+/* Centroid projection of the fused calls (ce_head_desc.projection).  The
+ * results are the same either way; only the time differs.
+ *   CE_PROJ_AUTO   fp32 heads: CE_PROJ_EXACT; bf16 heads: per pass of rows,
+ *                  CE_PROJ_MFMA when B*Nc*d >= 2^27 multiply-adds, where it
+ *                  is the faster, else CE_PROJ_EXACT
+ *   CE_PROJ_EXACT  every centroid score is the canonical key (a float64
+ *                  chain) before the top-K
+ *   CE_PROJ_MFMA   bf16 heads only: the matrix cores' fp32 sums, each within
+ *                  a bound E of its canonical key (from |h| and the largest
+ *                  centroid norm), and a top-K that recomputes canonical keys
+ *                  wherever E leaves the K-th place open, so the selected
+ *                  centroids are exactly those of CE_PROJ_EXACT
+ * ce_score_centroids (whose output is the keys) and ce_draft_step always
+ * compute canonical scores. */
+typedef enum ce_projection {
+  CE_PROJ_AUTO = 0,
+  CE_PROJ_EXACT = 1,
+  CE_PROJ_MFMA = 2
+} ce_projection;
+
 typedef enum ce_op {
   CE_OP_SCORE = 0,          /* ce_score_centroids */
   CE_OP_TOPK = 1,           /* ce_topk */
@@ -123,6 +143,7 @@ typedef struct ce_graph* ce_graph_t;
  *                   Empty clusters are allowed.  Copied at create.
  *   token_of_slot   HOST [V], a permutation of 0..V-1.  Copied at create.
  *   slab_format     ce_slab; CE_SLAB_FP8_E4M3 needs dtype CE_BF16.
+ *   projection      ce_projection; CE_PROJ_MFMA needs dtype CE_BF16.
  * The two device arrays are read only by ce_head_prepare, which packs them
  * into the persistent buffer; they may be freed or changed afterwards. */
 typedef struct ce_head_desc {
@@ -137,6 +158,7 @@ typedef struct ce_head_desc {
   const int32_t* cluster_offsets;
   const int32_t* token_of_slot;
   int32_t slab_format;
+  int32_t projection;
 } ce_head_desc;
 
 /* Validate desc on the host and create a head.  Makes no HIP call.
@@ -369,6 +391,21 @@ ce_status ce_probe_gather_events(hipEvent_t start, hipEvent_t stop);
  * Errors: NULL_POINTER, MISALIGNED (buf or bytes not a multiple of 16), HIP. */
 ce_status ce_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                hipStream_t stream);
+
+/* Measurement: of the rows the fused calls have processed with the MFMA
+ * projection since ce_head_prepare, counts[0] had the K-th place decided by
+ * recomputed canonical keys of the centroids near it, and counts[1] had all
+ * their keys recomputed (non-finite sums, masses of near-equal scores).
+ * Copies two counters from the persistent buffer and synchronises the
+ * device: not for the hot path.  Errors: NULL_POINTER, NOT_PREPARED, HIP. */
+ce_status ce_head_repair_counts(ce_head_t head, uint64_t counts[2]);
+
+/* Measurement probe: the MFMA projection alone, scores[b][c] = the matrix
+ * cores' fp32 sum of h[b] . centroid c (bf16 heads), the approximate scores
+ * whose error bound the certified top-K relies on.  Errors: as
+ * ce_score_centroids, plus BAD_DTYPE for an fp32 head. */
+ce_status ce_probe_approx_scores(ce_head_t head, const void* h, int32_t B, float* scores,
+                                 hipStream_t stream);
 
 /* Short name of a status code.  Never NULL. */
 const char* ce_status_string(ce_status status);

@@ -20,13 +20,14 @@ def to_device(a: np.ndarray, dtype: str):
     return t.to("cuda:0")
 
 
-def make_head(w, max_B: int = 64, max_K: int | None = None):
+def make_head(w, max_B: int = 64, max_K: int | None = None, projection: str = "auto"):
     from centroid_masked_sparse_amd import Head
     C = to_device(w.C, w.dtype)
     E = to_device(w.E, w.dtype)
     equal = np.all(np.diff(w.offsets) == w.V // w.Nc) and w.V % w.Nc == 0
     head = Head(C, E, w.tos, None if equal else w.offsets, max_B=max_B,
-                max_K=max_K if max_K is not None else w.Nc)
+                max_K=max_K if max_K is not None else w.Nc,
+                projection=projection if w.dtype == "bf16" else "auto")
     return head
 
 

@@ -48,13 +48,13 @@ def test_header_symbols_exported(lib):
 
 
 def _desc(d=64, V=256, Nc=4, max_B=8, max_K=4, dtype=_ffi.CE_BF16, tos=None, off=None,
-          c_ptr=FAKE, e_ptr=FAKE, slab=_ffi.CE_SLAB_NATIVE):
+          c_ptr=FAKE, e_ptr=FAKE, slab=_ffi.CE_SLAB_NATIVE, proj=_ffi.CE_PROJ_AUTO):
     tos = np.arange(V, dtype=np.int32) if tos is None else np.asarray(tos, dtype=np.int32)
     keep = [tos]
     desc = _ffi.HeadDesc(d=d, V=V, Nc=Nc, max_B=max_B, max_K=max_K, dtype=dtype,
                          centroids=c_ptr, emb_ordered=e_ptr,
                          token_of_slot=tos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                         slab_format=slab)
+                         slab_format=slab, projection=proj)
     if off is not None:
         off = np.asarray(off, dtype=np.int32)
         keep.append(off)
@@ -90,6 +90,8 @@ ERR = {v: k for k, v in _ffi.STATUS_NAMES.items()}
     (dict(c_ptr=0), "CE_ERR_NULL_POINTER"),
     (dict(slab=2), "CE_ERR_BAD_DTYPE"),
     (dict(slab=_ffi.CE_SLAB_FP8_E4M3, dtype=_ffi.CE_F32), "CE_ERR_BAD_DTYPE"),   # FP8 from bf16 only
+    (dict(proj=3), "CE_ERR_BAD_DTYPE"),
+    (dict(proj=_ffi.CE_PROJ_MFMA, dtype=_ffi.CE_F32), "CE_ERR_BAD_DTYPE"),      # MFMA for bf16 only
 ])
 def test_create_rejects(lib, kw, want):
     desc, _keep = _desc(**kw)
@@ -115,11 +117,12 @@ def test_create_ragged_and_sizes(lib):
     try:
         n = ctypes.c_size_t()
         assert lib.ce_head_persistent_bytes(h, ctypes.byref(n)) == 0
-        # offsets (5 ints) + token_of_slot (V ints) + the tile list (clusters
-        # of 0, 100, 30 and 126 tokens: 0+2+1+2 = 5 words) + the tiles' slot
-        # tokens (5 x 64 ints), each rounded up to 256 bytes, + packed
-        # embeddings (5 tiles) and centroids (1 tile) of 64 rows x 64 bf16
-        assert n.value == 256 + 1024 + 256 + 5 * 256 + 5 * 8192 + 8192
+        # statistics (4 words) + offsets (5 ints) + token_of_slot (V ints) +
+        # the tile list (clusters of 0, 100, 30 and 126 tokens: 0+2+1+2 = 5
+        # words) + the tiles' slot tokens (5 x 64 ints), each rounded up to
+        # 256 bytes, + packed embeddings (5 tiles) and centroids (1 tile) of
+        # 64 rows x 64 bf16
+        assert n.value == 256 + 256 + 1024 + 256 + 5 * 256 + 5 * 8192 + 8192
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOPK, ctypes.byref(n)) == 0
         assert n.value == 0
         sizes = {}
@@ -183,6 +186,10 @@ def test_compute_calls_before_prepare_fail_on_host(lib):
         assert lib.ce_head_prepare(h, FAKE + 16, 1 << 20, None) == ERR["CE_ERR_MISALIGNED"]
         assert lib.ce_head_prepare(h, FAKE, 16, None) == ERR["CE_ERR_WORKSPACE_TOO_SMALL"]
         assert lib.ce_probe_gather_events(None, None) == ERR["CE_ERR_NULL_POINTER"]
+        counts = (ctypes.c_uint64 * 2)()
+        assert lib.ce_head_repair_counts(h, counts) == NP
+        assert lib.ce_head_repair_counts(h, None) == ERR["CE_ERR_NULL_POINTER"]
+        assert lib.ce_probe_approx_scores(h, FAKE, 1, FAKE, None) == NP
     finally:
         assert lib.ce_head_destroy(h) == 0
     assert lib.ce_head_destroy(None) == 0

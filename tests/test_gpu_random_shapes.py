@@ -4,7 +4,8 @@ Each case draws a head (hidden size, vocabulary, centroid count, equal or
 ragged clusters), a top-K and a batch size, so that together the cases pass
 through every launch shape of the path: the by-row gather (up to 4 rows,
 equal clusters), the tile grid, the split grid (48 rows or more), one- and
-two-row projection waves, and batches of several 64-row passes.  Tokens,
+two-row projection waves, both projections (exact and the certified MFMA
+one), and batches of several 64-row passes.  Tokens,
 top-K ids, the forward rows and the top-m must equal the oracle's bit for
 bit.
 """
@@ -40,7 +41,8 @@ def test_random_shape_against_oracle(i):
     d, V, Nc, K, B, ragged = _case(i)
     w = make_random(900 + i, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)
     hb = rows(w, B)
-    head = make_head(w, max_B=B)
+    # odd cases take the certified MFMA projection, even ones the exact one
+    head = make_head(w, max_B=B, projection="mfma" if i % 2 else "exact")
     h = to_device(hb, "bf16")
     tk = torch.full((B, K), -7, dtype=torch.int32, device="cuda:0")
     tok = head.top_tokens(h, K, topk_out=tk)

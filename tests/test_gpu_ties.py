@@ -36,13 +36,14 @@ def _pooled(seed, d, V, Nc, ragged, pool=6):
     return dataclasses.replace(w, E=E, h=h)
 
 
+@pytest.mark.parametrize("proj", ["exact", "mfma"])
 @pytest.mark.parametrize("ragged,B", [(False, 3), (False, 9), (False, 64), (False, 70),
                                       (True, 3), (True, 64)])
-def test_tied_logits_tokens_top_m_and_rows(ragged, B):
+def test_tied_logits_tokens_top_m_and_rows(ragged, B, proj):
     torch = torch_mod()
     w = _pooled(81 + B, d=128, V=16384, Nc=128, ragged=ragged)   # 128 tokens (2 tiles) per cluster
     K, m = 6, 32
-    head = make_head(w, max_B=B, max_K=K)
+    head = make_head(w, max_B=B, max_K=K, projection=proj)
     hB = rows(w, B)
     h = to_device(hB, w.dtype)
     tok_o, sel_o, best_o = oracle.top_tokens(hB, w.C, w.E, w.offsets, w.tos, K, w.dtype)
