@@ -383,11 +383,12 @@ ce_status ce_graph_destroy(ce_graph_t graph);
 ce_status ce_probe_gather_events(hipEvent_t start, hipEvent_t stop);
 
 /* Measurement probe: enqueue on `stream` one kernel that reads every 16-byte
- * vector of the device buffer buf[0, bytes) once (coalesced, grid-stride, four
- * independent loads in flight per thread), the streaming read rate the
- * gather's bandwidth is compared against.  `sink` is a device word the kernel
- * writes only if the XOR of the data equals an improbable pattern; its
- * content is meaningless.  The caller owns both buffers.
+ * vector of the device buffer buf[0, bytes) once (coalesced, grid-stride,
+ * eight independent non-temporal loads in flight per thread: the fastest of
+ * the configurations measured), the streaming read rate the gather's
+ * bandwidth is compared against.  `sink` is a device word the kernel writes
+ * only if the XOR of the data equals an improbable pattern; its content is
+ * meaningless.  The caller owns both buffers.
  * Errors: NULL_POINTER, MISALIGNED (buf or bytes not a multiple of 16), HIP. */
 ce_status ce_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                hipStream_t stream);
