@@ -641,18 +641,27 @@ __device__ __forceinline__ void norm_finish(const NormRegs<T, RB, NCH>& nr, cons
 
 // ------------------------------------------------------------------ scores
 
-// Forward: -inf over out[0..n) ([B][V] rows, contiguous, 16-byte aligned),
-// the share of fill wave f of nfill: runs of 64 float4 (1 KiB per wave
-// store), strided over the fill waves.  Plain streaming stores.
+// Forward: -inf over out[0..n) (16-byte aligned), the share of fill group f
+// of nfill, groups of NT threads: runs of NT float4 (16 B a thread),
+// strided over the groups.  Plain streaming stores.
+template <int NT>
 __device__ __forceinline__ void fill_share(float* __restrict__ out, long n, long f, long nfill) {
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
   const float ninf = -__builtin_inff();
   const long n4 = n / 4;
-  for (long i = f * kWave + lane; i < n4; i += nfill * kWave)
+  for (long i = f * NT + t; i < n4; i += nfill * NT)
     reinterpret_cast<float4*>(out)[i] = make_float4(ninf, ninf, ninf, ninf);
   if (f == 0)
-    for (long i = 4 * n4 + lane; i < n; i += kWave) out[i] = ninf;
+    for (long i = 4 * n4 + t; i < n; i += NT) out[i] = ninf;
 }
+
+// The forward's -inf fill is shared between the projection kernel and the
+// top-K kernel, whose one workgroup per row leaves most CUs idle: the
+// projection's waves fill out[0, fill_split) and extra top-K workgroups the
+// rest.  Both kernels are otherwise latency- or VALU-bound, so each hides
+// its share of the stores.
+constexpr int kFillProjPct = 50;
+__host__ __device__ inline long fill_split(long n) { return (n * kFillProjPct / 100) & ~3l; }
 
 // One wave per (64-centroid tile, RB rows): S[b][c] for the tile's
 // centroids.  With `fill` (forward) the grid has more rows of workgroups
@@ -676,8 +685,8 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
   const int nvalid = min(kTileTokens, Nc - c0);
   const int ngroups = (B + RB - 1) / RB;
   if ((int)blockIdx.y >= ngroups) {
-    fill_share(fill, (long)B * V, (long)(blockIdx.y - ngroups) * gridDim.x + blockIdx.x,
-               (long)(gridDim.y - ngroups) * gridDim.x);
+    fill_share<kWave>(fill, fill_split((long)B * V), (long)(blockIdx.y - ngroups) * gridDim.x + blockIdx.x,
+                      (long)(gridDim.y - ngroups) * gridDim.x);
     return;
   }
   const int nrows = min(RB, B - r0);
@@ -740,8 +749,8 @@ __global__ __launch_bounds__(64) void proj_mfma_kernel(const v4u* __restrict__ C
   const int lane = threadIdx.x;
   const int ngroups = (B + 15) / 16;
   if ((int)blockIdx.y >= ngroups) {
-    fill_share(fill, (long)B * V, (long)(blockIdx.y - ngroups) * gridDim.x + blockIdx.x,
-               (long)(gridDim.y - ngroups) * gridDim.x);
+    fill_share<kWave>(fill, fill_split((long)B * V), (long)(blockIdx.y - ngroups) * gridDim.x + blockIdx.x,
+                      (long)(gridDim.y - ngroups) * gridDim.x);
     return;
   }
   const int r = lane & 15, kq = lane >> 4;
@@ -939,6 +948,10 @@ struct TopkArgs {
   int d;
   const unsigned long long* cmax;  // largest centroid row norm (bits of a double)
   unsigned long long* stats;       // [0] rows whose band was recomputed, [1] rows recomputed whole
+  // forward: workgroups from `rows` on fill out[fill_split(n), n) with -inf
+  int rows;
+  float* fill;
+  long fill_n;
 };
 
 // Number of the values vals[0..n) (LDS, read as broadcasts; n a multiple
@@ -1127,6 +1140,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t scan_sh[kTopkWaves];
   __shared__ uint32_t ncand;
   extern __shared__ __attribute__((aligned(16))) unsigned char topk_dyn[];   // APPROX: h row, band list
+  if ((int)blockIdx.x >= a.rows) {
+    const long from = fill_split(a.fill_n);
+    fill_share<kTopkThreads>(a.fill + from, a.fill_n - from, (long)blockIdx.x - a.rows,
+                             (long)gridDim.x - a.rows);
+    return;
+  }
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -1821,12 +1840,22 @@ hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* t
   return hipGetLastError();
 }
 
-// Fill waves of the forward: about one per 64 KiB of output rows, at least
-// one row of the grid, at most 1024.
+// Fill waves of the forward's projection: about one per 64 KiB of its
+// share of the output rows, at least one row of the grid, at most 1024.
 static int fill_grid_rows(const PassArgs& a, int gx) {
   if (!a.fill) return 0;
-  const long waves = std::min<long>(1024, std::max<long>(1, (long)a.B * a.V * 4 / 65536));
+  const long bytes = fill_split((long)a.B * a.V) * 4;
+  const long waves = std::min<long>(1024, std::max<long>(1, bytes / 65536));
   return (int)std::max<long>(1, (waves + gx - 1) / gx);
+}
+
+// Fill workgroups of the forward's top-K launch (512 threads): about one
+// per 256 KiB of the rest of the rows, at least one, at most 256.
+static int fill_topk_groups(const PassArgs& a) {
+  if (!a.fill) return 0;
+  const long n = (long)a.B * a.V;
+  const long bytes = (n - fill_split(n)) * 4;
+  return (int)std::min<long>(256, std::max<long>(1, bytes / 262144));
 }
 
 template <typename T, int RB, int NCH>
@@ -1898,20 +1927,20 @@ hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
 }
 
 template <int EPT>
-static void launch_topk_ept(const TopkArgs& t, int B, int mode, bool approx, hipStream_t s) {
+static void launch_topk_ept(const TopkArgs& t, int G, int mode, bool approx, hipStream_t s) {
   // the ranks (top-m on equal clusters) come from their own instantiation,
   // so the other calls' kernel carries none of their stores
   const size_t lds = (size_t)2 * t.d + sizeof(unsigned long long) * kRepairCap;
   if (mode == kTopkOnly)
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelIds>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelIds>), dim3(G), dim3(kTopkThreads), 0, s, t);
   else if (approx && t.rank)
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true, true>), dim3(B), dim3(kTopkThreads), lds, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true, true>), dim3(G), dim3(kTopkThreads), lds, s, t);
   else if (approx)
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, false, true>), dim3(B), dim3(kTopkThreads), lds, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, false, true>), dim3(G), dim3(kTopkThreads), lds, s, t);
   else if (t.rank)
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark, true>), dim3(G), dim3(kTopkThreads), 0, s, t);
   else
-    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark>), dim3(B), dim3(kTopkThreads), 0, s, t);
+    hipLaunchKernelGGL((topk_kernel<EPT, kSelMark>), dim3(G), dim3(kTopkThreads), 0, s, t);
 }
 
 hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
@@ -1932,13 +1961,17 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.d = a.d;
   t.cmax = a.t.stats;
   t.stats = a.t.stats + 1;
+  t.rows = a.B;
+  t.fill = a.fill;
+  t.fill_n = (long)a.B * a.V;
+  const int G = a.B + fill_topk_groups(a);
   const bool approx = a.approx && mode != kTopkOnly;
   const int ept = (a.Nc + kTopkThreads - 1) / kTopkThreads;
-  if (ept <= 1) launch_topk_ept<1>(t, a.B, mode, approx, s);
-  else if (ept <= 2) launch_topk_ept<2>(t, a.B, mode, approx, s);
-  else if (ept <= 4) launch_topk_ept<4>(t, a.B, mode, approx, s);
-  else if (ept <= 8) launch_topk_ept<8>(t, a.B, mode, approx, s);
-  else launch_topk_ept<16>(t, a.B, mode, approx, s);   // Nc <= kMaxNc: at most 16 keys a thread
+  if (ept <= 1) launch_topk_ept<1>(t, G, mode, approx, s);
+  else if (ept <= 2) launch_topk_ept<2>(t, G, mode, approx, s);
+  else if (ept <= 4) launch_topk_ept<4>(t, G, mode, approx, s);
+  else if (ept <= 8) launch_topk_ept<8>(t, G, mode, approx, s);
+  else launch_topk_ept<16>(t, G, mode, approx, s);   // Nc <= kMaxNc: at most 16 keys a thread
   return hipGetLastError();
 }
 
