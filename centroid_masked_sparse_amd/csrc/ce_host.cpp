@@ -33,10 +33,18 @@ struct ce_head {
   const void* E = nullptr;
   std::vector<int32_t> offsets;       // [Nc+1]
   std::vector<int32_t> tos;           // [V]
-  std::vector<uint32_t> tiles;        // every 64-slot tile: (index in cluster << 13) | cluster
+  // Equal tile counts per cluster (tpc > 0): every 64-slot tile of every
+  // cluster, (index in cluster << 13) | cluster, zero-padded past the
+  // cluster's end.  Otherwise (tpc == 0, `tiles` empty) the contiguous
+  // tiling: tile t holds slots [64t, 64t+64) and tcl their clusters.
+  std::vector<uint32_t> tiles;
   int tpc = 0;                        // tiles per cluster if all clusters hold as many, else 0
+  long long n_tiles = 0;
   std::vector<int32_t> ttok;          // [n_tiles][64] token id of each tile slot, -1 past the end
-  std::vector<long long> tiles_top;   // tiles_top[K] = tiles of the K clusters with the most tiles
+  std::vector<uint16_t> tcl;          // tpc == 0: [n_tiles][64] cluster of each slot
+  // tiles_top[K] = the most tiles the rows of K clusters touch (a bound on
+  // a row's tile segments): each cluster's tiles, summed over the K largest
+  std::vector<long long> tiles_top;
   bool prepared = false;
   ce::Tables tables{};
 };
@@ -116,7 +124,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
 
 // Offsets of the device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t stats, offsets, tos, tiles, ttok, et, escale, ct, total;
+  size_t stats, offsets, tos, tiles, ttok, tcl, et, escale, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -132,10 +140,12 @@ PersistLayout persist_layout(const ce_head* h) {
   p.tos = take((size_t)h->V * sizeof(int32_t));
   p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
   p.ttok = take(std::max<size_t>(h->ttok.size(), 1) * sizeof(int32_t));
+  p.tcl = h->tcl.empty() ? 0 : take(h->tcl.size() * sizeof(uint16_t));
   const size_t tile_bytes = (size_t)ce::kTileTokens * h->d * elem_bytes(h->dtype);
   const size_t slab_tile = h->slab == CE_SLAB_FP8_E4M3 ? (size_t)ce::kTileTokens * h->d : tile_bytes;
-  p.et = take(h->tiles.size() * slab_tile);
-  p.escale = h->slab == CE_SLAB_FP8_E4M3 ? take(h->tiles.size() * ce::kTileTokens * sizeof(float)) : 0;
+  const size_t n_tiles = (size_t)h->n_tiles;
+  p.et = take(n_tiles * slab_tile);
+  p.escale = h->slab == CE_SLAB_FP8_E4M3 ? take(n_tiles * ce::kTileTokens * sizeof(float)) : 0;
   p.ct = take((((size_t)h->Nc + ce::kTileTokens - 1) / ce::kTileTokens) * tile_bytes);
   p.total = off;
   return p;
@@ -378,23 +388,40 @@ ce_status ce_head_create(const ce_head_desc* desc, ce_head_t* out) {
     std::vector<long long> ntiles((size_t)Nc);
     for (int c = 0; c < Nc; ++c) {
       const long long size = h->offsets[c + 1] - h->offsets[c];
-      const long long nt = (size + ce::kTileTokens - 1) / ce::kTileTokens;
-      ntiles[c] = nt;
-      if (nt > ce::kMaxTilesPerCluster) {
+      ntiles[c] = (size + ce::kTileTokens - 1) / ce::kTileTokens;
+      if (ntiles[c] > ce::kMaxTilesPerCluster) {
         delete h;
         return fail(CE_ERR_UNSUPPORTED, "a cluster holds more than 2^19 * 64 tokens");
-      }
-      for (long long q = 0; q < nt; ++q) {
-        h->tiles.push_back(((uint32_t)q << ce::kTileShift) | (uint32_t)c);
-        for (int l = 0; l < ce::kTileTokens; ++l) {
-          const long long j = h->offsets[c] + q * ce::kTileTokens + l;
-          h->ttok.push_back(j < h->offsets[c + 1] ? h->tos[j] : -1);
-        }
       }
     }
     h->tpc = (int)ntiles[0];
     for (int c = 1; c < Nc; ++c)
       if (ntiles[c] != ntiles[0]) h->tpc = 0;
+    if (h->tpc > 0) {
+      for (int c = 0; c < Nc; ++c)
+        for (long long q = 0; q < ntiles[c]; ++q) {
+          h->tiles.push_back(((uint32_t)q << ce::kTileShift) | (uint32_t)c);
+          for (int l = 0; l < ce::kTileTokens; ++l) {
+            const long long j = h->offsets[c] + q * ce::kTileTokens + l;
+            h->ttok.push_back(j < h->offsets[c + 1] ? h->tos[j] : -1);
+          }
+        }
+      h->n_tiles = (long long)h->tiles.size();
+    } else {
+      // contiguous tiling: no padding, so a tile may hold several clusters
+      // and a cluster's first and last tiles may be shared
+      h->n_tiles = ((long long)V + ce::kTileTokens - 1) / ce::kTileTokens;
+      h->ttok.assign((size_t)h->n_tiles * ce::kTileTokens, -1);
+      h->tcl.assign((size_t)h->n_tiles * ce::kTileTokens, (uint16_t)ce::kNoCluster);
+      for (int c = 0; c < Nc; ++c) {
+        const long long lo = h->offsets[c], hi = h->offsets[c + 1];
+        for (long long j = lo; j < hi; ++j) {
+          h->ttok[(size_t)j] = h->tos[(size_t)j];
+          h->tcl[(size_t)j] = (uint16_t)c;
+        }
+        ntiles[c] = hi > lo ? (hi - 1) / ce::kTileTokens - lo / ce::kTileTokens + 1 : 0;
+      }
+    }
     std::sort(ntiles.begin(), ntiles.end(), std::greater<long long>());
     h->tiles_top.assign((size_t)Nc + 1, 0);
     for (int k = 0; k < Nc; ++k) h->tiles_top[k + 1] = h->tiles_top[k] + ntiles[k];
@@ -437,18 +464,24 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
                                   hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
   }
+  if (!head->tcl.empty()) {
+    hipError_t e = hipMemcpyAsync(base + p.tcl, head->tcl.data(), head->tcl.size() * sizeof(uint16_t),
+                                  hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
+  }
+  // the tile list of the padded tiling; the contiguous one packs rows in order
+  const uint32_t* tiles_dev =
+      head->tiles.empty() ? nullptr : reinterpret_cast<const uint32_t*>(base + p.tiles);
   hipError_t e = hipMemsetAsync(base + p.stats, 0, 4 * sizeof(unsigned long long), stream);
   if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
   e = ce::launch_cnorm_max(head->C, head->dtype, head->Nc, head->d,
                            reinterpret_cast<unsigned long long*>(base + p.stats), stream);
   if (e != hipSuccess) return fail_hip(e, "norm kernel launch");
   e = head->slab == CE_SLAB_FP8_E4M3
-          ? ce::launch_pack_fp8(head->E, head->d, (long)head->tiles.size(),
-                                reinterpret_cast<const uint32_t*>(base + p.tiles),
-                                reinterpret_cast<const int32_t*>(base + p.offsets), base + p.et,
-                                reinterpret_cast<float*>(base + p.escale), stream)
-          : ce::launch_pack(head->E, head->dtype, head->d, (long)head->tiles.size(),
-                            reinterpret_cast<const uint32_t*>(base + p.tiles),
+          ? ce::launch_pack_fp8(head->E, head->d, (long)head->n_tiles, tiles_dev,
+                                reinterpret_cast<const int32_t*>(base + p.offsets), head->V,
+                                base + p.et, reinterpret_cast<float*>(base + p.escale), stream)
+          : ce::launch_pack(head->E, head->dtype, head->d, (long)head->n_tiles, tiles_dev,
                             reinterpret_cast<const int32_t*>(base + p.offsets), head->V,
                             base + p.et, stream);
   if (e == hipSuccess)
@@ -460,10 +493,10 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
   head->tables.offsets = reinterpret_cast<const int32_t*>(base + p.offsets);
   head->tables.tos = reinterpret_cast<const int32_t*>(base + p.tos);
-  head->tables.tiles = reinterpret_cast<const uint32_t*>(base + p.tiles);
-  head->tables.n_tiles = (int)head->tiles.size();
+  head->tables.n_tiles = (int)head->n_tiles;
   head->tables.tpc = head->tpc;
   head->tables.ttok = reinterpret_cast<const int32_t*>(base + p.ttok);
+  head->tables.tcl = head->tcl.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + p.tcl);
   head->tables.ET = base + p.et;
   head->tables.slab = head->slab == CE_SLAB_FP8_E4M3 ? 1 : 0;
   head->tables.escale = head->slab == CE_SLAB_FP8_E4M3 ? reinterpret_cast<const float*>(base + p.escale)

@@ -14,15 +14,20 @@ constexpr int kMaxNc = 8192;      // centroid id fits the low 13 bits of a work 
 constexpr int kTileShift = 13;     // tile word: (tile index in cluster << 13) | cluster
 constexpr int kMaxTilesPerCluster = 1 << (32 - kTileShift);
 constexpr int kMaxD = 8192;
+constexpr int kNoCluster = 0xFFFF;  // slot past the vocabulary in a tile of the contiguous tiling
 
 // Device tables uploaded at prepare time.
 struct Tables {
   const int32_t* offsets;      // [Nc+1] cluster c owns slots [offsets[c], offsets[c+1])
   const int32_t* tos;          // [V] token id of each slot
-  const uint32_t* tiles;       // [n_tiles] every 64-slot tile of every cluster, cluster-major
+  // Two tilings.  When every cluster holds the same number of 64-slot tiles
+  // (tpc > 0), each tile belongs to one cluster, zero-padded past its end:
+  // tile t is tile t % tpc of cluster t / tpc.  Otherwise tile t holds slots
+  // [64t, 64t+64) whatever their clusters, and tcl names each slot's.
   int n_tiles;
   int tpc;                     // tiles per cluster when every cluster holds as many, else 0
-  const int32_t* ttok;         // [n_tiles][64] token id of each tile slot, -1 past the cluster's end
+  const int32_t* ttok;         // [n_tiles][64] token id of each tile slot, -1 past the end
+  const uint16_t* tcl;         // tpc == 0: [n_tiles][64] cluster of each slot, kNoCluster past V
   const void* ET;              // packed embeddings: [n_tiles][d/vec][64] 16-byte vectors
   int slab;                    // 0: the head's dtype; 1: E4M3 codes (16 per vector)
   const float* escale;         // E4M3 slabs: [n_tiles][64] row scales
@@ -103,12 +108,15 @@ struct PassArgs {
   hipEvent_t probe_stop;
 };
 
-// Pack rows of W into 64-row tiles [t][v][lane] (see ce_kernels.hip).
+// Pack rows of W into 64-row tiles [t][v][lane]: tile t of the cluster
+// tile list `tiles` ((index in cluster << 13) | cluster), or rows
+// [64t, 64t+64) of nrows_total without one (see ce_kernels.hip).
 hipError_t launch_pack(const void* W, int dtype, int d, long n_tiles, const uint32_t* tiles,
                        const int32_t* offsets, int nrows_total, void* out, hipStream_t s);
 // Quantise bf16 rows to E4M3 with row scales and pack them the same way.
 hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* tiles,
-                           const int32_t* offsets, void* out, float* scale, hipStream_t s);
+                           const int32_t* offsets, int nrows_total, void* out, float* scale,
+                           hipStream_t s);
 // Largest row norm of C [Nc][d] into *out (zeroed by the caller).
 hipError_t launch_cnorm_max(const void* C, int dtype, int Nc, int d, unsigned long long* out,
                             hipStream_t s);

@@ -194,12 +194,14 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(double v) {
 // Quantise the rows of W (bf16, [rows][d] row-major) to E4M3 with one float32
 // scale per row, s = fl32(max |w| / 448) (1 for a zero row), codes
 // E4M3(fl64(w / s)), and pack them like pack_kernel: tile t of the cluster
-// tile list, [t][d/16][lane] vectors of 16 codes, scale[t][lane].  One
-// thread per tile row; lanes past a tile's last row get zero codes and scale.
+// tile list, or rows [64t, 64t+64) without one, [t][d/16][lane] vectors of
+// 16 codes, scale[t][lane].  One thread per tile row; lanes past a tile's
+// last row get zero codes and scale.
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restrict__ W, int d,
                                                        long n_rows_out,
                                                        const uint32_t* __restrict__ tiles,
                                                        const int32_t* __restrict__ offsets,
+                                                       long nrows_total,
                                                        v4u* __restrict__ out,
                                                        float* __restrict__ scale) {
   const int nvec = d / 16;
@@ -207,11 +209,18 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint16_t* __restric
   for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < n_rows_out; o += stride) {
     const int lane = (int)(o % kTileTokens);
     const long t = o / kTileTokens;
-    const uint32_t w = tiles[t];
-    const int c = (int)(w & ((1u << kTileShift) - 1u));
-    const long row = (long)offsets[c] + (long)(w >> kTileShift) * kTileTokens + lane;
+    long row, end;
+    if (tiles) {
+      const uint32_t w = tiles[t];
+      const int c = (int)(w & ((1u << kTileShift) - 1u));
+      row = (long)offsets[c] + (long)(w >> kTileShift) * kTileTokens + lane;
+      end = offsets[c + 1];
+    } else {
+      row = t * kTileTokens + lane;
+      end = nrows_total;
+    }
     v4u* dst = out + t * (long)nvec * kTileTokens + lane;
-    if (row >= offsets[c + 1]) {
+    if (row >= end) {
       for (int v = 0; v < nvec; ++v) dst[(long)v * kTileTokens] = v4u{0u, 0u, 0u, 0u};
       scale[o] = 0.0f;
       continue;
@@ -346,15 +355,23 @@ struct NoOp {
   __device__ void operator()() const {}
 };
 
+// Buffer range of a tile for predicated loads: a lane whose byte offset is
+// at or past it reads zeros and fetches nothing.  Tiles are far smaller.
+constexpr uint32_t kBufRange = 0x40000000u;
+constexpr uint32_t kBufWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
 // With SPLIT (a compile-time chunk count only), the first stages' tile loads
 // are issued, then mid() runs, then the first stages' hidden loads: mid may
 // produce the hidden rows (in LDS) while the tile loads are in flight.
+// With PRED the tile is read by buffer loads at lane_off (the lane's byte
+// offset 16 * lane, or kBufRange beyond it for a lane that needs no row), so
+// the slots no row needs cost no memory traffic.
 template <typename T, int RB, int NCH, int STAGES = 2, bool SPLIT = false, typename Mid = NoOp,
-          bool STREAM = false>
+          bool STREAM = false, bool PRED = false>
 __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
                                          const typename Elem<T>::hidden* __restrict__ h,
                                          const int (&rows)[RB], int nrows, double (&acc)[RB],
-                                         Mid&& mid = Mid()) {
+                                         Mid&& mid = Mid(), uint32_t lane_off = 0u) {
   using TH = typename Elem<T>::hidden;
   constexpr int PV = Elem<T>::kPerVec;
   constexpr int VPC = kChunk / PV;              // weight vectors per chunk
@@ -374,11 +391,18 @@ __device__ __forceinline__ void dot_tile(const v4u* __restrict__ wt, int d,
     v4u e[VPC];
     HR h[RB];
   };
+  __amdgpu_buffer_rsrc_t rsrc;
+  if constexpr (PRED)
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u*>(wt), (short)0, (int)kBufRange,
+                                             (int)kBufWord3);
   auto load_w = [&](Stage& st, int ch) {
 #pragma unroll
     for (int p = 0; p < VPC; ++p) {
       // STREAM: tiles read once per call (the gather's slabs) skip the caches
-      if constexpr (STREAM) st.e[p] = __builtin_nontemporal_load(&wt[(ch * VPC + p) * kWave + lane]);
+      if constexpr (PRED)
+        st.e[p] = __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc, lane_off + (uint32_t)((ch * VPC + p) * kWave * 16), 0, STREAM ? 2 : 0);
+      else if constexpr (STREAM) st.e[p] = __builtin_nontemporal_load(&wt[(ch * VPC + p) * kWave + lane]);
       else st.e[p] = wt[(ch * VPC + p) * kWave + lane];
     }
   };
@@ -1457,9 +1481,11 @@ struct GatherArgs {
   int d;
   const unsigned long long* cl_sel;  // [ceil(Nc/64)][64] row selection words of the centroids
   int B;
-  const uint32_t* tiles;        // [n_tiles] (index in cluster << 13) | cluster
   int tpc;                      // tiles per cluster when all clusters hold as many, else 0
   const int32_t* ttok;          // [n_tiles][64] token of each slot, -1 past the cluster's end
+  // tpc == 0: tile t holds slots [64t, 64t+64) of every cluster in turn,
+  // and the cluster of each slot (kNoCluster past the last slot)
+  const uint16_t* tcl;          // [n_tiles][64]
   int split_shift;              // 2^split_shift waves per tile share its passes
   int n_tiles;
   // by row (equal clusters, small batches): one wave per (row, selected
@@ -1532,7 +1558,8 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   int t;
   int cl = 0;          // the tile's cluster (tile grid)
   int fixed_seg = 0;   // by row: the wave's fixed top-m segment
-  unsigned long long mask;
+  unsigned long long mask;        // rows that selected a cluster of the tile, taken pass by pass
+  unsigned long long lane_rows;   // rows that selected this lane's cluster
   auto skip_passes = [&](int n) {
     for (int i = 0; i < n * RB && mask; ++i) mask &= mask - 1ull;
   };
@@ -1546,16 +1573,42 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     t = a.topk[(long)b * a.ldK + k] * a.tpc + (rem - k * a.tpc);
     fixed_seg = rem;
     mask = 1ull << b;
+    lane_rows = mask;
   } else {
     const int slot = (int)blockIdx.x / a.n_tiles;
     t = (int)blockIdx.x - slot * a.n_tiles;
-    const int c = a.tpc > 0 ? t / a.tpc : (int)(a.tiles[t] & ((1u << kTileShift) - 1u));
-    cl = c;
-    // lane b reads row b's selection word of c's 64-centroid block
-    const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
-    mask = __ballot((word >> (c % kWave)) & 1ull);
+    if (a.tpc > 0) {
+      const int c = t / a.tpc;
+      cl = c;
+      // lane b reads row b's selection word of c's 64-centroid block
+      const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
+      mask = __ballot((word >> (c % kWave)) & 1ull);
+      lane_rows = mask;
+    } else {
+      // the tile's slots belong to consecutive clusters: for each one, lane
+      // b reads row b's selection word of its 64-centroid block (again only
+      // when the block changes) and a ballot gives the rows that selected it
+      const int myc = a.tcl[(long)t * kWave + lane];
+      unsigned long long todo = __ballot(myc != kNoCluster);
+      mask = 0ull;
+      lane_rows = 0ull;
+      int blk = -1;
+      unsigned long long word = 0ull;
+      while (todo) {
+        const int c = __builtin_amdgcn_readlane(myc, (int)__builtin_ctzll(todo));
+        if (c / kWave != blk) {
+          blk = c / kWave;
+          word = lane < a.B ? a.cl_sel[(long)blk * kWave + lane] : 0ull;
+        }
+        const unsigned long long m = __ballot((word >> (c % kWave)) & 1ull);
+        const bool mine = myc == c;
+        if (mine) lane_rows = m;
+        mask |= m;
+        todo &= ~__ballot(mine);
+      }
+    }
     skip_passes(slot);
-    if (!mask) return;   // no row selected this tile's cluster, or no pass left for this wave
+    if (!mask) return;   // no row selected a cluster of this tile, or no pass left for this wave
   }
   // the token ids are needed only after the first batch is dotted: they
   // are waited for there, not before the tile loads go out
@@ -1577,19 +1630,21 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     for (int r = 0; r < RB; ++r) {
       if (r < nrows) {
         const float f = std::is_same<T, uint8_t>::value ? canon(acc[r] * (double)sc) : canon(acc[r]);
+        // a candidate: a token in a cluster this row selected
+        const bool cand = tok >= 0 && ((lane_rows >> rows[r]) & 1ull);
         if (MODE == kArgmax) {
           unsigned long long k = 0ull;
-          if (tok >= 0)
+          if (cand)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           k = wave_max_u64(k);
           // result unused: no stall; one of the row's slots, by wave index
           if (lane == 0)
             atomicMax(&a.amax[rows[r] * kArgRowStride + (int)(blockIdx.x % kArgSlots) * kArgSlotStride], k);
         } else if (MODE == kMasked) {
-          if (tok >= 0) a.out[(long)rows[r] * a.V + tok] = f;
+          if (cand) a.out[(long)rows[r] * a.V + tok] = f;
         } else {
           unsigned long long k = 0ull;
-          if (tok >= 0)
+          if (cand)
             k = ((unsigned long long)order_key(f) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok);
           // the segment is the tile's 64 keys as they are (zero where the
           // slot holds no token; no key is 0) and its head the largest
@@ -1628,8 +1683,15 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
       for (int r = 0; r < RB; ++r)
         rk[r] = rp[a.tm_rank && !a.by_row ? (long)rows[r] * a.ldR + cl : 0];
     }
+    // lanes whose cluster none of the pass's rows selected fetch nothing
+    unsigned long long prow = 0ull;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+      if (r < nrows) prow |= 1ull << rows[r];
+    const uint32_t lane_off = ((lane_rows & prow) ? 0u : kBufRange) + 16u * (uint32_t)lane;
     double acc[RB];
-    dot_tile<T, RB, NCH, kGatherStages<T>, false, NoOp, kGatherStream>(wtb, a.d, h, rows, nrows, acc);
+    dot_tile<T, RB, NCH, kGatherStages<T>, false, NoOp, kGatherStream, true>(wtb, a.d, h, rows, nrows,
+                                                                             acc, NoOp(), lane_off);
     pin(tok);   // keep the loads out of the branches below
     pin(sc);
     finish(rows, nrows, acc);
@@ -1829,14 +1891,15 @@ hipError_t launch_cnorm_max(const void* C, int dtype, int Nc, int d, unsigned lo
 }
 
 hipError_t launch_pack_fp8(const void* W, int d, long n_tiles, const uint32_t* tiles,
-                           const int32_t* offsets, void* out, float* scale, hipStream_t s) {
+                           const int32_t* offsets, int nrows_total, void* out, float* scale,
+                           hipStream_t s) {
   const long n_rows_out = n_tiles * kTileTokens;
   if (n_rows_out == 0) return hipSuccess;
   long blocks = (n_rows_out + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      static_cast<const uint16_t*>(W), d, n_rows_out, tiles, offsets,
-                     static_cast<v4u*>(out), scale);
+                     (long)nrows_total, static_cast<v4u*>(out), scale);
   return hipGetLastError();
 }
 
@@ -1980,6 +2043,12 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
 // (B=32: 33.3 µs per call split or not); at 64 rows the two-pass tiles set
 // the gather's tail and splitting them takes the call from 39.2 to 37.8 µs.
 static int gather_split_shift(int B) { return B >= 48 ? kGatherSplitShift : 0; }
+// Ragged heads (the contiguous tiling): a tile shared by several clusters,
+// or of a cluster many rows selected, needs several passes (skewed head,
+// d=512, B=64: gather 44.3 µs with two waves a tile, 32.6 with four, 33.2
+// with eight).
+constexpr int kRaggedSplitShift = 2;
+static int gather_split_shift_ragged(int B) { return B >= 16 ? kRaggedSplitShift : 0; }
 
 // Largest batch whose gather runs by row (equal clusters only): up to it
 // the B·K·tpc waves of the selected (row, centroid, tile) triples cost less
@@ -1996,11 +2065,11 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.d = a.d;
   g.cl_sel = a.cl_sel;
   g.B = a.B;
-  g.tiles = a.t.tiles;
+  g.tcl = a.t.tcl;
   g.tpc = a.t.tpc;
   g.ttok = a.t.ttok;
   g.escale = a.t.escale;
-  g.split_shift = gather_split_shift(a.B);
+  g.split_shift = a.t.tpc > 0 ? gather_split_shift(a.B) : gather_split_shift_ragged(a.B);
   g.best = a.best;
   g.amax = a.amax;
   g.out = a.logits;

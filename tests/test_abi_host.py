@@ -118,11 +118,12 @@ def test_create_ragged_and_sizes(lib):
         n = ctypes.c_size_t()
         assert lib.ce_head_persistent_bytes(h, ctypes.byref(n)) == 0
         # statistics (4 words) + offsets (5 ints) + token_of_slot (V ints) +
-        # the tile list (clusters of 0, 100, 30 and 126 tokens: 0+2+1+2 = 5
-        # words) + the tiles' slot tokens (5 x 64 ints), each rounded up to
-        # 256 bytes, + packed embeddings (5 tiles) and centroids (1 tile) of
-        # 64 rows x 64 bf16
-        assert n.value == 256 + 256 + 1024 + 256 + 5 * 256 + 5 * 8192 + 8192
+        # an empty tile list (clusters of 0, 100, 30 and 126 tokens hold 0, 2,
+        # 1 and 2 tiles, so the tiling is the contiguous one: V / 64 = 4
+        # tiles) + the tiles' slot tokens (4 x 64 ints) and clusters (4 x 64
+        # shorts), each rounded up to 256 bytes, + packed embeddings (4 tiles)
+        # and centroids (1 tile) of 64 rows x 64 bf16
+        assert n.value == 256 + 256 + 1024 + 256 + 4 * 256 + 2 * 256 + 4 * 8192 + 8192
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOPK, ctypes.byref(n)) == 0
         assert n.value == 0
         sizes = {}
@@ -141,8 +142,8 @@ def test_create_ragged_and_sizes(lib):
         assert lib.ce_workspace_bytes(h, 8, 5, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
         assert lib.ce_workspace_bytes(h, 8, 0, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == ERR["CE_ERR_BAD_SHAPE"]
         assert lib.ce_workspace_bytes(h, 8, 1, 9, ctypes.byref(n)) == ERR["CE_ERR_UNSUPPORTED"]
-        # top-m: the masked sizes plus its segment lists (tiles of the K
-        # largest clusters: 2 + 2 for K=2, of one 64-token tile's keys each)
+        # top-m: the masked sizes plus its segment lists (tiles the K largest
+        # clusters touch: 2 + 2 for K=2, of one 64-token tile's keys each)
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_M, ctypes.byref(n)) == 0
         assert n.value >= sizes[_ffi.CE_OP_TOP_TOKENS] + 8 * 4 * 64 * 8
     finally:
@@ -230,9 +231,9 @@ def test_fp8_slab_sizes(lib):
         finally:
             lib.ce_head_destroy(h)
     native, fp8 = sizes[_ffi.CE_SLAB_NATIVE], sizes[_ffi.CE_SLAB_FP8_E4M3]
-    # 5 tiles of 64 rows x 64 elements: 5 * 8192 bytes of bf16 become 5 * 4096
-    # bytes of codes plus 5 * 256 bytes of scales (each region 256-aligned)
-    assert native[0] - fp8[0] == 5 * 8192 - 5 * 4096 - 5 * 256
+    # 4 tiles of 64 rows x 64 elements: 4 * 8192 bytes of bf16 become 4 * 4096
+    # bytes of codes plus 4 * 256 bytes of scales (each region 256-aligned)
+    assert native[0] - fp8[0] == 4 * 8192 - 4 * 4096 - 4 * 256
     assert native[1] == fp8[1]
 
 
