@@ -78,10 +78,22 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
   size_t scores = 0, topk = 0, cl_sel = 0, best = 0, amax = 0, tm_keys = 0, tm_heads = 0, tm_rank = 0,
-         total = 0;
+         crec = 0, total = 0;
   bool has_rank = false;
+  bool cert = false;
   int tm_segcap = 0;
 };
+
+// ce_top_tokens on a bf16 head takes the certified matrix-core argmax
+// with CE_PROJ_MFMA, and with CE_PROJ_AUTO where it measured faster than
+// the float64 dot: hidden sizes from 512, where each slot's chain is long,
+// and ragged heads, whose tiles carry many rows (B=64: skewed head, d=512,
+// gather 21.7 against 32.9 µs; wide head, d=1024, call 83.8 against 106.7;
+// sweep head, d=256, 23.4 against 20.8 the other way).
+bool cert_head(const ce_head* h) {
+  if (h->dtype != CE_BF16 || h->proj == CE_PROJ_EXACT) return false;
+  return h->proj == CE_PROJ_MFMA || h->d >= 512 || h->tpc == 0;
+}
 
 // CE_PROJ_AUTO takes the MFMA projection for a pass of at least this many
 // multiply-adds (B Nc d).  The exact projection costs in proportion to them;
@@ -109,6 +121,10 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   L.cl_sel = take(((size_t)h->Nc + 63) / 64 * ce::kPassRows * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
   L.amax = take(ce::kArgWords * sizeof(unsigned long long));
+  if (op == CE_OP_TOP_TOKENS && cert_head(h)) {
+    L.cert = true;
+    L.crec = take(nb * (size_t)h->n_tiles * 16);
+  }
   if (op == CE_OP_TOP_M) {
     L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);
     L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kTileTokens * sizeof(unsigned long long));
@@ -124,7 +140,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
 
 // Offsets of the device tables inside the persistent buffer.
 struct PersistLayout {
-  size_t stats, offsets, tos, tiles, ttok, tcl, et, escale, ct, total;
+  size_t stats, offsets, tos, tiles, ttok, tcl, et, escale, enorm, ct, total;
 };
 
 PersistLayout persist_layout(const ce_head* h) {
@@ -146,6 +162,7 @@ PersistLayout persist_layout(const ce_head* h) {
   const size_t n_tiles = (size_t)h->n_tiles;
   p.et = take(n_tiles * slab_tile);
   p.escale = h->slab == CE_SLAB_FP8_E4M3 ? take(n_tiles * ce::kTileTokens * sizeof(float)) : 0;
+  p.enorm = h->dtype == CE_BF16 ? take(n_tiles * ce::kTileTokens * sizeof(float)) : 0;
   p.ct = take((((size_t)h->Nc + ce::kTileTokens - 1) / ce::kTileTokens) * tile_bytes);
   p.total = off;
   return p;
@@ -187,6 +204,8 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.tm_segcap = L.tm_segcap;
   a.tm_rank = L.has_rank ? reinterpret_cast<int16_t*>(ws + L.tm_rank) : nullptr;
   a.ldR = a.Nc;
+  a.cert = L.cert;
+  a.crec = L.cert ? ws + L.crec : nullptr;
 }
 
 // The draft step's extra operands (ce_draft_step).
@@ -489,6 +508,12 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
                         ((long)head->Nc + ce::kTileTokens - 1) / ce::kTileTokens, nullptr, nullptr,
                         head->Nc, base + p.ct, stream);
   if (e != hipSuccess) return fail_hip(e, "pack kernel launch");
+  if (head->dtype == CE_BF16) {
+    e = ce::launch_slot_norms(base + p.et, head->slab == CE_SLAB_FP8_E4M3 ? 1 : 0,
+                              reinterpret_cast<const float*>(base + p.escale), (long)head->n_tiles,
+                              head->d, reinterpret_cast<float*>(base + p.enorm), stream);
+    if (e != hipSuccess) return fail_hip(e, "norm kernel launch");
+  }
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
   head->tables.offsets = reinterpret_cast<const int32_t*>(base + p.offsets);
@@ -502,6 +527,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   head->tables.escale = head->slab == CE_SLAB_FP8_E4M3 ? reinterpret_cast<const float*>(base + p.escale)
                                                         : nullptr;
   head->tables.CT = base + p.ct;
+  head->tables.enorm = head->dtype == CE_BF16 ? reinterpret_cast<const float*>(base + p.enorm) : nullptr;
   head->stats = reinterpret_cast<unsigned long long*>(base + p.stats);
   head->tables.stats = head->stats;
   head->prepared = true;

@@ -31,6 +31,7 @@ struct Tables {
   const void* ET;              // packed embeddings: [n_tiles][d/vec][64] 16-byte vectors
   int slab;                    // 0: the head's dtype; 1: E4M3 codes (16 per vector)
   const float* escale;         // E4M3 slabs: [n_tiles][64] row scales
+  const float* enorm;          // [n_tiles][64] |e| of each slot (times its scale), rounded up
   const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
   // [0] the largest centroid row norm (bits of a double, rounded up);
   // [1] rows whose top-K band was recomputed in canonical keys,
@@ -70,6 +71,8 @@ struct PassArgs {
   Tables t;
   const void* h;          // [B][d] rows of this pass
   bool approx;            // bf16 MFMA projection + certified top-K (else canonical scores)
+  bool cert;              // argmax by matrix-core dots + certified finalize (tile grid only)
+  void* crec;             // cert: [B][n_tiles] 16-byte bound records
   // workspace regions
   float* S;               // [B][ldS] centroid scores
   int ldS;
@@ -125,6 +128,9 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s);   // mode: T
 hipError_t launch_gather(const PassArgs& a, int mode, hipStream_t s);
 hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_finalize(const PassArgs& a, hipStream_t s);
+// Slot norms of the packed slabs (certified argmax) into out [n_tiles][64].
+hipError_t launch_slot_norms(const void* ET, int slab, const float* escale, long n_tiles, int d,
+                             float* out, hipStream_t s);
 // Size of the static scratch array of ce_top_tokens_static (bytes).
 constexpr size_t kStaticScratchBytes = size_t(4) << 20;
 // Device address of the static scratch array on the current device (looked

@@ -887,6 +887,7 @@ __device__ __forceinline__ uint32_t lanes_below(unsigned long long m) {
 __device__ __forceinline__ uint32_t popc64(unsigned long long m) { return (uint32_t)__popcll(m); }
 
 // Exclusive prefix sum over the threads of the block; *total gets the sum.
+template <int NW = kTopkWaves>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -895,7 +896,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const uint32_t s = sh[i];
     base += (i < w) ? s : 0u;
     tot += s;
@@ -1016,10 +1017,9 @@ __device__ __forceinline__ int bf16_lsb_exp(uint32_t bits) {
 // exact: the sequential chain then equals the exact sum, which the wave adds
 // in parallel.  Otherwise the chain runs in hidden-dimension order, each
 // vector broadcast from its lane.
-__device__ uint32_t wave_canonical_key(int c, const uint16_t* hl, const v4u* __restrict__ CT, int d) {
+__device__ uint32_t wave_row_key(const v4u* __restrict__ row, const uint16_t* hl, int d) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nvec = d / 8;
-  const v4u* row = CT + (long)(c / kTileTokens) * nvec * kWave + (c % kTileTokens);
   auto prod = [&](const v4u& hv, const v4u& cv, int e) {
     const uint32_t hb = (hv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
     const uint32_t cb = (cv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
@@ -1069,6 +1069,62 @@ __device__ uint32_t wave_canonical_key(int c, const uint16_t* hl, const v4u* __r
                                           (double)__uint_as_float(((cv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16), acc);
   }
   return order_key(canon(acc));
+}
+__device__ __forceinline__ uint32_t wave_canonical_key(int c, const uint16_t* hl, const v4u* __restrict__ CT,
+                                                       int d) {
+  return wave_row_key(CT + (long)(c / kTileTokens) * (d / 8) * kWave + (c % kTileTokens), hl, d);
+}
+
+// Exponent of the last significant bit of a nonzero decoded E4M3 value
+// (at most four significant bits; subnormal codes are multiples of 2^-9).
+__device__ __forceinline__ int e4m3_lsb_exp(float f) { return max(ilogbf(f) - 3, -9); }
+
+// The same for a slot of an FP8 slab (vector v = 16 codes at row[64 v]) and
+// its row scale: the key of canon(chain * scale), the chain of the bf16
+// row's elements times the decoded codes (exact products), by the same
+// exact-sum test.
+__device__ uint32_t wave_row_key_fp8(const v4u* __restrict__ row, const uint16_t* hl, int d, float sc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nvec = d / 16;
+  double part = 0.0, mag = 0.0;
+  int q = 0x7FFFFFFF;
+#pragma unroll 1
+  for (int v0 = 0; v0 < nvec; v0 += kWave) {
+    const int v = v0 + lane;
+    if (v < nvec) {
+      const v4u cv = row[(long)v * kWave];
+      double x[16];
+      widen(cv, x, uint8_t());
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t hb = hl[16 * v + e];
+        const double p = (double)__uint_as_float(hb << 16) * x[e];
+        if (p != 0.0) {
+          part += p;
+          mag += fabs(p);
+          q = min(q, bf16_lsb_exp(hb) + e4m3_lsb_exp((float)x[e]));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    part += __shfl_xor(part, o);
+    mag += __shfl_xor(mag, o);
+    q = min(q, __shfl_xor(q, o));
+  }
+  if (q == 0x7FFFFFFF || mag * (1.0 + 0x1p-30) < ldexp(1.0, q + 53))
+    return order_key(canon(part * (double)sc));
+  double acc = 0.0;
+#pragma unroll 1
+  for (int v = 0; v < nvec; ++v) {
+    const v4u cv = row[(long)v * kWave];   // the same address in every lane
+    double x[16];
+    widen(cv, x, uint8_t());
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc = fma((double)__uint_as_float((uint32_t)hl[16 * v + e] << 16), x[e], acc);
+  }
+  return order_key(canon(acc * (double)sc));
 }
 
 // Canonical keys of this thread's centroids first + i for the bits i of
@@ -1507,6 +1563,10 @@ struct GatherArgs {
   // so no counter is claimed; null otherwise
   const int16_t* tm_rank;       // [B][ldR]
   int ldR;
+  // certified argmax (matrix-core dots): slot norms and the per-(row, tile)
+  // bound records
+  const float* enorm;           // [n_tiles][64] |e| of each slot (times its FP8 scale), rounded up
+  v4u* crec;                    // [B][n_tiles] per (row, tile): best L, its U, others' U, slot
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -1537,6 +1597,44 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
 template <typename T>
 constexpr int kGatherStages = std::is_same<T, float>::value ? 2 : 4;
 constexpr bool kGatherStream = true;    // non-temporal slab loads (read once per call: 21.1 -> 20.1 us at B=64)
+
+// Tile t of the tile grid: the rows that selected a cluster of the tile
+// (mask) and, in each lane, the rows that selected the cluster of the
+// lane's slot (lane_rows); cl is the tile's cluster in the padded tiling.
+__device__ __forceinline__ void tile_rows(const GatherArgs& a, int t, unsigned long long& mask,
+                                          unsigned long long& lane_rows, int& cl) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (a.tpc > 0) {
+    const int c = t / a.tpc;
+    cl = c;
+    // lane b reads row b's selection word of c's 64-centroid block
+    const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
+    mask = __ballot((word >> (c % kWave)) & 1ull);
+    lane_rows = mask;
+    return;
+  }
+  // the tile's slots belong to consecutive clusters: for each one, lane b
+  // reads row b's selection word of its 64-centroid block (again only when
+  // the block changes) and a ballot gives the rows that selected it
+  const int myc = a.tcl[(long)t * kWave + lane];
+  unsigned long long todo = __ballot(myc != kNoCluster);
+  mask = 0ull;
+  lane_rows = 0ull;
+  int blk = -1;
+  unsigned long long word = 0ull;
+  while (todo) {
+    const int c = __builtin_amdgcn_readlane(myc, (int)__builtin_ctzll(todo));
+    if (c / kWave != blk) {
+      blk = c / kWave;
+      word = lane < a.B ? a.cl_sel[(long)blk * kWave + lane] : 0ull;
+    }
+    const unsigned long long m = __ballot((word >> (c % kWave)) & 1ull);
+    const bool mine = myc == c;
+    if (mine) lane_rows = m;
+    mask |= m;
+    todo &= ~__ballot(mine);
+  }
+}
 
 // One wave per packed tile (2^split_shift waves from 48 rows), or, by row,
 // one wave per selected (row, centroid, tile).  Once the rows that selected
@@ -1577,36 +1675,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   } else {
     const int slot = (int)blockIdx.x / a.n_tiles;
     t = (int)blockIdx.x - slot * a.n_tiles;
-    if (a.tpc > 0) {
-      const int c = t / a.tpc;
-      cl = c;
-      // lane b reads row b's selection word of c's 64-centroid block
-      const unsigned long long word = lane < a.B ? a.cl_sel[(long)(c / kWave) * kWave + lane] : 0ull;
-      mask = __ballot((word >> (c % kWave)) & 1ull);
-      lane_rows = mask;
-    } else {
-      // the tile's slots belong to consecutive clusters: for each one, lane
-      // b reads row b's selection word of its 64-centroid block (again only
-      // when the block changes) and a ballot gives the rows that selected it
-      const int myc = a.tcl[(long)t * kWave + lane];
-      unsigned long long todo = __ballot(myc != kNoCluster);
-      mask = 0ull;
-      lane_rows = 0ull;
-      int blk = -1;
-      unsigned long long word = 0ull;
-      while (todo) {
-        const int c = __builtin_amdgcn_readlane(myc, (int)__builtin_ctzll(todo));
-        if (c / kWave != blk) {
-          blk = c / kWave;
-          word = lane < a.B ? a.cl_sel[(long)blk * kWave + lane] : 0ull;
-        }
-        const unsigned long long m = __ballot((word >> (c % kWave)) & 1ull);
-        const bool mine = myc == c;
-        if (mine) lane_rows = m;
-        mask |= m;
-        todo &= ~__ballot(mine);
-      }
-    }
+    tile_rows(a, t, mask, lane_rows, cl);
     skip_passes(slot);
     if (!mask) return;   // no row selected a cluster of this tile, or no pass left for this wave
   }
@@ -1696,6 +1765,465 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     pin(sc);
     finish(rows, nrows, acc);
     skip_passes(nsplit - 1);
+  }
+}
+
+// ------------------------------------------------------------------ certified argmax
+
+// fp32 at or above x (x >= 0): the nearest float, raised one step if below.
+__device__ __forceinline__ float f32_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+
+// Bound of a matrix-core dot: the canonical key of a (token, row) pair, as a
+// real, lies within E of the fp32 result l~ (bf16 x bf16, or bf16 x decoded
+// E4M3 codes, then times the slot's scale), where
+// E = beta A (1 + 2^-8) + 2^-21 (|l~| + beta A) + d 2^-125, A = |h| |e| >=
+// sum_k |h_k e_k| and beta = d 2^-23: every instruction adds 32 exact
+// products and the accumulator with at most 32 roundings of fp32
+// precision; the key's own rounding is within 2^-24 of its magnitude, the
+// float64 chain within d 2^-53 of the exact sum, and the slack covers the
+// fp32 arithmetic of E, l~ - E and l~ + E.
+__device__ __forceinline__ float cert_bound(float lt, float A, float beta, float tiny) {
+  const float bA = beta * A;
+  return bA * (1.0f + 0x1p-8f) + 0x1p-21f * (fabsf(lt) + bA) + tiny;
+}
+
+// The argmax gather by matrix cores.  One wave per tile of the tile grid
+// (2^split_shift waves share its passes); a pass takes up to 16 of the
+// rows that selected a cluster of the tile, lane r's row the r-th.  The
+// tile streams in blocks of 32 hidden dims: lane 16q + r loads the 16-byte
+// vector 4kb + q of token 16m + r for each block m of 16 tokens (FP8: the
+// half vector of codes, decoded to bf16), which is the A operand of
+// v_mfma_f32_16x16x32_bf16 as it stands, and the B operand is hidden row r's
+// dims 32kb + 8q .. +7; lane l ends with the sums of tokens 16m + 4(l/16) + i
+// and row l%16.  Tokens that no row of the pass selected load nothing.
+//
+// Each (token, row) sum gets the bound E of cert_bound (|h| from the same
+// loads, |e| from the slot table): its canonical key lies in [L, U] =
+// [l~ - E, l~ + E].  For each of its rows the wave writes one record at
+// (row, tile), with no atomics: the largest L among the tile's candidates,
+// that token's U and slot, and the largest U of the tile's other
+// candidates.  Every (row, tile) pair of a row's selected clusters is
+// written by exactly one wave, so the records need no clearing.
+template <typename T, int NKB>
+__global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
+  constexpr bool F8 = std::is_same<T, uint8_t>::value;
+  static_assert(F8 || std::is_same<T, uint16_t>::value, "bf16 or E4M3 slabs");
+  __shared__ unsigned long long lr_sh[kWave];   // lane_rows of each slot of the tile
+  const int lane = threadIdx.x;
+  const int r = lane & 15, kq = lane >> 4;
+  const int nsplit = 1 << a.split_shift;
+  const int slot = (int)blockIdx.x / a.n_tiles;
+  const int t = (int)blockIdx.x - slot * a.n_tiles;
+  unsigned long long mask, lane_rows;
+  int cl = 0;
+  tile_rows(a, t, mask, lane_rows, cl);
+  for (int i = 0; i < 16 * slot && mask; ++i) mask &= mask - 1ull;
+  if (!mask) return;
+  lr_sh[lane] = lane_rows;
+  const long tb = (long)t * kWave;
+  // the tokens, norms (and scales) of this lane's sixteen outputs
+  v4u tok4[4], en4[4], sc4[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const long o = tb + 16 * m + 4 * kq;
+    tok4[m] = *reinterpret_cast<const v4u*>(a.ttok + o);
+    en4[m] = *reinterpret_cast<const v4u*>(a.enorm + o);
+    if constexpr (F8) sc4[m] = *reinterpret_cast<const v4u*>(a.escale + o);
+  }
+  __syncthreads();
+  const int d = a.d;
+  const int nkb = NKB > 0 ? NKB : d / 32;
+  const float beta = (float)d * 0x1p-23f;
+  const float tiny = (float)d * 0x1p-125f;
+  const v4u* wt = a.ET + tb * (d / Elem<T>::kPerVec);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u*>(wt), (short)0, (int)kBufRange, (int)kBufWord3);
+  const auto* hb = reinterpret_cast<const uint16_t*>(a.h);
+
+  while (mask) {
+    // this pass's rows: lane r takes the r-th lowest bit of mask
+    int myrow = -1;
+    unsigned long long prow = 0ull;
+    for (int i = 0; i < 16 && mask; ++i) {
+      const int b = __builtin_ctzll(mask);
+      mask &= mask - 1ull;
+      if (r == i) myrow = b;
+      prow |= 1ull << b;
+    }
+    for (int i = 0; i < 16 * (nsplit - 1) && mask; ++i) mask &= mask - 1ull;
+    const int hrow = myrow >= 0 ? myrow : (int)__builtin_ctzll(prow);   // a valid row for every lane
+    uint32_t aoff[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int tau = 16 * m + r;
+      const bool act = (lr_sh[tau] & prow) != 0ull;
+      aoff[m] = (act ? 0u : kBufRange) + 16u * (uint32_t)tau + (F8 ? 8u * (uint32_t)(kq & 1) : 0u);
+    }
+    const v4u* hp = reinterpret_cast<const v4u*>(hb + (long)hrow * d) + kq;
+
+    v4f acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+    double ss = 0.0;
+    // groups of G blocks in two register stages, loads clamped to the last
+    // block (so unconditional) and the blocks past the end skipped
+    constexpr int G = 4;
+    using AT = typename std::conditional<F8, v2u, v4u>::type;
+    struct Stage {
+      AT x[G][4];
+      v4u h[G];
+    };
+    auto load = [&](Stage& st, int k0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int kb = min(k0 + j, nkb - 1);
+        // vector of this lane's dims: bf16 4kb + q, E4M3 2kb + q/2 (half q%2)
+        const uint32_t voff = (uint32_t)((F8 ? 2 * kb + (kq >> 1) : 4 * kb + kq) * kWave * 16);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if constexpr (F8) st.x[j][m] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, aoff[m] + voff, 0, 2);
+          else st.x[j][m] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, aoff[m] + voff, 0, 2);
+        }
+        st.h[j] = hp[4 * kb];
+      }
+    };
+    auto run = [&](const Stage& st, int k0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (k0 + j < nkb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const double lo = (double)__uint_as_float(st.h[j][e] << 16);
+            const double hi = (double)__uint_as_float(st.h[j][e] & 0xFFFF0000u);
+            ss = fma(lo, lo, ss);
+            ss = fma(hi, hi, ss);
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            v4u av;
+            if constexpr (F8) {
+              // E4M3 -> fp32 exactly, then the upper halves: exact bf16
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)st.x[j][m][w], false);
+                const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)st.x[j][m][w], true);
+                av[2 * w] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+                av[2 * w + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
+              }
+            } else {
+              av = st.x[j][m];
+            }
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                             __builtin_bit_cast(v8bf, st.h[j]), acc[m],
+                                                             0, 0, 0);
+          }
+        }
+      }
+    };
+    Stage st0, st1;
+    load(st0, 0);
+    if (nkb > G) load(st1, G);
+#pragma unroll
+    for (int k0 = 0; k0 < nkb; k0 += 2 * G) {
+      run(st0, k0);
+      if (k0 + 2 * G < nkb) load(st0, k0 + 2 * G);
+      if (k0 + G < nkb) {
+        run(st1, k0 + G);
+        if (k0 + 3 * G < nkb) load(st1, k0 + 3 * G);
+      }
+    }
+
+    // the row's |h|: its four lanes hold the squares of disjoint dims
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float hn = f32_up(sqrt(ss) * (1.0 + 0x1p-40));
+    // this lane's best candidate (largest L, then lowest slot), its U, and
+    // the largest U of its other candidates
+    uint32_t bl = 0u, bu = 0u, u2 = 0u, btau = 0u, bad = 0u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tau = 16 * m + 4 * kq + i;
+        const int tok = (int)tok4[m][i];
+        float lt = acc[m][i];
+        if constexpr (F8) lt *= __uint_as_float(sc4[m][i]);
+        const float E = cert_bound(lt, hn * __uint_as_float(en4[m][i]), beta, tiny);
+        if (myrow >= 0 && tok >= 0 && ((lr_sh[tau] >> myrow) & 1ull)) {
+          // fails for a NaN too
+          if (!(fabsf(lt) <= 0x1.fffffep127f && E <= 0x1.fffffep127f)) bad = 1u;
+          const uint32_t lk = order_key(lt - E), uk = order_key(lt + E);
+          if (lk > bl) {   // slots rise with i, so a tie keeps the lower one
+            u2 = max(u2, bu);
+            bl = lk;
+            bu = uk;
+            btau = (uint32_t)tau;
+          } else {
+            u2 = max(u2, uk);
+          }
+        }
+      }
+    }
+    // merge the row's four lanes (xor 16, then 32)
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const uint32_t obl = (uint32_t)__shfl_xor((int)bl, o), obu = (uint32_t)__shfl_xor((int)bu, o);
+      const uint32_t ou2 = (uint32_t)__shfl_xor((int)u2, o), otau = (uint32_t)__shfl_xor((int)btau, o);
+      bad |= (uint32_t)__shfl_xor((int)bad, o);
+      const bool take = obl > bl || (obl == bl && otau < btau);
+      u2 = max(max(u2, ou2), take ? bu : obu);
+      if (take) {
+        bl = obl;
+        bu = obu;
+        btau = otau;
+      }
+    }
+    if (kq == 0 && myrow >= 0)
+      a.crec[(long)myrow * a.n_tiles + t] = v4u{bl, bu, u2, btau | (bad << 6)};
+  }
+}
+
+// The canonical key of one slot by one thread: the float64 chain over the
+// hidden dims in order (FP8: times the slot's scale), for a whole recompute.
+template <typename T>
+__device__ uint32_t slot_chain_key(const v4u* __restrict__ row, const uint16_t* hl, int d, float sc) {
+  constexpr int PV = Elem<T>::kPerVec;
+  double acc = 0.0;
+#pragma unroll 1
+  for (int v = 0; v < d / PV; ++v) {
+    double x[PV];
+    widen(row[(long)v * kWave], x, T());
+#pragma unroll
+    for (int e = 0; e < PV; ++e) acc = fma((double)__uint_as_float((uint32_t)hl[PV * v + e] << 16), x[e], acc);
+  }
+  return order_key(canon(std::is_same<T, uint8_t>::value ? acc * (double)sc : acc));
+}
+
+struct CertArgs {
+  const v4u* crec;        // [B][n_tiles] records of the gather
+  int n_tiles;
+  const v4u* ET;
+  const float* escale;
+  const int32_t* ttok;
+  const uint16_t* tcl;    // contiguous tiling: cluster of each slot
+  const unsigned long long* cl_sel;
+  const uint16_t* h;      // [B][d] bf16
+  int d;
+  // the row's selected clusters and their tiles
+  const int32_t* topk;
+  int ldK, K;
+  const int32_t* offsets;
+  int tpc;
+  int32_t* tokens;
+};
+constexpr int kCertThreads = 256;
+constexpr int kCertWaves = kCertThreads / kWave;
+constexpr int kSurvCap = 128;   // tokens, and whole tiles, recomputed by waves (more: the whole row)
+
+// The k-th selected cluster of row b and its tiles [t0, t1) in the tiling;
+// a contiguous tile shared with the previous selected cluster is left to it.
+__device__ __forceinline__ void cert_tiles(const CertArgs& f, int b, int k, int& c, long& t0, long& t1) {
+  c = f.topk[(long)b * f.ldK + k];
+  const int lo = f.offsets[c], hi = f.offsets[c + 1];
+  if (f.tpc > 0) {
+    t0 = (long)c * f.tpc;
+    t1 = t0 + f.tpc;
+    return;
+  }
+  t0 = lo / kWave;
+  t1 = hi > lo ? (long)(hi - 1) / kWave + 1 : t0;
+  if (k > 0 && t1 > t0) {
+    const int pc = f.topk[(long)b * f.ldK + k - 1];
+    const int phi = f.offsets[pc + 1], plo = f.offsets[pc];
+    if (phi > plo && (phi - 1) / kWave == t0) ++t0;
+  }
+}
+
+// fn(t) for every tile of row b's selected clusters, spread over the
+// workgroup: per 256 clusters, a scan of their tile counts, then thread i
+// takes the tiles i, i + 256, ... of the run (found by binary search).  A
+// tile shared by two selected clusters with an empty one between them comes
+// twice, which the callers allow.  Every thread of the block must call it.
+template <typename F>
+__device__ __forceinline__ void for_row_tiles(const CertArgs& f, int b, uint32_t* pre_sh, long* t0_sh,
+                                              uint32_t* scan_sh, F&& fn) {
+  const int tid = threadIdx.x;
+  for (int k0 = 0; k0 < f.K; k0 += kCertThreads) {
+    const int k = k0 + tid;
+    int c = 0;
+    long t0 = 0, t1 = 0;
+    if (k < f.K) cert_tiles(f, b, k, c, t0, t1);
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<kCertWaves>((uint32_t)(t1 - t0), scan_sh, &tot);
+    pre_sh[tid] = pre;
+    t0_sh[tid] = t0;
+    __syncthreads();
+    const int last = min(kCertThreads, f.K - k0) - 1;
+    for (uint32_t i = tid; i < tot; i += kCertThreads) {
+      // the last cluster whose run starts at or before i (empty ones share
+      // the next one's start and are passed over)
+      int lo = 0, hi = last;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre_sh[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      fn(t0_sh[lo] + (long)(i - pre_sh[lo]));
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per row.  M, the largest L over the row's records, is a
+// lower bound of the row's best canonical key; a token can win only if its
+// U reaches M.  The records name each tile's best token (with its U) and
+// bound its other candidates' U: when only one named token reaches M and
+// no tile's others can, that token wins outright.  Otherwise the named
+// tokens that reach M get canonical keys (a wave each, by the exact-sum
+// test) and the tiles whose others can reach M are recomputed whole (a lane
+// per slot); past kSurvCap of either, or with a non-finite record, every
+// candidate of the row is recomputed (a thread per slot).  The row's token
+// is the largest (key, ~token); -1 with no candidate.
+template <typename T>
+__global__ __launch_bounds__(kCertThreads) void finalize_cert_kernel(CertArgs f) {
+  constexpr bool F8 = std::is_same<T, uint8_t>::value;
+  constexpr int PV = Elem<T>::kPerVec;
+  extern __shared__ __attribute__((aligned(16))) unsigned char cert_dyn[];
+  uint16_t* hrow = reinterpret_cast<uint16_t*>(cert_dyn);   // [d]
+  __shared__ uint32_t surv[kSurvCap];      // (tile << 6) | slot of named tokens that reach M
+  __shared__ uint32_t fullt[kSurvCap];     // tiles whose other candidates reach M
+  __shared__ unsigned long long wbest[kCertWaves];
+  __shared__ uint32_t wM[kCertWaves];
+  __shared__ uint32_t nsurv, nfull, nbad;
+  __shared__ uint32_t tile_pre[kCertThreads];
+  __shared__ long tile_t0[kCertThreads];
+  __shared__ uint32_t scan_sh[kCertWaves];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int d = f.d;
+  for (int k = tid; k < d; k += kCertThreads) hrow[k] = f.h[(long)b * d + k];
+  if (tid == 0) {
+    nsurv = 0u;
+    nfull = 0u;
+    nbad = 0u;
+  }
+  const v4u* rec = f.crec + (long)b * f.n_tiles;
+  uint32_t M = 0u, bad = 0u;
+  for_row_tiles(f, b, tile_pre, tile_t0, scan_sh, [&](long t) {
+    const v4u rc = rec[t];
+    M = max(M, rc[0]);
+    bad |= rc[3] >> 6;
+  });
+  M = __ockl_wfred_max_u32(M);
+  bad = __ockl_wfred_max_u32(bad);
+  if (lane == 0) {
+    wM[wv] = M;
+    if (bad) nbad = 1u;
+  }
+  __syncthreads();
+  M = wM[0];
+#pragma unroll
+  for (int i = 1; i < kCertWaves; ++i) M = max(M, wM[i]);
+  bool whole = nbad != 0u;
+  if (!whole) {
+    for_row_tiles(f, b, tile_pre, tile_t0, scan_sh, [&](long t) {
+      const v4u rc = rec[t];
+      if (rc[1] >= M) {
+        const uint32_t at = atomicAdd(&nsurv, 1u);
+        if (at < (uint32_t)kSurvCap) surv[at] = ((uint32_t)t << 6) | (rc[3] & 63u);
+      }
+      if (rc[2] >= M) {
+        const uint32_t at = atomicAdd(&nfull, 1u);
+        if (at < (uint32_t)kSurvCap) fullt[at] = (uint32_t)t;
+      }
+    });
+  }
+  __syncthreads();
+  const uint32_t ns = nsurv, nf = nfull;
+  whole = whole || ns > (uint32_t)kSurvCap || nf > (uint32_t)kSurvCap;
+  unsigned long long best = 0ull;
+  if (!whole && ns == 1u && nf == 0u) {
+    // one token can reach the best lower bound: it wins
+    const uint32_t w = surv[0];
+    const uint32_t tok = (uint32_t)f.ttok[(long)(w >> 6) * kWave + (w & 63u)];
+    best = (1ull << 32) | (unsigned long long)(0xFFFFFFFFu - tok);
+  } else if (!whole) {
+    for (uint32_t i = wv; i < ns; i += kCertWaves) {
+      const uint32_t w = surv[i];
+      const long t = w >> 6;
+      const int tau = (int)(w & 63u);
+      const v4u* row = f.ET + t * (d / PV) * kWave + tau;
+      const uint32_t tok = (uint32_t)f.ttok[t * kWave + tau];
+      const uint32_t key = F8 ? wave_row_key_fp8(row, hrow, d, f.escale[t * kWave + tau])
+                              : wave_row_key(row, hrow, d);
+      best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - tok));
+    }
+    // whole tiles: a lane per slot, the candidates of this row only
+    for (uint32_t i = wv; i < nf; i += kCertWaves) {
+      const long t = fullt[i];
+      const int tok = f.ttok[t * kWave + lane];
+      bool cand = tok >= 0;
+      if (cand && f.tpc == 0) {
+        const int c = f.tcl[t * kWave + lane];
+        cand = ((f.cl_sel[(long)(c / kWave) * kWave + b] >> (c % kWave)) & 1ull) != 0ull;
+      }
+      if (cand) {
+        const v4u* row = f.ET + t * (d / PV) * kWave + lane;
+        const uint32_t key = slot_chain_key<T>(row, hrow, d, F8 ? f.escale[t * kWave + lane] : 1.0f);
+        best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok));
+      }
+    }
+  } else {
+    // every candidate of the row, a thread per slot: the float64 chain in order
+    for (int k = 0; k < f.K; ++k) {
+      const int c = f.topk[(long)b * f.ldK + k];
+      const int lo = f.offsets[c], hi = f.offsets[c + 1];
+      for (int s2 = lo + tid; s2 < hi; s2 += kCertThreads) {
+        const long t = f.tpc > 0 ? (long)c * f.tpc + (s2 - lo) / kWave : s2 / kWave;
+        const int tau = f.tpc > 0 ? (s2 - lo) % kWave : s2 % kWave;
+        const v4u* row = f.ET + t * (d / PV) * kWave + tau;
+        const uint32_t tok = (uint32_t)f.ttok[t * kWave + tau];
+        const uint32_t key = slot_chain_key<T>(row, hrow, d, F8 ? f.escale[t * kWave + tau] : 1.0f);
+        best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - tok));
+      }
+    }
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) wbest[wv] = best;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long m = wbest[0];
+#pragma unroll
+    for (int i = 1; i < kCertWaves; ++i) m = max(m, wbest[i]);
+    f.tokens[b] = m ? (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull)) : -1;
+  }
+}
+
+// Slot norms for the certified argmax: |e| of each packed slot (FP8: the
+// decoded codes' norm times the row scale), float64 then rounded up.
+template <typename T>
+__global__ __launch_bounds__(256) void slot_norm_kernel(const v4u* __restrict__ ET, const float* __restrict__ escale,
+                                                        long n_slots, int d, float* __restrict__ out) {
+  constexpr int PV = Elem<T>::kPerVec;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < n_slots; o += stride) {
+    const long t = o / kWave;
+    const int tau = (int)(o % kWave);
+    const v4u* row = ET + t * (d / PV) * kWave + tau;
+    double ss = 0.0;
+    for (int v = 0; v < d / PV; ++v) {
+      double x[PV];
+      widen(row[(long)v * kWave], x, T());
+#pragma unroll
+      for (int e = 0; e < PV; ++e) ss = fma(x[e], x[e], ss);
+    }
+    double nrm = sqrt(ss) * (1.0 + 0x1p-40);
+    if (std::is_same<T, uint8_t>::value) nrm *= (double)escale[o] * (1.0 + 0x1p-50);
+    out[o] = f32_up(nrm);
   }
 }
 
@@ -1989,6 +2517,8 @@ hipError_t launch_scores(const PassArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+static bool cert_gather(const PassArgs& a);
+
 template <int EPT>
 static void launch_topk_ept(const TopkArgs& t, int G, int mode, bool approx, hipStream_t s) {
   // the ranks (top-m on equal clusters) come from their own instantiation,
@@ -2057,6 +2587,12 @@ static int gather_split_shift_ragged(int B) { return B >= 16 ? kRaggedSplitShift
 // 19.6; B=8 22.8 → 23.2 and B=16 24.2 → 25.8 the other way).
 constexpr int kGatherByRowMaxB = 4;
 
+// The certified matrix-core argmax runs on the tile grid only: by row a
+// wave holds a single row, which the float64 chain serves better.
+static bool cert_gather(const PassArgs& a) {
+  return a.cert && !(a.t.tpc > 0 && a.B <= kGatherByRowMaxB);
+}
+
 template <typename T, int MODE>
 static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   GatherArgs g;
@@ -2086,6 +2622,28 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.ldK = a.ldK;
   g.K = a.K;
   g.by_row = a.t.tpc > 0 && a.B <= kGatherByRowMaxB && g.split_shift == 0;
+  g.enorm = a.t.enorm;
+  g.crec = reinterpret_cast<v4u*>(a.crec);
+  if constexpr (MODE == kArgmax && !std::is_same<T, float>::value) {
+    if (cert_gather(a)) {
+      // one wave a tile: a pass holds 16 rows
+      g.split_shift = 0;
+      const dim3 cgrid((unsigned)a.t.n_tiles);
+      auto go_cert = [&](auto kern) {
+        if (a.probe_start && a.probe_stop)
+          hipExtLaunchKernelGGL(kern, cgrid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);
+        else
+          hipLaunchKernelGGL(kern, cgrid, dim3(64), 0, s, g);
+      };
+      switch (a.d / 32) {
+        case 8: go_cert(gather_cert_kernel<T, 8>); break;
+        case 16: go_cert(gather_cert_kernel<T, 16>); break;
+        case 32: go_cert(gather_cert_kernel<T, 32>); break;
+        default: go_cert(gather_cert_kernel<T, 0>); break;
+      }
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(g.by_row ? (unsigned)(a.B * a.K * a.t.tpc)
                            : a.t.n_tiles > 0 ? (unsigned)a.t.n_tiles << g.split_shift : 1u);
   auto go = [&](auto kern) {
@@ -2186,9 +2744,33 @@ hipError_t launch_finalize(const PassArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL(finalize_embed_kernel<float>, dim3(a.B), dim3(kEmbedThreads), 0, s,
                          a.amax, a.tokens, e);
+  } else if (cert_gather(a)) {
+    CertArgs f{reinterpret_cast<const v4u*>(a.crec), a.t.n_tiles, static_cast<const v4u*>(a.t.ET),
+               a.t.escale, a.t.ttok, a.t.tcl, a.cl_sel, static_cast<const uint16_t*>(a.h), a.d,
+               a.topk, a.ldK, a.K, a.t.offsets, a.t.tpc, a.tokens};
+    const size_t lds = (size_t)2 * a.d;
+    if (a.t.slab == 1)
+      hipLaunchKernelGGL(finalize_cert_kernel<uint8_t>, dim3(a.B), dim3(kCertThreads), lds, s, f);
+    else
+      hipLaunchKernelGGL(finalize_cert_kernel<uint16_t>, dim3(a.B), dim3(kCertThreads), lds, s, f);
   } else {
     hipLaunchKernelGGL(finalize_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.amax, a.B, a.tokens);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_norms(const void* ET, int slab, const float* escale, long n_tiles, int d,
+                             float* out, hipStream_t s) {
+  const long n = n_tiles * kWave;
+  if (n == 0) return hipSuccess;
+  long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (slab == 1)
+    hipLaunchKernelGGL(slot_norm_kernel<uint8_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const v4u*>(ET), escale, n, d, out);
+  else
+    hipLaunchKernelGGL(slot_norm_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const v4u*>(ET), escale, n, d, out);
   return hipGetLastError();
 }
 

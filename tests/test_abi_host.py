@@ -121,9 +121,10 @@ def test_create_ragged_and_sizes(lib):
         # an empty tile list (clusters of 0, 100, 30 and 126 tokens hold 0, 2,
         # 1 and 2 tiles, so the tiling is the contiguous one: V / 64 = 4
         # tiles) + the tiles' slot tokens (4 x 64 ints) and clusters (4 x 64
-        # shorts), each rounded up to 256 bytes, + packed embeddings (4 tiles)
-        # and centroids (1 tile) of 64 rows x 64 bf16
-        assert n.value == 256 + 256 + 1024 + 256 + 4 * 256 + 2 * 256 + 4 * 8192 + 8192
+        # shorts), each rounded up to 256 bytes, + packed embeddings (4 tiles),
+        # their slots' norms (4 x 64 floats) and centroids (1 tile) of 64 rows
+        # x 64 bf16
+        assert n.value == 256 + 256 + 1024 + 256 + 4 * 256 + 2 * 256 + 4 * 8192 + 4 * 256 + 8192
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOPK, ctypes.byref(n)) == 0
         assert n.value == 0
         sizes = {}
@@ -132,7 +133,9 @@ def test_create_ragged_and_sizes(lib):
             sizes[op] = n.value
             assert n.value % 256 == 0
         assert sizes[_ffi.CE_OP_SCORE] == 0
-        assert 0 < sizes[_ffi.CE_OP_TOP_TOKENS] <= sizes[_ffi.CE_OP_MASKED_LOGITS]
+        # top tokens on a ragged bf16 head adds the certified argmax's
+        # records: one of 16 bytes per (row, tile), 8 rows x 4 tiles
+        assert sizes[_ffi.CE_OP_TOP_TOKENS] == sizes[_ffi.CE_OP_MASKED_LOGITS] + 8 * 4 * 16
         # more than one pass of rows needs no more workspace than one full pass
         assert lib.ce_workspace_bytes(h, 64, 2, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == 0
         one = n.value
@@ -145,7 +148,7 @@ def test_create_ragged_and_sizes(lib):
         # top-m: the masked sizes plus its segment lists (tiles the K largest
         # clusters touch: 2 + 2 for K=2, of one 64-token tile's keys each)
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_M, ctypes.byref(n)) == 0
-        assert n.value >= sizes[_ffi.CE_OP_TOP_TOKENS] + 8 * 4 * 64 * 8
+        assert n.value >= sizes[_ffi.CE_OP_MASKED_LOGITS] + 8 * 4 * 64 * 8
     finally:
         lib.ce_head_destroy(h)
 

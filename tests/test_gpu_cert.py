@@ -1,0 +1,105 @@
+"""GPU parity of the certified matrix-core argmax (projection="mfma" forces
+it on every tile-grid call of a bf16 head) against the oracle.
+
+The gather bounds each matrix-core sum and the finalize recomputes canonical
+keys only where the bounds leave the winner open, so the tokens must equal
+the oracle's bit for bit on every path of the finalize: a single token that
+alone reaches the best lower bound, named tokens recomputed by waves, whole
+tiles recomputed a lane per slot, and whole rows (tied logits, zero rows).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8_slabs as f8
+from tests.gpu_helpers import make_head, rows, to_device, torch_mod
+from workloads import make_random
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8_head(w, max_B, max_K):
+    from centroid_masked_sparse_amd import Head
+    equal = np.all(np.diff(w.offsets) == w.V // w.Nc) and w.V % w.Nc == 0
+    return Head(to_device(w.C, w.dtype), to_device(w.E, w.dtype), w.tos,
+                None if equal else w.offsets, max_B=max_B, max_K=max_K, slabs="fp8",
+                projection="mfma")
+
+
+def _tokens(head, w, B, K):
+    torch = torch_mod()
+    tk = torch.full((B, K), -7, dtype=torch.int32, device="cuda:0")
+    tok = head.top_tokens(to_device(rows(w, B), w.dtype), K, topk_out=tk)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), tk.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed,d,V,Nc,K,B,ragged", [
+    (201, 64, 8192, 64, 4, 5, False),       # smallest tile-grid batch
+    (202, 128, 20000, 100, 6, 16, True),     # ragged: shared tiles, tiny clusters
+    (203, 256, 16384, 128, 8, 64, False),
+    (204, 512, 12000, 90, 5, 64, True),      # many rows per tile: several passes
+    (205, 320, 8192, 64, 3, 70, False),      # generic pipeline, two passes of rows
+    (206, 1024, 8192, 128, 16, 33, False),
+])
+def test_bf16_heads(seed, d, V, Nc, K, B, ragged):
+    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)
+    head = make_head(w, max_B=B, max_K=K, projection="mfma")
+    tok, tk = _tokens(head, w, B, K)
+    tok_o, sel_o, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
+    assert tk.tolist() == sel_o.tolist()
+    assert tok.tolist() == tok_o.tolist()
+
+
+@pytest.mark.parametrize("seed,d,V,Nc,K,B,ragged", [
+    (211, 128, 8192, 64, 4, 9, False),
+    (212, 64, 3000, 40, 3, 17, True),
+    (213, 512, 5000, 50, 2, 70, True),
+])
+def test_fp8_heads(seed, d, V, Nc, K, B, ragged):
+    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)
+    head = _fp8_head(w, max_B=B, max_K=K)
+    tok, tk = _tokens(head, w, B, K)
+    codes, sc = f8.quantize_rows(w.E)
+    tok_o, sel_o = f8.top_tokens_fp8(rows(w, B), w.C, codes, sc, w.offsets, w.tos, K)
+    assert tk.tolist() == sel_o.tolist()
+    assert tok.tolist() == tok_o.tolist()
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_near_ties_and_exact_ties(ragged):
+    """Embedding rows drawn from a pool of 4, half of them nudged by one bf16
+    ulp in one dim: every row's best logit is shared by many tokens (whole
+    tiles and whole rows recomputed) or missed by a hair (named tokens
+    recomputed); a zero row ties every candidate at +0."""
+    w = make_random(221, d=128, V=16384, Nc=64, dtype="bf16", rows=64, ragged=ragged)
+    rng = np.random.default_rng(222)
+    P = w.E[rng.integers(0, w.V, size=4)]
+    E = np.ascontiguousarray(P[rng.integers(0, 4, size=w.V)])
+    nudge = rng.random(w.V) < 0.5
+    E[nudge, 7] = E[nudge, 7] + 1            # next bf16 bit pattern: one ulp away
+    h = w.h.copy()
+    h[3] = 0
+    w = dataclasses.replace(w, E=E, h=h)
+    B, K = 64, 4
+    head = make_head(w, max_B=B, max_K=K, projection="mfma")
+    tok, tk = _tokens(head, w, B, K)
+    tok_o, sel_o, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
+    assert tk.tolist() == sel_o.tolist()
+    assert tok.tolist() == tok_o.tolist()
+
+
+def test_exact_and_certified_agree_on_repeated_calls():
+    """The records need no clearing: calls with different rows on one
+    workspace give the oracle's tokens each time."""
+    w = make_random(231, d=512, V=16384, Nc=128, dtype="bf16", rows=64, ragged=True)
+    B, K = 24, 6
+    head = make_head(w, max_B=64, max_K=K, projection="mfma")
+    for lo in (0, 40, 17):
+        hb = np.ascontiguousarray(w.h[lo:lo + B])
+        tok = head.top_tokens(to_device(hb, w.dtype), K)
+        tok_o, _, _ = oracle.top_tokens(hb, w.C, w.E, w.offsets, w.tos, K, w.dtype)
+        assert tok.cpu().numpy().tolist() == tok_o.tolist(), lo
