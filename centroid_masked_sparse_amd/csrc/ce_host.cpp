@@ -103,7 +103,7 @@ bool cert_head(const ce_head* h) {
 // Nc = 2048) stays exact up to B = 64.
 constexpr long long kMfmaMinMacs = 1ll << 27;
 
-Layout make_layout(const ce_head* h, int B, int K, int op) {
+Layout make_layout(const ce_head* h, int B, int K, int op, bool allow_cert = true) {
   Layout L;
   const size_t nb = (size_t)std::min(B, ce::kPassRows);
   size_t off = 0;
@@ -121,7 +121,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op) {
   L.cl_sel = take(((size_t)h->Nc + 63) / 64 * ce::kPassRows * sizeof(unsigned long long));
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
   L.amax = take(ce::kArgWords * sizeof(unsigned long long));
-  if (op == CE_OP_TOP_TOKENS && cert_head(h)) {
+  if (op == CE_OP_TOP_TOKENS && allow_cert && cert_head(h)) {
     L.cert = true;
     L.crec = take(nb * (size_t)h->n_tiles * 16);
   }
@@ -247,7 +247,7 @@ ce_status check_draft(const ce_head* h, const void* x, int B, const DraftArgs& d
 ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* out,
                      int32_t* topk_ids, void* ws, size_t ws_bytes, hipStream_t stream,
                      int m = 0, float* out2 = nullptr, const DraftArgs* draft = nullptr,
-                     bool dry = false) {
+                     bool dry = false, bool allow_cert = true) {
   ce_status st = check_call(h, hin, B, K, true);
   if (st != CE_SUCCESS) return st;
   if (op == CE_OP_DRAFT_STEP) {
@@ -266,7 +266,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
   if (!aligned(hin, 16) || !aligned(out, op == CE_OP_MASKED_LOGITS ? 16 : 4) || !aligned(ws, 256) ||
       (topk_ids && !aligned(topk_ids, 4)) || (out2 && !aligned(out2, 4)))
     return fail(CE_ERR_MISALIGNED, "h and logits need 16-byte, ws 256-byte alignment");
-  const Layout L = make_layout(h, B, K, op);
+  const Layout L = make_layout(h, B, K, op, allow_cert);
   if (ws_bytes < L.total) return fail(CE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than ce_workspace_bytes");
   if (dry) return CE_SUCCESS;   // arguments checked, nothing enqueued
 
@@ -615,7 +615,10 @@ ce_status ce_top_tokens_static(ce_head_t head, const void* h, int32_t B, int32_t
                                int32_t* topk_ids_or_null, hipStream_t stream) {
   ce_status st = check_call(head, h, B, K, true);
   if (st != CE_SUCCESS) return st;
-  const size_t need = make_layout(head, B, K, CE_OP_TOP_TOKENS).total;
+  // the certified argmax's records where they fit, else the float64 dot
+  // (the same tokens)
+  const bool cert = make_layout(head, B, K, CE_OP_TOP_TOKENS).total <= ce::kStaticScratchBytes;
+  const size_t need = make_layout(head, B, K, CE_OP_TOP_TOKENS, cert).total;
   if (need > ce::kStaticScratchBytes)
     return fail(CE_ERR_UNSUPPORTED, "this call needs " + std::to_string(need) +
                                         " bytes of workspace; the static scratch holds " +
@@ -626,7 +629,7 @@ ce_status ce_top_tokens_static(ce_head_t head, const void* h, int32_t B, int32_t
   const hipError_t e = ce::static_scratch(&ws);
   if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
   return run_sparse(head, CE_OP_TOP_TOKENS, h, B, K, tokens, topk_ids_or_null, ws,
-                    ce::kStaticScratchBytes, stream);
+                    ce::kStaticScratchBytes, stream, 0, nullptr, nullptr, false, cert);
 }
 
 ce_status ce_masked_logits(ce_head_t head, const void* h, int32_t B, int32_t K, float* logits,

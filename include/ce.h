@@ -92,20 +92,30 @@ typedef enum ce_slab {
   CE_SLAB_FP8_E4M3 = 1
 } ce_slab;
 
-/* Centroid projection of the fused calls (ce_head_desc.projection).  The
- * results are the same either way; only the time differs.
- *   CE_PROJ_AUTO   fp32 heads: CE_PROJ_EXACT; bf16 heads: per pass of rows,
- *                  CE_PROJ_MFMA when B*Nc*d >= 2^27 multiply-adds, where it
- *                  is the faster, else CE_PROJ_EXACT
- *   CE_PROJ_EXACT  every centroid score is the canonical key (a float64
- *                  chain) before the top-K
- *   CE_PROJ_MFMA   bf16 heads only: the matrix cores' fp32 sums, each within
- *                  a bound E of its canonical key (from |h| and the largest
- *                  centroid norm), and a top-K that recomputes canonical keys
- *                  wherever E leaves the K-th place open, so the selected
- *                  centroids are exactly those of CE_PROJ_EXACT
+/* Matrix-core use of the fused calls (ce_head_desc.projection): the
+ * centroid projection, and the sparse dot of ce_top_tokens.  The results are
+ * the same either way; only the time differs.
+ *   CE_PROJ_AUTO   fp32 heads: CE_PROJ_EXACT.  bf16 heads: the projection
+ *                  per pass of rows by matrix cores when B*Nc*d >= 2^27
+ *                  multiply-adds, where it is the faster; ce_top_tokens'
+ *                  dot by matrix cores for d >= 512 or clusters of unequal
+ *                  tile counts (above 4 rows on equal ones), else exact
+ *   CE_PROJ_EXACT  every score and logit is the canonical key (a float64
+ *                  chain) before it is compared
+ *   CE_PROJ_MFMA   bf16 heads only, everywhere it applies: the projection is
+ *                  the matrix cores' fp32 sums, each within a bound E of its
+ *                  canonical key (from |h| and the largest centroid norm),
+ *                  with a top-K that recomputes canonical keys wherever E
+ *                  leaves the K-th place open; ce_top_tokens' candidate
+ *                  logits likewise (E from |h| and each slot's |e|), with a
+ *                  finalize that recomputes canonical keys wherever the
+ *                  bounds leave the argmax open.  The selected centroids and
+ *                  tokens are exactly those of CE_PROJ_EXACT.  Batches of at
+ *                  most 4 rows on clusters of equal tile counts keep the
+ *                  float64 dot.
  * ce_score_centroids (whose output is the keys) and ce_draft_step always
- * compute canonical scores. */
+ * compute canonical scores; ce_masked_logits and ce_top_m always compute
+ * canonical logits. */
 typedef enum ce_projection {
   CE_PROJ_AUTO = 0,
   CE_PROJ_EXACT = 1,
@@ -237,8 +247,10 @@ ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K,
  * streams, or from several threads without ordering) race and must not be
  * issued; calls ordered on one stream are safe.  The array's content is not
  * needed from one call to the next (every region is written before it is
- * read).  Errors: as ce_top_tokens, plus UNSUPPORTED when the call's
- * workspace (ce_workspace_bytes(head, B, K, CE_OP_TOP_TOKENS)) exceeds
+ * read).  When the matrix-core argmax's records (part of
+ * ce_workspace_bytes(head, B, K, CE_OP_TOP_TOKENS)) would not fit, the call
+ * takes the float64 dot instead, with the same tokens.  Errors: as
+ * ce_top_tokens, plus UNSUPPORTED when even that workspace exceeds
  * CE_STATIC_SCRATCH_BYTES, HIP if the array's address cannot be found. */
 #define CE_STATIC_SCRATCH_BYTES (4u << 20)
 ce_status ce_top_tokens_static(ce_head_t head, const void* h, int32_t B, int32_t K,

@@ -70,3 +70,25 @@ def test_static_scratch_rejects_too_large_a_call():
     assert (out.cpu().numpy() == -9).all()
     # a smaller K fits and matches
     _compare(head, r, 64, 300)
+
+
+def test_static_scratch_takes_the_float64_dot_when_records_do_not_fit():
+    """A ragged head of 4096 tiles takes the matrix-core argmax, whose
+    records at B = 64 (64 x 4096 x 16 bytes) alone fill the static scratch:
+    the static call takes the float64 dot instead, with the same tokens as
+    ce_top_tokens (which takes the matrix cores) and the oracle."""
+    import oracle
+    from centroid_masked_sparse_amd import _ffi
+    r = make_random(97, d=64, V=262144, Nc=2048, dtype="bf16", rows=64, ragged=True)
+    head = make_head(r, max_B=64, max_K=4)
+    assert head.workspace_bytes(64, 4, _ffi.CE_OP_TOP_TOKENS) > _ffi.CE_STATIC_SCRATCH_BYTES
+    _compare(head, r, 64, 4)
+    _compare(head, r, 7, 4)
+    tok_o, _, _ = oracle.top_tokens(rows(r, 7), r.C, r.E, r.offsets, r.tos, 4, r.dtype)
+    torch = torch_mod()
+    h = to_device(rows(r, 7), r.dtype)
+    out = torch.full((7,), -9, dtype=torch.int32, device="cuda:0")
+    tk = torch.full((7, 4), -9, dtype=torch.int32, device="cuda:0")
+    assert _static_call(head, h, 4, out, tk) == "CE_SUCCESS"
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == tok_o.tolist()
