@@ -91,17 +91,19 @@ struct Layout {
 // gather 21.7 against 32.9 µs; wide head, d=1024, call 83.8 against 106.7;
 // sweep head, d=256, 23.4 against 20.8 the other way).
 bool cert_head(const ce_head* h) {
-  if (h->dtype != CE_BF16 || h->proj == CE_PROJ_EXACT) return false;
+  // the records carry token ids in 25 bits
+  if (h->dtype != CE_BF16 || h->proj == CE_PROJ_EXACT || h->V > (1 << 25)) return false;
   return h->proj == CE_PROJ_MFMA || h->d >= 512 || h->tpc == 0;
 }
 
 // CE_PROJ_AUTO takes the MFMA projection for a pass of at least this many
 // multiply-adds (B Nc d).  The exact projection costs in proportion to them;
 // the certified top-K adds a few microseconds whatever their number (its
-// band recomputation included), measured as the break-even on the wide head
-// (d = 1024, Nc = 4096: MFMA from B = 32) while the sweep head (d = 256,
-// Nc = 2048) stays exact up to B = 64.
-constexpr long long kMfmaMinMacs = 1ll << 27;
+// band recomputation included).  The sweep head (d = 256, Nc = 2048) stays
+// exact up to B = 64 (2^25), where MFMA measured 1-2 µs slower; the skewed
+// head (d = 512, Nc = 2048) at B = 64 (2^26) takes it: 46.3 -> 42.1 µs per
+// call, with no other benchmark row changed.
+constexpr long long kMfmaMinMacs = 1ll << 26;
 
 Layout make_layout(const ce_head* h, int B, int K, int op, bool allow_cert = true) {
   Layout L;
@@ -122,8 +124,17 @@ Layout make_layout(const ce_head* h, int B, int K, int op, bool allow_cert = tru
   L.best = take(ce::kPassRows * sizeof(unsigned long long));
   L.amax = take(ce::kArgWords * sizeof(unsigned long long));
   if (op == CE_OP_TOP_TOKENS && allow_cert && cert_head(h)) {
+    // one 16-byte record per (row, tile): padded tiling, in the order of
+    // the row's selected clusters (their ranks from the top-K); contiguous,
+    // by tile
     L.cert = true;
-    L.crec = take(nb * (size_t)h->n_tiles * 16);
+    if (h->tpc > 0) {
+      L.crec = take(nb * (size_t)K * h->tpc * 16);
+      L.tm_rank = take(nb * (size_t)h->Nc * sizeof(int16_t));
+      L.has_rank = true;
+    } else {
+      L.crec = take(nb * (size_t)h->n_tiles * 16);
+    }
   }
   if (op == CE_OP_TOP_M) {
     L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);

@@ -1566,7 +1566,8 @@ struct GatherArgs {
   // certified argmax (matrix-core dots): slot norms and the per-(row, tile)
   // bound records
   const float* enorm;           // [n_tiles][64] |e| of each slot (times its FP8 scale), rounded up
-  v4u* crec;                    // [B][n_tiles] per (row, tile): best L, its U, others' U, slot
+  v4u* crec;                    // per (row, tile): best L, its U, others' U, token and slot
+  const int16_t* crank;         // padded tiling: [B][ldR] rank of each selected centroid
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -1803,11 +1804,14 @@ __device__ __forceinline__ float cert_bound(float lt, float A, float beta, float
 //
 // Each (token, row) sum gets the bound E of cert_bound (|h| from the same
 // loads, |e| from the slot table): its canonical key lies in [L, U] =
-// [l~ - E, l~ + E].  For each of its rows the wave writes one record at
-// (row, tile), with no atomics: the largest L among the tile's candidates,
-// that token's U and slot, and the largest U of the tile's other
-// candidates.  Every (row, tile) pair of a row's selected clusters is
-// written by exactly one wave, so the records need no clearing.
+// [l~ - E, l~ + E].  For each of its rows the wave writes one record, with
+// no atomics: the largest L among the tile's candidates, that token's U,
+// the largest U of the tile's other candidates, and the token and its slot
+// ((token << 7) | (non-finite << 6) | slot).  The record's place is fixed
+// (padded tiling: the cluster's rank in the row's selection times tpc plus
+// the tile in the cluster, so a row's records are contiguous; contiguous
+// tiling: the tile).  Every (row, tile) pair of a row's selected clusters
+// is written by exactly one wave, so the records need no clearing.
 template <typename T, int NKB>
 __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
   constexpr bool F8 = std::is_same<T, uint8_t>::value;
@@ -1982,8 +1986,17 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
         btau = otau;
       }
     }
-    if (kq == 0 && myrow >= 0)
-      a.crec[(long)myrow * a.n_tiles + t] = v4u{bl, bu, u2, btau | (bad << 6)};
+    if (kq == 0 && myrow >= 0) {
+      // padded tiling: the row's record sits at (rank of the cluster in the
+      // row's selection) * tpc + tile in cluster; contiguous: at the tile
+      const long at = a.tpc > 0 ? (long)myrow * a.K * a.tpc +
+                                      (long)a.crank[(long)myrow * a.ldR + cl] * a.tpc + (t - cl * a.tpc)
+                                : (long)myrow * a.n_tiles + t;
+      // the token again from the tile's row of ids (read at the start, so
+      // a cache hit), rather than sixteen ids held through the stream
+      const uint32_t btok = (uint32_t)a.ttok[tb + btau];
+      a.crec[at] = v4u{bl, bu, u2, (btok << 7) | (bad << 6) | btau};
+    }
   }
 }
 
@@ -2082,42 +2095,71 @@ __device__ __forceinline__ void for_row_tiles(const CertArgs& f, int b, uint32_t
 // lower bound of the row's best canonical key; a token can win only if its
 // U reaches M.  The records name each tile's best token (with its U) and
 // bound its other candidates' U: when only one named token reaches M and
-// no tile's others can, that token wins outright.  Otherwise the named
-// tokens that reach M get canonical keys (a wave each, by the exact-sum
-// test) and the tiles whose others can reach M are recomputed whole (a lane
-// per slot); past kSurvCap of either, or with a non-finite record, every
+// no tile's others can, that token wins outright, with no other load (the
+// usual case; on the padded tiling the row's records are one contiguous
+// run, read once).  Otherwise the hidden row goes to LDS, the named tokens
+// that reach M get canonical keys (a wave each, by the exact-sum test) and
+// the tiles whose others can reach M are recomputed whole (a lane per
+// slot); past kSurvCap of either, or with a non-finite record, every
 // candidate of the row is recomputed (a thread per slot).  The row's token
 // is the largest (key, ~token); -1 with no candidate.
 template <typename T>
 __global__ __launch_bounds__(kCertThreads) void finalize_cert_kernel(CertArgs f) {
   constexpr bool F8 = std::is_same<T, uint8_t>::value;
   constexpr int PV = Elem<T>::kPerVec;
+  constexpr int R = 4;   // records a thread holds from the first pass to the second
   extern __shared__ __attribute__((aligned(16))) unsigned char cert_dyn[];
   uint16_t* hrow = reinterpret_cast<uint16_t*>(cert_dyn);   // [d]
-  __shared__ uint32_t surv[kSurvCap];      // (tile << 6) | slot of named tokens that reach M
-  __shared__ uint32_t fullt[kSurvCap];     // tiles whose other candidates reach M
+  __shared__ uint32_t surv[kSurvCap];      // (record << 6) | slot of named tokens that reach M
+  __shared__ uint32_t fullt[kSurvCap];     // records whose tile's other candidates reach M
   __shared__ unsigned long long wbest[kCertWaves];
   __shared__ uint32_t wM[kCertWaves];
-  __shared__ uint32_t nsurv, nfull, nbad;
+  __shared__ uint32_t nsurv, nfull, nbad, tok0;
   __shared__ uint32_t tile_pre[kCertThreads];
   __shared__ long tile_t0[kCertThreads];
   __shared__ uint32_t scan_sh[kCertWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int d = f.d;
-  for (int k = tid; k < d; k += kCertThreads) hrow[k] = f.h[(long)b * d + k];
+  const bool padded = f.tpc > 0;
+  const int nrec = padded ? f.K * f.tpc : 0;
+  const v4u* prec = f.crec + (long)b * nrec;         // padded: the row's records in order
+  const v4u* trec = f.crec + (long)b * f.n_tiles;    // contiguous: by tile
   if (tid == 0) {
     nsurv = 0u;
     nfull = 0u;
     nbad = 0u;
   }
-  const v4u* rec = f.crec + (long)b * f.n_tiles;
+  // the tile of record i (padded), or the tile itself (contiguous)
+  auto tile_of = [&](uint32_t i) -> long {
+    return padded ? (long)f.topk[(long)b * f.ldK + (int)(i / (uint32_t)f.tpc)] * f.tpc + (long)(i % (uint32_t)f.tpc)
+                  : (long)i;
+  };
+  v4u cache[R];
   uint32_t M = 0u, bad = 0u;
-  for_row_tiles(f, b, tile_pre, tile_t0, scan_sh, [&](long t) {
-    const v4u rc = rec[t];
-    M = max(M, rc[0]);
-    bad |= rc[3] >> 6;
-  });
+  if (padded) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int i = tid + kCertThreads * j;
+      cache[j] = i < nrec ? prec[i] : v4u{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      M = max(M, cache[j][0]);
+      bad |= (cache[j][3] >> 6) & 1u;
+    }
+    for (int i = tid + kCertThreads * R; i < nrec; i += kCertThreads) {
+      const v4u rc = prec[i];
+      M = max(M, rc[0]);
+      bad |= (rc[3] >> 6) & 1u;
+    }
+  } else {
+    for_row_tiles(f, b, tile_pre, tile_t0, scan_sh, [&](long t) {
+      const v4u rc = trec[t];
+      M = max(M, rc[0]);
+      bad |= (rc[3] >> 6) & 1u;
+    });
+  }
   M = __ockl_wfred_max_u32(M);
   bad = __ockl_wfred_max_u32(bad);
   if (lane == 0) {
@@ -2129,18 +2171,29 @@ __global__ __launch_bounds__(kCertThreads) void finalize_cert_kernel(CertArgs f)
 #pragma unroll
   for (int i = 1; i < kCertWaves; ++i) M = max(M, wM[i]);
   bool whole = nbad != 0u;
+  // the named tokens and the tiles that can reach M
+  auto consider = [&](const v4u& rc, uint32_t i) {
+    if (rc[1] >= M) {
+      const uint32_t at = atomicAdd(&nsurv, 1u);
+      if (at < (uint32_t)kSurvCap) surv[at] = (i << 6) | (rc[3] & 63u);
+      if (at == 0u) tok0 = rc[3] >> 7;
+    }
+    if (rc[2] >= M) {
+      const uint32_t at = atomicAdd(&nfull, 1u);
+      if (at < (uint32_t)kSurvCap) fullt[at] = i;
+    }
+  };
   if (!whole) {
-    for_row_tiles(f, b, tile_pre, tile_t0, scan_sh, [&](long t) {
-      const v4u rc = rec[t];
-      if (rc[1] >= M) {
-        const uint32_t at = atomicAdd(&nsurv, 1u);
-        if (at < (uint32_t)kSurvCap) surv[at] = ((uint32_t)t << 6) | (rc[3] & 63u);
+    if (padded) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int i = tid + kCertThreads * j;
+        if (i < nrec) consider(cache[j], (uint32_t)i);
       }
-      if (rc[2] >= M) {
-        const uint32_t at = atomicAdd(&nfull, 1u);
-        if (at < (uint32_t)kSurvCap) fullt[at] = (uint32_t)t;
-      }
-    });
+      for (int i = tid + kCertThreads * R; i < nrec; i += kCertThreads) consider(prec[i], (uint32_t)i);
+    } else {
+      for_row_tiles(f, b, tile_pre, tile_t0, scan_sh, [&](long t) { consider(trec[t], (uint32_t)t); });
+    }
   }
   __syncthreads();
   const uint32_t ns = nsurv, nf = nfull;
@@ -2148,47 +2201,49 @@ __global__ __launch_bounds__(kCertThreads) void finalize_cert_kernel(CertArgs f)
   unsigned long long best = 0ull;
   if (!whole && ns == 1u && nf == 0u) {
     // one token can reach the best lower bound: it wins
-    const uint32_t w = surv[0];
-    const uint32_t tok = (uint32_t)f.ttok[(long)(w >> 6) * kWave + (w & 63u)];
-    best = (1ull << 32) | (unsigned long long)(0xFFFFFFFFu - tok);
-  } else if (!whole) {
-    for (uint32_t i = wv; i < ns; i += kCertWaves) {
-      const uint32_t w = surv[i];
-      const long t = w >> 6;
-      const int tau = (int)(w & 63u);
-      const v4u* row = f.ET + t * (d / PV) * kWave + tau;
-      const uint32_t tok = (uint32_t)f.ttok[t * kWave + tau];
-      const uint32_t key = F8 ? wave_row_key_fp8(row, hrow, d, f.escale[t * kWave + tau])
-                              : wave_row_key(row, hrow, d);
-      best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - tok));
-    }
-    // whole tiles: a lane per slot, the candidates of this row only
-    for (uint32_t i = wv; i < nf; i += kCertWaves) {
-      const long t = fullt[i];
-      const int tok = f.ttok[t * kWave + lane];
-      bool cand = tok >= 0;
-      if (cand && f.tpc == 0) {
-        const int c = f.tcl[t * kWave + lane];
-        cand = ((f.cl_sel[(long)(c / kWave) * kWave + b] >> (c % kWave)) & 1ull) != 0ull;
-      }
-      if (cand) {
-        const v4u* row = f.ET + t * (d / PV) * kWave + lane;
-        const uint32_t key = slot_chain_key<T>(row, hrow, d, F8 ? f.escale[t * kWave + lane] : 1.0f);
-        best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok));
-      }
-    }
-  } else {
-    // every candidate of the row, a thread per slot: the float64 chain in order
-    for (int k = 0; k < f.K; ++k) {
-      const int c = f.topk[(long)b * f.ldK + k];
-      const int lo = f.offsets[c], hi = f.offsets[c + 1];
-      for (int s2 = lo + tid; s2 < hi; s2 += kCertThreads) {
-        const long t = f.tpc > 0 ? (long)c * f.tpc + (s2 - lo) / kWave : s2 / kWave;
-        const int tau = f.tpc > 0 ? (s2 - lo) % kWave : s2 % kWave;
+    best = (1ull << 32) | (unsigned long long)(0xFFFFFFFFu - tok0);
+  } else if (ns > 0u || whole) {
+    for (int k = tid; k < d; k += kCertThreads) hrow[k] = f.h[(long)b * d + k];
+    __syncthreads();
+    if (!whole) {
+      for (uint32_t i = wv; i < ns; i += kCertWaves) {
+        const uint32_t w = surv[i];
+        const long t = tile_of(w >> 6);
+        const int tau = (int)(w & 63u);
         const v4u* row = f.ET + t * (d / PV) * kWave + tau;
         const uint32_t tok = (uint32_t)f.ttok[t * kWave + tau];
-        const uint32_t key = slot_chain_key<T>(row, hrow, d, F8 ? f.escale[t * kWave + tau] : 1.0f);
+        const uint32_t key = F8 ? wave_row_key_fp8(row, hrow, d, f.escale[t * kWave + tau])
+                                : wave_row_key(row, hrow, d);
         best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - tok));
+      }
+      // whole tiles: a lane per slot, the candidates of this row only
+      for (uint32_t i = wv; i < nf; i += kCertWaves) {
+        const long t = tile_of(fullt[i]);
+        const int tok = f.ttok[t * kWave + lane];
+        bool cand = tok >= 0;
+        if (cand && !padded) {
+          const int c = f.tcl[t * kWave + lane];
+          cand = ((f.cl_sel[(long)(c / kWave) * kWave + b] >> (c % kWave)) & 1ull) != 0ull;
+        }
+        if (cand) {
+          const v4u* row = f.ET + t * (d / PV) * kWave + lane;
+          const uint32_t key = slot_chain_key<T>(row, hrow, d, F8 ? f.escale[t * kWave + lane] : 1.0f);
+          best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)tok));
+        }
+      }
+    } else {
+      // every candidate of the row, a thread per slot: the float64 chain in order
+      for (int k = 0; k < f.K; ++k) {
+        const int c = f.topk[(long)b * f.ldK + k];
+        const int lo = f.offsets[c], hi = f.offsets[c + 1];
+        for (int s2 = lo + tid; s2 < hi; s2 += kCertThreads) {
+          const long t = padded ? (long)c * f.tpc + (s2 - lo) / kWave : s2 / kWave;
+          const int tau = padded ? (s2 - lo) % kWave : s2 % kWave;
+          const v4u* row = f.ET + t * (d / PV) * kWave + tau;
+          const uint32_t tok = (uint32_t)f.ttok[t * kWave + tau];
+          const uint32_t key = slot_chain_key<T>(row, hrow, d, F8 ? f.escale[t * kWave + tau] : 1.0f);
+          best = max(best, ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - tok));
+        }
       }
     }
   }
@@ -2624,6 +2679,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.by_row = a.t.tpc > 0 && a.B <= kGatherByRowMaxB && g.split_shift == 0;
   g.enorm = a.t.enorm;
   g.crec = reinterpret_cast<v4u*>(a.crec);
+  g.crank = a.tm_rank;
   if constexpr (MODE == kArgmax && !std::is_same<T, float>::value) {
     if (cert_gather(a)) {
       // one wave a tile: a pass holds 16 rows

@@ -96,7 +96,7 @@ typedef enum ce_slab {
  * centroid projection, and the sparse dot of ce_top_tokens.  The results are
  * the same either way; only the time differs.
  *   CE_PROJ_AUTO   fp32 heads: CE_PROJ_EXACT.  bf16 heads: the projection
- *                  per pass of rows by matrix cores when B*Nc*d >= 2^27
+ *                  per pass of rows by matrix cores when B*Nc*d >= 2^26
  *                  multiply-adds, where it is the faster; ce_top_tokens'
  *                  dot by matrix cores for d >= 512 or clusters of unequal
  *                  tile counts (above 4 rows on equal ones), else exact
@@ -247,9 +247,9 @@ ce_status ce_top_tokens(ce_head_t head, const void* h, int32_t B, int32_t K,
  * streams, or from several threads without ordering) race and must not be
  * issued; calls ordered on one stream are safe.  The array's content is not
  * needed from one call to the next (every region is written before it is
- * read).  When the matrix-core argmax's records (part of
- * ce_workspace_bytes(head, B, K, CE_OP_TOP_TOKENS)) would not fit, the call
- * takes the float64 dot instead, with the same tokens.  Errors: as
+ * read).  When the matrix-core argmax's records (16 bytes per row and tile,
+ * part of ce_workspace_bytes(head, B, K, CE_OP_TOP_TOKENS)) would not fit,
+ * the call takes the float64 dot instead, with the same tokens.  Errors: as
  * ce_top_tokens, plus UNSUPPORTED when even that workspace exceeds
  * CE_STATIC_SCRATCH_BYTES, HIP if the array's address cannot be found. */
 #define CE_STATIC_SCRATCH_BYTES (4u << 20)
