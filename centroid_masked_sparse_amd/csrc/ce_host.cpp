@@ -78,7 +78,7 @@ size_t elem_bytes(int dtype) { return dtype == CE_BF16 ? 2 : 4; }
 // Workspace regions of one pass (at most ce::kPassRows rows).
 struct Layout {
   size_t scores = 0, topk = 0, cl_sel = 0, best = 0, amax = 0, tm_keys = 0, tm_heads = 0, tm_rank = 0,
-         crec = 0, total = 0;
+         crec = 0, hnorm = 0, total = 0;
   bool has_rank = false;
   bool cert = false;
   int tm_segcap = 0;
@@ -128,6 +128,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op, bool allow_cert = tru
     // the row's selected clusters (their ranks from the top-K); contiguous,
     // by tile
     L.cert = true;
+    L.hnorm = take(ce::kPassRows * sizeof(float));
     if (h->tpc > 0) {
       L.crec = take(nb * (size_t)K * h->tpc * 16);
       L.tm_rank = take(nb * (size_t)h->Nc * sizeof(int16_t));
@@ -217,6 +218,7 @@ void bind_workspace(ce::PassArgs& a, const Layout& L, char* ws) {
   a.ldR = a.Nc;
   a.cert = L.cert;
   a.crec = L.cert ? ws + L.crec : nullptr;
+  a.hnorm = L.cert ? reinterpret_cast<float*>(ws + L.hnorm) : nullptr;
 }
 
 // The draft step's extra operands (ce_draft_step).

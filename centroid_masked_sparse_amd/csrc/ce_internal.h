@@ -72,7 +72,8 @@ struct PassArgs {
   const void* h;          // [B][d] rows of this pass
   bool approx;            // bf16 MFMA projection + certified top-K (else canonical scores)
   bool cert;              // argmax by matrix-core dots + certified finalize (tile grid only)
-  void* crec;             // cert: [B][n_tiles] 16-byte bound records
+  void* crec;             // cert: 16-byte bound records per (row, tile)
+  float* hnorm;           // cert: [kPassRows] each row's |h|, rounded up
   // workspace regions
   float* S;               // [B][ldS] centroid scores
   int ldS;

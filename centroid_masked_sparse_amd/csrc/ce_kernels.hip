@@ -129,6 +129,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// fp32 at or above x (x >= 0): the nearest float, raised one step if below.
+__device__ __forceinline__ float f32_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+
 // Inverse of order_key (a key of -0 does not occur: order_key maps it to +0).
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -973,6 +980,7 @@ struct TopkArgs {
   int d;
   const unsigned long long* cmax;  // largest centroid row norm (bits of a double)
   unsigned long long* stats;       // [0] rows whose band was recomputed, [1] rows recomputed whole
+  float* hnorm;                    // certified argmax: each row's |h|, rounded up (or null)
   // forward: workgroups from `rows` on fill out[fill_split(n), n) with -inf
   int rows;
   float* fill;
@@ -1242,9 +1250,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     v[i] = row[c < Nc ? c : Nc - 1];   // unconditional (clamped) loads
   }
   // APPROX: the largest centroid norm and the hidden row (into LDS, with
-  // its squared norm), loaded beside the scores
+  // its squared norm), loaded beside the scores; the exact scores need the
+  // row's squared norm only for the certified argmax
   unsigned long long cmax_bits = 0;
   double ss = 0.0;
+  if (!APPROX && a.hnorm) {
+#pragma unroll 1
+    for (int k = tid; k < a.d; k += kTopkThreads) {
+      const double f = (double)__uint_as_float((uint32_t)a.h[(long)b * a.d + k] << 16);
+      ss = fma(f, f, ss);
+    }
+  }
   uint16_t* hrow = reinterpret_cast<uint16_t*>(topk_dyn);
   if constexpr (APPROX) {
     cmax_bits = *a.cmax;
@@ -1295,6 +1311,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       dsh[wv] = ss;
       part[0][wv] = mx;
       part[1][wv] = bad;
+    }
+  }
+  if (a.hnorm) {
+    // the row's |h| for the certified argmax: float64 squares of the bf16
+    // elements, summed (within d 2^-53 of the exact sum), rounded up
+    if constexpr (!APPROX) {
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      if (lane == 0) dsh[wv] = ss;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double t2 = 0.0;
+#pragma unroll
+      for (int i = 0; i < kTopkWaves; ++i) t2 += dsh[i];
+      a.hnorm[b] = f32_up(sqrt(t2) * (1.0 + 0x1p-40));
     }
   }
 
@@ -1568,6 +1600,7 @@ struct GatherArgs {
   const float* enorm;           // [n_tiles][64] |e| of each slot (times its FP8 scale), rounded up
   v4u* crec;                    // per (row, tile): best L, its U, others' U, token and slot
   const int16_t* crank;         // padded tiling: [B][ldR] rank of each selected centroid
+  const float* hnorm;           // [B] each row's |h|, rounded up (by the top-K kernel)
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -1771,13 +1804,6 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 
 // ------------------------------------------------------------------ certified argmax
 
-// fp32 at or above x (x >= 0): the nearest float, raised one step if below.
-__device__ __forceinline__ float f32_up(double x) {
-  float f = (float)x;
-  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
-  return f;
-}
-
 // Bound of a matrix-core dot: the canonical key of a (token, row) pair, as a
 // real, lies within E of the fp32 result l~ (bf16 x bf16, or bf16 x decoded
 // E4M3 codes, then times the slot's scale), where
@@ -1802,8 +1828,8 @@ __device__ __forceinline__ float cert_bound(float lt, float A, float beta, float
 // dims 32kb + 8q .. +7; lane l ends with the sums of tokens 16m + 4(l/16) + i
 // and row l%16.  Tokens that no row of the pass selected load nothing.
 //
-// Each (token, row) sum gets the bound E of cert_bound (|h| from the same
-// loads, |e| from the slot table): its canonical key lies in [L, U] =
+// Each (token, row) sum gets the bound E of cert_bound (|h| from the top-K
+// kernel, |e| from the slot table): its canonical key lies in [L, U] =
 // [l~ - E, l~ + E].  For each of its rows the wave writes one record, with
 // no atomics: the largest L among the tile's candidates, that token's U,
 // the largest U of the tile's other candidates, and the token and its slot
@@ -1868,11 +1894,11 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
       aoff[m] = (act ? 0u : kBufRange) + 16u * (uint32_t)tau + (F8 ? 8u * (uint32_t)(kq & 1) : 0u);
     }
     const v4u* hp = reinterpret_cast<const v4u*>(hb + (long)hrow * d) + kq;
+    const float hn = a.hnorm[hrow];
 
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-    double ss = 0.0;
     // groups of G blocks in two register stages, loads clamped to the last
     // block (so unconditional) and the blocks past the end skipped
     constexpr int G = 4;
@@ -1899,13 +1925,6 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         if (k0 + j < nkb) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const double lo = (double)__uint_as_float(st.h[j][e] << 16);
-            const double hi = (double)__uint_as_float(st.h[j][e] & 0xFFFF0000u);
-            ss = fma(lo, lo, ss);
-            ss = fma(hi, hi, ss);
-          }
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             v4u av;
@@ -1941,10 +1960,6 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
       }
     }
 
-    // the row's |h|: its four lanes hold the squares of disjoint dims
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    const float hn = f32_up(sqrt(ss) * (1.0 + 0x1p-40));
     // this lane's best candidate (largest L, then lowest slot), its U, and
     // the largest U of its other candidates
     uint32_t bl = 0u, bu = 0u, u2 = 0u, btau = 0u, bad = 0u;
@@ -2609,6 +2624,7 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.d = a.d;
   t.cmax = a.t.stats;
   t.stats = a.t.stats + 1;
+  t.hnorm = cert_gather(a) ? a.hnorm : nullptr;
   t.rows = a.B;
   t.fill = a.fill;
   t.fill_n = (long)a.B * a.V;
@@ -2680,11 +2696,15 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.enorm = a.t.enorm;
   g.crec = reinterpret_cast<v4u*>(a.crec);
   g.crank = a.tm_rank;
+  g.hnorm = a.hnorm;
   if constexpr (MODE == kArgmax && !std::is_same<T, float>::value) {
     if (cert_gather(a)) {
-      // one wave a tile: a pass holds 16 rows
-      g.split_shift = 0;
-      const dim3 cgrid((unsigned)a.t.n_tiles);
+      // a pass holds 16 rows; where a tile carries more on average (B K / Nc
+      // of them), its passes go to 2 or 4 waves, which share the XCD's L2
+      // (slot-major grid, n_tiles a multiple of 8 on large heads)
+      const long rows_per_tile = (long)a.B * a.K / a.Nc;
+      g.split_shift = rows_per_tile > 32 ? 2 : rows_per_tile > 16 ? 1 : 0;
+      const dim3 cgrid((unsigned)a.t.n_tiles << g.split_shift);
       auto go_cert = [&](auto kern) {
         if (a.probe_start && a.probe_stop)
           hipExtLaunchKernelGGL(kern, cgrid, dim3(64), 0, s, a.probe_start, a.probe_stop, 0, g);

@@ -133,9 +133,10 @@ def test_create_ragged_and_sizes(lib):
             sizes[op] = n.value
             assert n.value % 256 == 0
         assert sizes[_ffi.CE_OP_SCORE] == 0
-        # top tokens on a ragged bf16 head adds the certified argmax's
-        # records: one of 16 bytes per (row, tile), 8 rows x 4 tiles
-        assert sizes[_ffi.CE_OP_TOP_TOKENS] == sizes[_ffi.CE_OP_MASKED_LOGITS] + 8 * 4 * 16
+        # top tokens on a ragged bf16 head adds the certified argmax's row
+        # norms (64 floats, one 256-byte region) and records: one of 16 bytes
+        # per (row, tile), 8 rows x 4 tiles
+        assert sizes[_ffi.CE_OP_TOP_TOKENS] == sizes[_ffi.CE_OP_MASKED_LOGITS] + 256 + 8 * 4 * 16
         # more than one pass of rows needs no more workspace than one full pass
         assert lib.ce_workspace_bytes(h, 64, 2, _ffi.CE_OP_TOP_TOKENS, ctypes.byref(n)) == 0
         one = n.value
