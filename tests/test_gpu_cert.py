@@ -103,3 +103,31 @@ def test_exact_and_certified_agree_on_repeated_calls():
         tok = head.top_tokens(to_device(hb, w.dtype), K)
         tok_o, _, _ = oracle.top_tokens(hb, w.C, w.E, w.offsets, w.tos, K, w.dtype)
         assert tok.cpu().numpy().tolist() == tok_o.tolist(), lo
+
+
+@pytest.mark.parametrize("ragged,B", [(False, 16), (True, 64)])
+def test_certified_argmax_graph_replays(ragged, B):
+    """Captured once and replayed with eager work in between: the certified
+    path's records are rewritten by each replay, so every replay gives the
+    oracle's tokens."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import OP_TOP_TOKENS
+    w = make_random(241 + B, d=512, V=12000, Nc=96, dtype="bf16", rows=64, ragged=ragged)
+    K = 5
+    head = make_head(w, max_B=64, max_K=K, projection="mfma")
+    h = to_device(rows(w, B), w.dtype)
+    out = torch.full((B,), -9, dtype=torch.int32, device="cuda:0")
+    tk = torch.full((B, K), -9, dtype=torch.int32, device="cuda:0")
+    g = head.capture(OP_TOP_TOKENS, h, K, out, topk_out=tk)
+    tok_o, sel_o, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
+    other = to_device(np.ascontiguousarray(w.h[::-1][:B]), w.dtype)
+    for i in range(4):
+        out.fill_(-9)
+        tk.fill_(-9)
+        g.launch()
+        torch.cuda.synchronize()
+        assert out.cpu().tolist() == tok_o.tolist(), i
+        assert tk.cpu().tolist() == sel_o.tolist(), i
+        head.top_tokens(other, K)       # eager calls rewrite the records in between
+        torch.cuda.synchronize()
+    g.close()
