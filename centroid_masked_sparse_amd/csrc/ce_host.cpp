@@ -28,7 +28,7 @@ static_assert(CE_STATIC_SCRATCH_BYTES == ce::kStaticScratchBytes,
 struct ce_head {
   int32_t d = 0, V = 0, Nc = 0, max_B = 0, max_K = 0, dtype = 0, slab = CE_SLAB_NATIVE;
   int32_t proj = CE_PROJ_AUTO;
-  unsigned long long* stats = nullptr;   // device: [cmax bits, repaired rows, recomputed rows]
+  unsigned long long* stats = nullptr;   // device: [cmax bits, ..., repaired rows, recomputed rows]
   const void* C = nullptr;
   const void* E = nullptr;
   std::vector<int32_t> offsets;       // [Nc+1]
@@ -163,7 +163,7 @@ PersistLayout persist_layout(const ce_head* h) {
     off = round_up(off + bytes, 256);
     return at;
   };
-  p.stats = take(4 * sizeof(unsigned long long));
+  p.stats = take(ce::kStatsWords * sizeof(unsigned long long));
   p.offsets = take(((size_t)h->Nc + 1) * sizeof(int32_t));
   p.tos = take((size_t)h->V * sizeof(int32_t));
   p.tiles = take(std::max<size_t>(h->tiles.size(), 1) * sizeof(uint32_t));
@@ -504,7 +504,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
   // the tile list of the padded tiling; the contiguous one packs rows in order
   const uint32_t* tiles_dev =
       head->tiles.empty() ? nullptr : reinterpret_cast<const uint32_t*>(base + p.tiles);
-  hipError_t e = hipMemsetAsync(base + p.stats, 0, 4 * sizeof(unsigned long long), stream);
+  hipError_t e = hipMemsetAsync(base + p.stats, 0, ce::kStatsWords * sizeof(unsigned long long), stream);
   if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
   e = ce::launch_cnorm_max(head->C, head->dtype, head->Nc, head->d,
                            reinterpret_cast<unsigned long long*>(base + p.stats), stream);
@@ -795,7 +795,7 @@ ce_status ce_head_repair_counts(ce_head_t head, uint64_t counts[2]) {
   if (!head || !counts) return fail(CE_ERR_NULL_POINTER, "head or counts is NULL");
   if (!head->prepared) return fail(CE_ERR_NOT_PREPARED, "ce_head_prepare has not been called");
   unsigned long long c[2] = {0, 0};
-  const hipError_t e = hipMemcpy(c, head->stats + 1, sizeof(c), hipMemcpyDeviceToHost);
+  const hipError_t e = hipMemcpy(c, head->stats + ce::kStatsCounters, sizeof(c), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpy");
   counts[0] = c[0];
   counts[1] = c[1];

@@ -15,6 +15,11 @@ constexpr int kTileShift = 13;     // tile word: (tile index in cluster << 13) |
 constexpr int kMaxTilesPerCluster = 1 << (32 - kTileShift);
 constexpr int kMaxD = 8192;
 constexpr int kNoCluster = 0xFFFF;  // slot past the vocabulary in a tile of the contiguous tiling
+// The repair counters sit a 128-byte line after the centroid norm that every
+// certified top-K row reads first: device-scope atomics on them then never
+// touch the norm's line.
+constexpr int kStatsCounters = 16;
+constexpr int kStatsWords = 32;     // the stats region, 256 bytes
 
 // Device tables uploaded at prepare time.
 struct Tables {
@@ -34,8 +39,9 @@ struct Tables {
   const float* enorm;          // [n_tiles][64] |e| of each slot (times its scale), rounded up
   const void* CT;              // packed centroids:  [ceil(Nc/64)][d/vec][64]
   // [0] the largest centroid row norm (bits of a double, rounded up);
-  // [1] rows whose top-K band was recomputed in canonical keys,
-  // [2] rows recomputed whole (both counted since prepare, atomically)
+  // [kStatsCounters] rows whose top-K band was recomputed in canonical
+  // keys, [kStatsCounters + 1] rows recomputed whole (both counted since
+  // prepare, atomically)
   unsigned long long* stats;
 };
 

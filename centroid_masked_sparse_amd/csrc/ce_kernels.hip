@@ -2623,7 +2623,7 @@ hipError_t launch_topk(const PassArgs& a, int mode, hipStream_t s) {
   t.CT = static_cast<const v4u*>(a.t.CT);
   t.d = a.d;
   t.cmax = a.t.stats;
-  t.stats = a.t.stats + 1;
+  t.stats = a.t.stats + kStatsCounters;
   t.hnorm = cert_gather(a) ? a.hnorm : nullptr;
   t.rows = a.B;
   t.fill = a.fill;
