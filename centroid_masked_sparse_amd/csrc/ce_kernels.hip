@@ -2701,9 +2701,14 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
     if (cert_gather(a)) {
       // a pass holds 16 rows; where a tile carries more on average (B K / Nc
       // of them), its passes go to 2 or 4 waves, which share the XCD's L2
-      // (slot-major grid, n_tiles a multiple of 8 on large heads)
+      // (slot-major grid, n_tiles a multiple of 8 on large heads).  Ragged
+      // heads' correlated rows pile onto a few tiles: from 17 rows their
+      // passes take two waves (skewed head, B=64: gather 24.0 -> 17.2 µs,
+      // call 40.3 -> 32.9; four waves the same)
       const long rows_per_tile = (long)a.B * a.K / a.Nc;
-      g.split_shift = rows_per_tile > 32 ? 2 : rows_per_tile > 16 ? 1 : 0;
+      g.split_shift = rows_per_tile > 32                                 ? 2
+                      : (rows_per_tile > 16 || (a.t.tpc == 0 && a.B > 16)) ? 1
+                                                                         : 0;
       const dim3 cgrid((unsigned)a.t.n_tiles << g.split_shift);
       auto go_cert = [&](auto kern) {
         if (a.probe_start && a.probe_stop)
