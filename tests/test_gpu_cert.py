@@ -131,3 +131,34 @@ def test_certified_argmax_graph_replays(ragged, B):
         head.top_tokens(other, K)       # eager calls rewrite the records in between
         torch.cuda.synchronize()
     g.close()
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    d = int(rng.choice([64, 128, 192, 256, 512]))
+    Nc = int(rng.integers(8, 160))
+    V = int(rng.integers(Nc * 8, Nc * 96))
+    ragged = bool(rng.random() < 0.6)
+    K = int(rng.integers(1, min(Nc, 12) + 1))
+    B = int(rng.choice([5, 9, 17, 33, 64, 65, 100]))
+    fp8 = bool(rng.random() < 0.3)
+    return d, V, Nc, K, B, ragged, fp8
+
+
+@pytest.mark.parametrize("seed", range(300, 316))
+def test_random_heads(seed):
+    """Seeded random heads (equal or ragged clusters, d from 64 to 512, bf16
+    or FP8 slabs, 5 to 100 rows) through the certified argmax."""
+    d, V, Nc, K, B, ragged, fp8 = _random_case(seed)
+    if not ragged:
+        V = V // Nc * Nc
+    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)
+    head = _fp8_head(w, max_B=B, max_K=K) if fp8 else make_head(w, max_B=B, max_K=K, projection="mfma")
+    tok, tk = _tokens(head, w, B, K)
+    if fp8:
+        codes, sc = f8.quantize_rows(w.E)
+        tok_o, sel_o = f8.top_tokens_fp8(rows(w, B), w.C, codes, sc, w.offsets, w.tos, K)
+    else:
+        tok_o, sel_o, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
+    assert tk.tolist() == sel_o.tolist(), (d, V, Nc, K, B, ragged, fp8)
+    assert tok.tolist() == tok_o.tolist(), (d, V, Nc, K, B, ragged, fp8)
