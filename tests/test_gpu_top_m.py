@@ -37,9 +37,11 @@ def test_tiny_config(K, m):
     (42, 64, 3000, 40, 3, 7, 16, True),     # ragged clusters, some tiny
     (43, 192, 16384, 256, 16, 64, 32, False),
     (44, 64, 5000, 50, 1, 70, 20, True),    # two passes of rows
+    (46, 128, 8192, 64, 4, 3, 8, False),    # clusters of two tiles, by-row launch
+    (47, 64, 8192, 64, 4, 70, 12, False),   # equal clusters, two passes of rows
 ])
 def test_random_shapes(seed, d, V, Nc, K, B, m, ragged):
-    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)
+    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=max(64, B), ragged=ragged)
     _check(make_head(w, max_B=B), w, B, K, m)
 
 
@@ -64,6 +66,38 @@ def test_empty_clusters_pad():
         assert np.array_equal(val.cpu().numpy().view(np.uint32), val_o.view(np.uint32)), (K, m)
         if K == 2:
             assert tok_o[0].tolist() == [-1] * m      # row 0 selected only empty clusters
+
+
+def test_merge_limit_edge():
+    """The merge holds a row's segment heads (one per tile of its K clusters)
+    and m * 64 candidate keys in 8160 words of LDS.  A head whose largest
+    cluster spans 6112 tiles fills it exactly at K = 1, m = 32 (6112 + 2048),
+    and is one over it with its second cluster's two tiles at K = 2, m = 32;
+    m = 31 fits again.  Row 0 selects the large cluster at K = 1."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import CeError, Head
+    d = 64
+    big = 6112 * 64
+    V = big + 100
+    rng = np.random.default_rng(48)
+    h = np.zeros((2, d), dtype=np.float32)
+    h[:, 1:] = rng.standard_normal((2, d - 1)).astype(np.float32) / 8
+    h[0, 0], h[1, 0] = 1.0, -1.0
+    C = np.zeros((2, d), dtype=np.float32)
+    C[0, 0], C[1, 0] = 1.0, -1.0            # row 0 -> cluster 0 first, row 1 -> cluster 1
+    E = (rng.standard_normal((V, d)) / 8).astype(np.float32)
+    off = np.array([0, big, V], dtype=np.int32)
+    tos = rng.permutation(V).astype(np.int32)
+    head = Head(torch.from_numpy(C).cuda(), torch.from_numpy(E).cuda(), tos, off, max_B=2, max_K=2)
+    hd = torch.from_numpy(h).cuda()
+    for K, m in ((1, 32), (2, 31)):
+        tok, val = head.top_m(hd, m, K)
+        tok_o, val_o = oracle.top_m(h, C, E, off, tos, K, m, "f32")
+        assert tok.cpu().numpy().tolist() == tok_o.tolist(), (K, m)
+        assert np.array_equal(val.cpu().numpy().view(np.uint32), val_o.view(np.uint32)), (K, m)
+    with pytest.raises(CeError) as e:
+        head.top_m(hd, 32, 2)
+    assert e.value.status_name == "CE_ERR_UNSUPPORTED"
 
 
 def test_sweep_config_top8():
