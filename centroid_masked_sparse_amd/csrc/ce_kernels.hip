@@ -1819,14 +1819,18 @@ __device__ __forceinline__ float cert_bound(float lt, float A, float beta, float
 }
 
 // The argmax gather by matrix cores.  One wave per tile of the tile grid
-// (2^split_shift waves share its passes); a pass takes up to 16 of the
-// rows that selected a cluster of the tile, lane r's row the r-th.  The
+// (2^split_shift waves share its passes); a pass takes up to 16 RG of the
+// rows that selected a cluster of the tile, in RG groups of 16, lane r's
+// row of group g the (16 g + r)-th, and every block of the tile it loads
+// feeds the RG groups' instructions, so a tile that up to 16 RG rows
+// selected streams from memory once.  The
 // tile streams in blocks of 32 hidden dims: lane 16q + r loads the 16-byte
 // vector 4kb + q of token 16m + r for each block m of 16 tokens (FP8: the
 // half vector of codes, decoded to bf16), which is the A operand of
-// v_mfma_f32_16x16x32_bf16 as it stands, and the B operand is hidden row r's
-// dims 32kb + 8q .. +7; lane l ends with the sums of tokens 16m + 4(l/16) + i
-// and row l%16.  Tokens that no row of the pass selected load nothing.
+// v_mfma_f32_16x16x32_bf16 as it stands, and the B operand of group g is
+// its hidden row r's dims 32kb + 8q .. +7; lane l ends with the sums of
+// tokens 16m + 4(l/16) + i and row l%16 of each group.  Tokens that no row
+// of the pass selected load nothing.
 //
 // Each (token, row) sum gets the bound E of cert_bound (|h| from the top-K
 // kernel, |e| from the slot table): its canonical key lies in [L, U] =
@@ -1838,10 +1842,12 @@ __device__ __forceinline__ float cert_bound(float lt, float A, float beta, float
 // the tile in the cluster, so a row's records are contiguous; contiguous
 // tiling: the tile).  Every (row, tile) pair of a row's selected clusters
 // is written by exactly one wave, so the records need no clearing.
-template <typename T, int NKB>
+template <typename T, int NKB, int RG>
 __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
   constexpr bool F8 = std::is_same<T, uint8_t>::value;
   static_assert(F8 || std::is_same<T, uint16_t>::value, "bf16 or E4M3 slabs");
+  static_assert(RG == 1 || RG == 2 || RG == 4, "row groups per pass");
+  constexpr int PR = 16 * RG;                    // rows per pass
   __shared__ unsigned long long lr_sh[kWave];   // lane_rows of each slot of the tile
   const int lane = threadIdx.x;
   const int r = lane & 15, kq = lane >> 4;
@@ -1851,7 +1857,7 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
   unsigned long long mask, lane_rows;
   int cl = 0;
   tile_rows(a, t, mask, lane_rows, cl);
-  for (int i = 0; i < 16 * slot && mask; ++i) mask &= mask - 1ull;
+  for (int i = 0; i < PR * slot && mask; ++i) mask &= mask - 1ull;
   if (!mask) return;
   lr_sh[lane] = lane_rows;
   const long tb = (long)t * kWave;
@@ -1875,17 +1881,21 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
   const auto* hb = reinterpret_cast<const uint16_t*>(a.h);
 
   while (mask) {
-    // this pass's rows: lane r takes the r-th lowest bit of mask
-    int myrow = -1;
+    // this pass's rows: lane r of group g takes the (16 g + r)-th lowest bit
+    // of mask
+    int myrow[RG];
     unsigned long long prow = 0ull;
-    for (int i = 0; i < 16 && mask; ++i) {
-      const int b = __builtin_ctzll(mask);
-      mask &= mask - 1ull;
-      if (r == i) myrow = b;
-      prow |= 1ull << b;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      myrow[g] = -1;
+      for (int i = 0; i < 16 && mask; ++i) {
+        const int b = __builtin_ctzll(mask);
+        mask &= mask - 1ull;
+        if (r == i) myrow[g] = b;
+        prow |= 1ull << b;
+      }
     }
-    for (int i = 0; i < 16 * (nsplit - 1) && mask; ++i) mask &= mask - 1ull;
-    const int hrow = myrow >= 0 ? myrow : (int)__builtin_ctzll(prow);   // a valid row for every lane
+    for (int i = 0; i < PR * (nsplit - 1) && mask; ++i) mask &= mask - 1ull;
     uint32_t aoff[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -1893,19 +1903,30 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
       const bool act = (lr_sh[tau] & prow) != 0ull;
       aoff[m] = (act ? 0u : kBufRange) + 16u * (uint32_t)tau + (F8 ? 8u * (uint32_t)(kq & 1) : 0u);
     }
-    const v4u* hp = reinterpret_cast<const v4u*>(hb + (long)hrow * d) + kq;
-    const float hn = a.hnorm[hrow];
-
-    v4f acc[4];
+    const v4u* hp[RG];
+    float hn[RG];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < RG; ++g) {
+      // a valid row for every lane
+      const int hrow = myrow[g] >= 0 ? myrow[g] : (int)__builtin_ctzll(prow);
+      hp[g] = reinterpret_cast<const v4u*>(hb + (long)hrow * d) + kq;
+      hn[g] = a.hnorm[hrow];
+    }
+
+    v4f acc[RG][4];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
     // groups of G blocks in two register stages, loads clamped to the last
-    // block (so unconditional) and the blocks past the end skipped
-    constexpr int G = 4;
+    // block (so unconditional) and the blocks past the end skipped; with
+    // four row groups each block's hidden vectors take as many registers as
+    // its tile vectors, so the stages hold half the blocks
+    constexpr int G = RG >= 4 ? 2 : 4;
     using AT = typename std::conditional<F8, v2u, v4u>::type;
     struct Stage {
       AT x[G][4];
-      v4u h[G];
+      v4u h[G][RG];
     };
     auto load = [&](Stage& st, int k0) {
 #pragma unroll
@@ -1918,7 +1939,8 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
           if constexpr (F8) st.x[j][m] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, aoff[m] + voff, 0, 2);
           else st.x[j][m] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, aoff[m] + voff, 0, 2);
         }
-        st.h[j] = hp[4 * kb];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) st.h[j][g] = hp[g][4 * kb];
       }
     };
     auto run = [&](const Stage& st, int k0) {
@@ -1940,9 +1962,11 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
             } else {
               av = st.x[j][m];
             }
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
-                                                             __builtin_bit_cast(v8bf, st.h[j]), acc[m],
-                                                             0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+              acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                                  __builtin_bit_cast(v8bf, st.h[j][g]),
+                                                                  acc[g][m], 0, 0, 0);
           }
         }
       }
@@ -1960,57 +1984,61 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
       }
     }
 
-    // this lane's best candidate (largest L, then lowest slot), its U, and
-    // the largest U of its other candidates
-    uint32_t bl = 0u, bu = 0u, u2 = 0u, btau = 0u, bad = 0u;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int g = 0; g < RG; ++g) {
+      // this lane's best candidate for its row of group g (largest L, then
+      // lowest slot), its U, and the largest U of its other candidates
+      uint32_t bl = 0u, bu = 0u, u2 = 0u, btau = 0u, bad = 0u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tau = 16 * m + 4 * kq + i;
-        const int tok = (int)tok4[m][i];
-        float lt = acc[m][i];
-        if constexpr (F8) lt *= __uint_as_float(sc4[m][i]);
-        const float E = cert_bound(lt, hn * __uint_as_float(en4[m][i]), beta, tiny);
-        if (myrow >= 0 && tok >= 0 && ((lr_sh[tau] >> myrow) & 1ull)) {
-          // fails for a NaN too
-          if (!(fabsf(lt) <= 0x1.fffffep127f && E <= 0x1.fffffep127f)) bad = 1u;
-          const uint32_t lk = order_key(lt - E), uk = order_key(lt + E);
-          if (lk > bl) {   // slots rise with i, so a tie keeps the lower one
-            u2 = max(u2, bu);
-            bl = lk;
-            bu = uk;
-            btau = (uint32_t)tau;
-          } else {
-            u2 = max(u2, uk);
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tau = 16 * m + 4 * kq + i;
+          const int tok = (int)tok4[m][i];
+          float lt = acc[g][m][i];
+          if constexpr (F8) lt *= __uint_as_float(sc4[m][i]);
+          const float E = cert_bound(lt, hn[g] * __uint_as_float(en4[m][i]), beta, tiny);
+          if (myrow[g] >= 0 && tok >= 0 && ((lr_sh[tau] >> myrow[g]) & 1ull)) {
+            // fails for a NaN too
+            if (!(fabsf(lt) <= 0x1.fffffep127f && E <= 0x1.fffffep127f)) bad = 1u;
+            const uint32_t lk = order_key(lt - E), uk = order_key(lt + E);
+            if (lk > bl) {   // slots rise with i, so a tie keeps the lower one
+              u2 = max(u2, bu);
+              bl = lk;
+              bu = uk;
+              btau = (uint32_t)tau;
+            } else {
+              u2 = max(u2, uk);
+            }
           }
         }
       }
-    }
-    // merge the row's four lanes (xor 16, then 32)
+      // merge the row's four lanes (xor 16, then 32)
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const uint32_t obl = (uint32_t)__shfl_xor((int)bl, o), obu = (uint32_t)__shfl_xor((int)bu, o);
-      const uint32_t ou2 = (uint32_t)__shfl_xor((int)u2, o), otau = (uint32_t)__shfl_xor((int)btau, o);
-      bad |= (uint32_t)__shfl_xor((int)bad, o);
-      const bool take = obl > bl || (obl == bl && otau < btau);
-      u2 = max(max(u2, ou2), take ? bu : obu);
-      if (take) {
-        bl = obl;
-        bu = obu;
-        btau = otau;
+      for (int o = 16; o <= 32; o <<= 1) {
+        const uint32_t obl = (uint32_t)__shfl_xor((int)bl, o), obu = (uint32_t)__shfl_xor((int)bu, o);
+        const uint32_t ou2 = (uint32_t)__shfl_xor((int)u2, o), otau = (uint32_t)__shfl_xor((int)btau, o);
+        bad |= (uint32_t)__shfl_xor((int)bad, o);
+        const bool take = obl > bl || (obl == bl && otau < btau);
+        u2 = max(max(u2, ou2), take ? bu : obu);
+        if (take) {
+          bl = obl;
+          bu = obu;
+          btau = otau;
+        }
       }
-    }
-    if (kq == 0 && myrow >= 0) {
-      // padded tiling: the row's record sits at (rank of the cluster in the
-      // row's selection) * tpc + tile in cluster; contiguous: at the tile
-      const long at = a.tpc > 0 ? (long)myrow * a.K * a.tpc +
-                                      (long)a.crank[(long)myrow * a.ldR + cl] * a.tpc + (t - cl * a.tpc)
-                                : (long)myrow * a.n_tiles + t;
-      // the token again from the tile's row of ids (read at the start, so
-      // a cache hit), rather than sixteen ids held through the stream
-      const uint32_t btok = (uint32_t)a.ttok[tb + btau];
-      a.crec[at] = v4u{bl, bu, u2, (btok << 7) | (bad << 6) | btau};
+      if (kq == 0 && myrow[g] >= 0) {
+        // padded tiling: the row's record sits at (rank of the cluster in the
+        // row's selection) * tpc + tile in cluster; contiguous: at the tile
+        const int row = myrow[g];
+        const long at = a.tpc > 0 ? (long)row * a.K * a.tpc +
+                                        (long)a.crank[(long)row * a.ldR + cl] * a.tpc + (t - cl * a.tpc)
+                                  : (long)row * a.n_tiles + t;
+        // the token again from the tile's row of ids (read at the start, so
+        // a cache hit), rather than sixteen ids held through the stream
+        const uint32_t btok = (uint32_t)a.ttok[tb + btau];
+        a.crec[at] = v4u{bl, bu, u2, (btok << 7) | (bad << 6) | btau};
+      }
     }
   }
 }
@@ -2664,6 +2692,17 @@ static bool cert_gather(const PassArgs& a) {
   return a.cert && !(a.t.tpc > 0 && a.B <= kGatherByRowMaxB);
 }
 
+// Row groups of 16 per pass of the certified gather: where the selected
+// tiles carry more than 16 rows on average (B K / Nc on equal clusters), a
+// pass takes 32 or 64 rows, so each tile streams from memory once rather
+// than once per 16 rows.
+static int cert_row_groups(const PassArgs& a) {
+  const long rows_per_tile = (long)a.B * a.K / a.Nc;
+  if (a.t.tpc > 0 && rows_per_tile > 32) return 4;
+  if (a.t.tpc > 0 && rows_per_tile > 16) return 2;
+  return 1;
+}
+
 template <typename T, int MODE>
 static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   GatherArgs g;
@@ -2706,7 +2745,8 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
       // passes take two waves (skewed head, B=64: gather 24.0 -> 17.2 µs,
       // call 40.3 -> 32.9; four waves the same)
       const long rows_per_tile = (long)a.B * a.K / a.Nc;
-      g.split_shift = rows_per_tile > 32                                 ? 2
+      const int rg = cert_row_groups(a);
+      g.split_shift = rg > 1 ? 0
                       : (rows_per_tile > 16 || (a.t.tpc == 0 && a.B > 16)) ? 1
                                                                          : 0;
       const dim3 cgrid((unsigned)a.t.n_tiles << g.split_shift);
@@ -2716,12 +2756,17 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
         else
           hipLaunchKernelGGL(kern, cgrid, dim3(64), 0, s, g);
       };
-      switch (a.d / 32) {
-        case 8: go_cert(gather_cert_kernel<T, 8>); break;
-        case 16: go_cert(gather_cert_kernel<T, 16>); break;
-        case 32: go_cert(gather_cert_kernel<T, 32>); break;
-        default: go_cert(gather_cert_kernel<T, 0>); break;
-      }
+#define CE_CERT(RGN)                                                  \
+  switch (a.d / 32) {                                                 \
+    case 8: go_cert(gather_cert_kernel<T, 8, RGN>); break;            \
+    case 16: go_cert(gather_cert_kernel<T, 16, RGN>); break;          \
+    case 32: go_cert(gather_cert_kernel<T, 32, RGN>); break;          \
+    default: go_cert(gather_cert_kernel<T, 0, RGN>); break;           \
+  }
+      if (rg == 4) CE_CERT(4)
+      else if (rg == 2) CE_CERT(2)
+      else CE_CERT(1)
+#undef CE_CERT
       return hipGetLastError();
     }
   }

@@ -69,12 +69,14 @@ def test_fp8_heads(seed, d, V, Nc, K, B, ragged):
     assert tok.tolist() == tok_o.tolist()
 
 
-@pytest.mark.parametrize("ragged", [False, True])
-def test_near_ties_and_exact_ties(ragged):
+@pytest.mark.parametrize("ragged,K", [(False, 4), (True, 4), (False, 32), (False, 48)])
+def test_near_ties_and_exact_ties(ragged, K):
     """Embedding rows drawn from a pool of 4, half of them nudged by one bf16
     ulp in one dim: every row's best logit is shared by many tokens (whole
     tiles and whole rows recomputed) or missed by a hair (named tokens
-    recomputed); a zero row ties every candidate at +0."""
+    recomputed); a zero row ties every candidate at +0.  K = 32 and 48 put
+    32 and 48 rows on each selected tile of the equal clusters: passes of
+    two and four row groups."""
     w = make_random(221, d=128, V=16384, Nc=64, dtype="bf16", rows=64, ragged=ragged)
     rng = np.random.default_rng(222)
     P = w.E[rng.integers(0, w.V, size=4)]
@@ -84,10 +86,36 @@ def test_near_ties_and_exact_ties(ragged):
     h = w.h.copy()
     h[3] = 0
     w = dataclasses.replace(w, E=E, h=h)
-    B, K = 64, 4
+    B = 64
     head = make_head(w, max_B=B, max_K=K, projection="mfma")
     tok, tk = _tokens(head, w, B, K)
     tok_o, sel_o, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
+    assert tk.tolist() == sel_o.tolist()
+    assert tok.tolist() == tok_o.tolist()
+
+
+@pytest.mark.parametrize("seed,d,V,Nc,K,B,fp8", [
+    (251, 256, 8192, 64, 32, 64, False),     # 32 rows a tile: two row groups
+    (252, 512, 6400, 50, 40, 64, False),     # 51: four row groups
+    (253, 320, 4096, 32, 20, 40, False),     # 25, generic pipeline: two
+    (254, 192, 4096, 16, 16, 70, False),     # K = Nc, 64 then 6 rows: four, then one
+    (255, 256, 8192, 64, 48, 64, True),      # FP8 slabs, 48: four
+    (256, 128, 4096, 32, 12, 50, True),      # FP8 slabs, 18: two
+    (257, 1024, 8192, 128, 64, 64, False),   # 32 rows, d = 1024: two
+    (258, 1024, 8192, 64, 64, 64, False),    # K = Nc, d = 1024: four
+])
+def test_row_groups(seed, d, V, Nc, K, B, fp8):
+    """Equal clusters whose selected tiles carry more than 16 rows on
+    average (B K / Nc): a pass takes two or four groups of 16 rows, each
+    loaded block feeding every group's instructions."""
+    w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=max(64, B), ragged=False)
+    head = _fp8_head(w, max_B=B, max_K=K) if fp8 else make_head(w, max_B=B, max_K=K, projection="mfma")
+    tok, tk = _tokens(head, w, B, K)
+    if fp8:
+        codes, sc = f8.quantize_rows(w.E)
+        tok_o, sel_o = f8.top_tokens_fp8(rows(w, B), w.C, codes, sc, w.offsets, w.tos, K)
+    else:
+        tok_o, sel_o, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
     assert tk.tolist() == sel_o.tolist()
     assert tok.tolist() == tok_o.tolist()
 
