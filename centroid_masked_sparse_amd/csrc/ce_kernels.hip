@@ -1842,6 +1842,68 @@ __device__ __forceinline__ float cert_bound(float lt, float A, float beta, float
 // the tile in the cluster, so a row's records are contiguous; contiguous
 // tiling: the tile).  Every (row, tile) pair of a row's selected clusters
 // is written by exactly one wave, so the records need no clearing.
+// The record of one row of a pass for tile t (see gather_cert_kernel):
+// this lane's best candidate for the row (largest L, then lowest slot), its
+// U and the largest U of its other candidates, merged over the row's four
+// lanes (xor 16, then 32) and written by the first.  acc holds the lane's
+// sums of tokens 16m + 4(lane/16) + i for the row.
+template <bool F8>
+__device__ __forceinline__ void cert_record(const GatherArgs& a, const v4f (&acc)[4], int myrow, float hn,
+                                            const v4u (&tok4)[4], const v4u (&en4)[4],
+                                            const v4u (&sc4)[4], const unsigned long long* lr,
+                                            int t, int cl, long tb, float beta, float tiny) {
+  const int kq = (threadIdx.x & (kWave - 1)) >> 4;
+  uint32_t bl = 0u, bu = 0u, u2 = 0u, btau = 0u, bad = 0u;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tau = 16 * m + 4 * kq + i;
+      const int tok = (int)tok4[m][i];
+      float lt = acc[m][i];
+      if constexpr (F8) lt *= __uint_as_float(sc4[m][i]);
+      const float E = cert_bound(lt, hn * __uint_as_float(en4[m][i]), beta, tiny);
+      if (myrow >= 0 && tok >= 0 && ((lr[tau] >> myrow) & 1ull)) {
+        // fails for a NaN too
+        if (!(fabsf(lt) <= 0x1.fffffep127f && E <= 0x1.fffffep127f)) bad = 1u;
+        const uint32_t lk = order_key(lt - E), uk = order_key(lt + E);
+        if (lk > bl) {   // slots rise with i, so a tie keeps the lower one
+          u2 = max(u2, bu);
+          bl = lk;
+          bu = uk;
+          btau = (uint32_t)tau;
+        } else {
+          u2 = max(u2, uk);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const uint32_t obl = (uint32_t)__shfl_xor((int)bl, o), obu = (uint32_t)__shfl_xor((int)bu, o);
+    const uint32_t ou2 = (uint32_t)__shfl_xor((int)u2, o), otau = (uint32_t)__shfl_xor((int)btau, o);
+    bad |= (uint32_t)__shfl_xor((int)bad, o);
+    const bool take = obl > bl || (obl == bl && otau < btau);
+    u2 = max(max(u2, ou2), take ? bu : obu);
+    if (take) {
+      bl = obl;
+      bu = obu;
+      btau = otau;
+    }
+  }
+  if (kq == 0 && myrow >= 0) {
+    // padded tiling: the row's record sits at (rank of the cluster in the
+    // row's selection) * tpc + tile in cluster; contiguous: at the tile
+    const long at = a.tpc > 0 ? (long)myrow * a.K * a.tpc +
+                                    (long)a.crank[(long)myrow * a.ldR + cl] * a.tpc + (t - cl * a.tpc)
+                              : (long)myrow * a.n_tiles + t;
+    // the token again from the tile's row of ids (read at the start, so a
+    // cache hit), rather than sixteen ids held through the stream
+    const uint32_t btok = (uint32_t)a.ttok[tb + btau];
+    a.crec[at] = v4u{bl, bu, u2, (btok << 7) | (bad << 6) | btau};
+  }
+}
+
 template <typename T, int NKB, int RG>
 __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
   constexpr bool F8 = std::is_same<T, uint8_t>::value;
@@ -1985,61 +2047,189 @@ __global__ __launch_bounds__(64) void gather_cert_kernel(GatherArgs a) {
     }
 
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      // this lane's best candidate for its row of group g (largest L, then
-      // lowest slot), its U, and the largest U of its other candidates
-      uint32_t bl = 0u, bu = 0u, u2 = 0u, btau = 0u, bad = 0u;
+    for (int g = 0; g < RG; ++g)
+      cert_record<F8>(a, acc[g], myrow[g], hn[g], tok4, en4, sc4, lr_sh, t, cl, tb, beta, tiny);
+  }
+}
+
+// The certified gather for passes of 64 rows in four groups (selected tiles
+// carrying more than 32 rows on average, d <= kCertHlMaxD).  The pass's
+// hidden rows sit in LDS, loaded once per workgroup, each row padded by 16
+// bytes so that the 16 rows an instruction's B operand reads fall in
+// different banks; a wave's register stages then hold tile blocks only,
+// twice as many as when each block's hidden vectors ride along.  The grid
+// is persistent: kCertHlWaves waves a workgroup, one workgroup a CU (the
+// rows take most of its LDS), each wave taking tiles in turn; every wave
+// leaves after its last tile.
+constexpr int kCertHlWaves = 8;
+constexpr int kCertHlMaxD = 1024;
+constexpr int kCertHlGroups = 256;
+
+template <typename T, int NKB>
+__global__ __launch_bounds__(64 * kCertHlWaves) void gather_cert_hl_kernel(GatherArgs a) {
+  constexpr bool F8 = std::is_same<T, uint8_t>::value;
+  static_assert(F8 || std::is_same<T, uint16_t>::value, "bf16 or E4M3 slabs");
+  extern __shared__ __attribute__((aligned(16))) unsigned char hl_dyn[];   // [B][2d + 16] bytes
+  // per wave, for the tile at hand: each slot's rows (lane_rows), token,
+  // |e| and FP8 scale; the last three wait in LDS while the tile streams
+  __shared__ unsigned long long lr_all[kCertHlWaves][kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t tok_all[kCertHlWaves][kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t en_all[kCertHlWaves][kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t sc_all[F8 ? kCertHlWaves : 1][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = (int)threadIdx.x / kWave;
+  const int r = lane & 15, kq = lane >> 4;
+  const int d = a.d;
+  const int nkb = NKB > 0 ? NKB : d / 32;
+  const int ldh = 2 * d + 16;
+  {
+    const int nv = d / 8;   // 16-byte vectors a row
+    const v4u* hsrc = static_cast<const v4u*>(a.h);
+    for (int i = threadIdx.x; i < a.B * nv; i += (int)blockDim.x) {
+      const int b = i / nv, v = i - b * nv;
+      *reinterpret_cast<v4u*>(hl_dyn + (long)b * ldh + 16 * v) = hsrc[(long)b * nv + v];
+    }
+  }
+  __syncthreads();
+  unsigned long long* lr = lr_all[wv];
+  const float beta = (float)d * 0x1p-23f;
+  const float tiny = (float)d * 0x1p-125f;
+  for (int t = (int)blockIdx.x * kCertHlWaves + wv; t < a.n_tiles; t += (int)gridDim.x * kCertHlWaves) {
+    unsigned long long mask, lane_rows;
+    int cl = 0;
+    tile_rows(a, t, mask, lane_rows, cl);
+    if (!mask) continue;
+    // the previous tile's reads of lr are done before this write (one wave:
+    // its LDS operations run in order; the fences keep the compiler's too)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    lr[lane] = lane_rows;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const long tb = (long)t * kWave;
+    // this lane's slot: loaded now, put in LDS once the first blocks' loads
+    // are on their way
+    const uint32_t my_tok = (uint32_t)a.ttok[tb + lane];
+    const uint32_t my_en = __float_as_uint(a.enorm[tb + lane]);
+    uint32_t my_sc = 0u;
+    if constexpr (F8) my_sc = __float_as_uint(a.escale[tb + lane]);
+    const v4u* wt = a.ET + tb * (d / Elem<T>::kPerVec);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u*>(wt), (short)0, (int)kBufRange, (int)kBufWord3);
+    // the pass: lane r of group g takes the (16 g + r)-th row of mask (at
+    // most 64 rows: one pass)
+    int myrow[4];
+    unsigned long long prow = 0ull;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+    for (int g = 0; g < 4; ++g) {
+      myrow[g] = -1;
+      for (int i = 0; i < 16 && mask; ++i) {
+        const int b = __builtin_ctzll(mask);
+        mask &= mask - 1ull;
+        if (r == i) myrow[g] = b;
+        prow |= 1ull << b;
+      }
+    }
+    uint32_t aoff[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tau = 16 * m + 4 * kq + i;
-          const int tok = (int)tok4[m][i];
-          float lt = acc[g][m][i];
-          if constexpr (F8) lt *= __uint_as_float(sc4[m][i]);
-          const float E = cert_bound(lt, hn[g] * __uint_as_float(en4[m][i]), beta, tiny);
-          if (myrow[g] >= 0 && tok >= 0 && ((lr_sh[tau] >> myrow[g]) & 1ull)) {
-            // fails for a NaN too
-            if (!(fabsf(lt) <= 0x1.fffffep127f && E <= 0x1.fffffep127f)) bad = 1u;
-            const uint32_t lk = order_key(lt - E), uk = order_key(lt + E);
-            if (lk > bl) {   // slots rise with i, so a tie keeps the lower one
-              u2 = max(u2, bu);
-              bl = lk;
-              bu = uk;
-              btau = (uint32_t)tau;
+    for (int m = 0; m < 4; ++m) {
+      const int tau = 16 * m + r;
+      const bool act = (lr[tau] & prow) != 0ull;
+      aoff[m] = (act ? 0u : kBufRange) + 16u * (uint32_t)tau + (F8 ? 8u * (uint32_t)(kq & 1) : 0u);
+    }
+    uint32_t hoff[4];
+    float hn[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int hrow = myrow[g] >= 0 ? myrow[g] : (int)__builtin_ctzll(prow);   // a valid row
+      hoff[g] = (uint32_t)(hrow * ldh + 16 * kq);
+      hn[g] = a.hnorm[hrow];
+    }
+    v4f acc[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[g][m] = v4f{0.f, 0.f, 0.f, 0.f};
+    // blocks a register stage (two stages): the most that fit in the 256
+    // registers a wave has at two waves a SIMD beside the 64 accumulators
+    constexpr int G = 3;
+    using AT = typename std::conditional<F8, v2u, v4u>::type;
+    struct Stage {
+      AT x[G][4];
+    };
+    auto load = [&](Stage& st, int k0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int kb = min(k0 + j, nkb - 1);
+        const uint32_t voff = (uint32_t)((F8 ? 2 * kb + (kq >> 1) : 4 * kb + kq) * kWave * 16);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if constexpr (F8) st.x[j][m] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, aoff[m] + voff, 0, 2);
+          else st.x[j][m] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, aoff[m] + voff, 0, 2);
+        }
+      }
+    };
+    auto run = [&](const Stage& st, int k0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (k0 + j < nkb) {
+          v4u hv[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            hv[g] = *reinterpret_cast<const v4u*>(hl_dyn + hoff[g] + 64 * (k0 + j));
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            v4u av;
+            if constexpr (F8) {
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)st.x[j][m][w], false);
+                const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)st.x[j][m][w], true);
+                av[2 * w] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+                av[2 * w + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
+              }
             } else {
-              u2 = max(u2, uk);
+              av = st.x[j][m];
             }
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                                  __builtin_bit_cast(v8bf, hv[g]),
+                                                                  acc[g][m], 0, 0, 0);
           }
         }
       }
-      // merge the row's four lanes (xor 16, then 32)
+    };
+    Stage st0, st1;
+    load(st0, 0);
+    if (nkb > G) load(st1, G);
+    __builtin_amdgcn_sched_barrier(0);
+    tok_all[wv][lane] = my_tok;
+    en_all[wv][lane] = my_en;
+    if constexpr (F8) sc_all[wv][lane] = my_sc;
 #pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const uint32_t obl = (uint32_t)__shfl_xor((int)bl, o), obu = (uint32_t)__shfl_xor((int)bu, o);
-        const uint32_t ou2 = (uint32_t)__shfl_xor((int)u2, o), otau = (uint32_t)__shfl_xor((int)btau, o);
-        bad |= (uint32_t)__shfl_xor((int)bad, o);
-        const bool take = obl > bl || (obl == bl && otau < btau);
-        u2 = max(max(u2, ou2), take ? bu : obu);
-        if (take) {
-          bl = obl;
-          bu = obu;
-          btau = otau;
-        }
-      }
-      if (kq == 0 && myrow[g] >= 0) {
-        // padded tiling: the row's record sits at (rank of the cluster in the
-        // row's selection) * tpc + tile in cluster; contiguous: at the tile
-        const int row = myrow[g];
-        const long at = a.tpc > 0 ? (long)row * a.K * a.tpc +
-                                        (long)a.crank[(long)row * a.ldR + cl] * a.tpc + (t - cl * a.tpc)
-                                  : (long)row * a.n_tiles + t;
-        // the token again from the tile's row of ids (read at the start, so
-        // a cache hit), rather than sixteen ids held through the stream
-        const uint32_t btok = (uint32_t)a.ttok[tb + btau];
-        a.crec[at] = v4u{bl, bu, u2, (btok << 7) | (bad << 6) | btau};
+    for (int k0 = 0; k0 < nkb; k0 += 2 * G) {
+      run(st0, k0);
+      if (k0 + 2 * G < nkb) load(st0, k0 + 2 * G);
+      if (k0 + G < nkb) {
+        run(st1, k0 + G);
+        if (k0 + 3 * G < nkb) load(st1, k0 + 3 * G);
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    v4u tok4[4], en4[4], sc4[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      tok4[m] = *reinterpret_cast<const v4u*>(&tok_all[wv][16 * m + 4 * kq]);
+      en4[m] = *reinterpret_cast<const v4u*>(&en_all[wv][16 * m + 4 * kq]);
+      if constexpr (F8) sc4[m] = *reinterpret_cast<const v4u*>(&sc_all[wv][16 * m + 4 * kq]);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      cert_record<F8>(a, acc[g], myrow[g], hn[g], tok4, en4, sc4, lr, t, cl, tb, beta, tiny);
   }
 }
 
@@ -2763,7 +2953,28 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
     case 32: go_cert(gather_cert_kernel<T, 32, RGN>); break;          \
     default: go_cert(gather_cert_kernel<T, 0, RGN>); break;           \
   }
-      if (rg == 4) CE_CERT(4)
+      if (rg == 4 && a.d <= kCertHlMaxD) {
+        // the persistent kernel with the pass's rows in LDS
+        const unsigned groups = (unsigned)std::min<long>(
+            kCertHlGroups, ((long)a.t.n_tiles + kCertHlWaves - 1) / kCertHlWaves);
+        const size_t lds = (size_t)a.B * (2 * a.d + 16);
+        auto go_hl = [&](auto kern) {
+          (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (a.probe_start && a.probe_stop)
+            hipExtLaunchKernelGGL(kern, dim3(groups), dim3(64 * kCertHlWaves), lds, s, a.probe_start,
+                                  a.probe_stop, 0, g);
+          else
+            hipLaunchKernelGGL(kern, dim3(groups), dim3(64 * kCertHlWaves), lds, s, g);
+        };
+        // (d = 1024 takes the rolled pipeline: unrolled, its 32 blocks
+        // would not fit the registers)
+        switch (a.d / 32) {
+          case 8: go_hl(gather_cert_hl_kernel<T, 8>); break;
+          case 16: go_hl(gather_cert_hl_kernel<T, 16>); break;
+          default: go_hl(gather_cert_hl_kernel<T, 0>); break;
+        }
+      } else if (rg == 4) CE_CERT(4)
       else if (rg == 2) CE_CERT(2)
       else CE_CERT(1)
 #undef CE_CERT
