@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 MIN_SECONDS = 0.1   # every row but the headline is timed for at least this long
 METRIC = "sparse-head draft rows/sec at B=1..64 + achieved HBM GB/s vs peak (1 MI355X)"
 
@@ -411,7 +412,7 @@ def _wide_section(torch, args, stream, log):
     centroid: the exact dense argmax), beside a dense comparison path, the
     vendor bf16 GEMM (fp32 output) of all V logits followed by an argmax.
     Cold over two weight copies."""
-    from centroid_masked_sparse_amd import OP_TOP_TOKENS, Head
+    from centroid_masked_sparse_amd import OP_TOP_TOKENS, Head, _ffi
     from workloads import make_workload
     w = make_workload("wide")
     d, V, Nc, K, B = w.d, w.V, w.Nc, w.K, 64
@@ -444,11 +445,32 @@ def _wide_section(torch, args, stream, log):
         rc1 = [hd.repair_counts() for hd in heads]
         repaired = sum(r1[0] - r0[0] + r1[1] - r0[1] for r0, r1 in zip(rc0, rc1)) / (20 * len(heads))
         us = _time_calls(torch, calls, max(20, args.steps // 8), max(5, args.warmup // 8))
+        # the gather alone (HIP events around its launch), and its matrix-core
+        # throughput on the useful multiply-adds: d per (row, candidate token)
+        n = max(20, args.probe_calls // 4)
+        start_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        stop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in start_ev + stop_ev:
+            e.record()
+        torch.cuda.synchronize()
+        for i in range(n):
+            _ffi.check(heads[0]._lib.ce_probe_gather_events(start_ev[i].cuda_event, stop_ev[i].cuda_event),
+                       "ce_probe_gather_events")
+            f, a_, _o = calls[i % len(calls)]
+            f(*a_)
+        torch.cuda.synchronize()
+        g_us = float(np.mean([x.elapsed_time(y) for x, y in zip(start_ev, stop_ev)])) * 1e3
+        cand = int(sum(sizes[c] for row in topk.cpu().numpy() for c in row))
+        tflops = 2.0 * d * cand / (g_us * 1e-6) / 1e12
         out[f"sparse_K{k}"] = {"us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
                                "unique_MiB": round(unique / 2**20, 2),
                                "GB_s": round(unique / (us * 1e-6) / 1e9, 1),
                                "frac_peak": round(unique / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                                "repaired_rows_per_call": round(repaired, 2),
+                               "gather_us": round(g_us, 3),
+                               "gather_GB_s": round(slab / (g_us * 1e-6) / 1e9, 1),
+                               "gather_mfma_useful_TFLOP_s": round(tflops, 1),
+                               "gather_mfma_frac_of_bf16_dense_peak": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
                                "calls": "eager C-ABI calls"}
         log(f"[bench] wide sparse K={k}: {out[f'sparse_K{k}']}")
     # dense comparison: E in token order, logits^T = E_tok @ h^T (fp32 out)
