@@ -103,11 +103,15 @@ def test_near_ties_and_exact_ties(ragged, K):
     (256, 128, 4096, 32, 12, 50, True),      # FP8 slabs, 18: two
     (257, 1024, 8192, 128, 64, 64, False),   # 32 rows, d = 1024: two
     (258, 1024, 8192, 64, 64, 64, False),    # K = Nc, d = 1024: four
+    (259, 320, 4096, 32, 30, 40, False),     # 37 rows of 40, generic pipeline: four
+    (260, 2048, 2048, 16, 16, 64, False),    # d = 2048, past the rows-in-LDS limit: four
+    (261, 1024, 2048, 32, 24, 64, True),     # FP8 slabs, d = 1024, 48: four
 ])
 def test_row_groups(seed, d, V, Nc, K, B, fp8):
     """Equal clusters whose selected tiles carry more than 16 rows on
     average (B K / Nc): a pass takes two or four groups of 16 rows, each
-    loaded block feeding every group's instructions."""
+    loaded block feeding every group's instructions; four groups run in the
+    persistent kernel with the pass's rows in LDS up to d = 1024."""
     w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=max(64, B), ragged=False)
     head = _fp8_head(w, max_B=B, max_K=K) if fp8 else make_head(w, max_B=B, max_K=K, projection="mfma")
     tok, tk = _tokens(head, w, B, K)
