@@ -137,15 +137,16 @@ def test_exact_and_certified_agree_on_repeated_calls():
         assert tok.cpu().numpy().tolist() == tok_o.tolist(), lo
 
 
-@pytest.mark.parametrize("ragged,B", [(False, 16), (True, 64)])
-def test_certified_argmax_graph_replays(ragged, B):
+@pytest.mark.parametrize("ragged,B,K", [(False, 16, 5), (True, 64, 5), (False, 64, 40)])
+def test_certified_argmax_graph_replays(ragged, B, K):
     """Captured once and replayed with eager work in between: the certified
     path's records are rewritten by each replay, so every replay gives the
-    oracle's tokens."""
+    oracle's tokens.  K = 40 of 96 equal clusters puts 26 rows on each
+    selected tile at B = 64: passes of two row groups."""
     torch = torch_mod()
     from centroid_masked_sparse_amd import OP_TOP_TOKENS
-    w = make_random(241 + B, d=512, V=12000, Nc=96, dtype="bf16", rows=64, ragged=ragged)
-    K = 5
+    V = 12000 if ragged else 96 * 128
+    w = make_random(241 + B + K, d=512, V=V, Nc=96, dtype="bf16", rows=64, ragged=ragged)
     head = make_head(w, max_B=64, max_K=K, projection="mfma")
     h = to_device(rows(w, B), w.dtype)
     out = torch.full((B,), -9, dtype=torch.int32, device="cuda:0")
@@ -161,6 +162,30 @@ def test_certified_argmax_graph_replays(ragged, B):
         assert out.cpu().tolist() == tok_o.tolist(), i
         assert tk.cpu().tolist() == sel_o.tolist(), i
         head.top_tokens(other, K)       # eager calls rewrite the records in between
+        torch.cuda.synchronize()
+    g.close()
+
+
+def test_rows_in_lds_kernel_under_graph_replays():
+    """The persistent certified gather (64 rows a pass, the rows in LDS)
+    captured into a graph and replayed against the oracle, with eager calls
+    of another batch in between."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import OP_TOP_TOKENS
+    w = make_random(262, d=256, V=8192, Nc=64, dtype="bf16", rows=64, ragged=False)
+    B, K = 64, 48                          # 48 rows on each selected tile
+    head = make_head(w, max_B=B, max_K=K, projection="mfma")
+    h = to_device(rows(w, B), w.dtype)
+    out = torch.full((B,), -9, dtype=torch.int32, device="cuda:0")
+    g = head.capture(OP_TOP_TOKENS, h, K, out)
+    tok_o, _, _ = oracle.top_tokens(rows(w, B), w.C, w.E, w.offsets, w.tos, K, w.dtype)
+    other = to_device(np.ascontiguousarray(w.h[::-1][:B]), w.dtype)
+    for i in range(3):
+        out.fill_(-9)
+        g.launch()
+        torch.cuda.synchronize()
+        assert out.cpu().tolist() == tok_o.tolist(), i
+        head.top_tokens(other, K)
         torch.cuda.synchronize()
     g.close()
 
