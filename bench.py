@@ -749,6 +749,9 @@ def main() -> int:
                 break
         secs = time.perf_counter() - t0
         cpu = {"value": round(calls * Bp / secs, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
+               # the headline's unique bytes (centroids and the rows' slab
+               # union) per oracle call of the same rows
+               "GB_s": round(calls * head_unique / secs / 1e9, 5),
                "sample": f"{calls} oracle top_tokens call(s) of the first {Bp} rows of the sweep "
                          f"workload, {secs:.1f} s single-threaded numpy (float64 canonical dots); "
                          f"host has {len(os.sched_getaffinity(0))} usable of {os.cpu_count()} cores; "
