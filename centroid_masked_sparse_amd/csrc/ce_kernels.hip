@@ -1625,11 +1625,26 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
   return n;
 }
 
-// Register stages of the gather's tile ring: bf16 and FP8 keep four chunks
-// in flight (a whole 256-dim tile), so a wave waits on one round trip
-// rather than three; fp32 chunks are twice as large and keep two.
+// Register stages of the gather's tile ring (chunks of 64 dims in flight
+// per wave).  Four hold a whole 256-dim bf16 tile (212 registers, two waves
+// a SIMD); fewer stages fit more waves.  Measured on the sweep head (µs per
+// call; four / three / two stages): without the split (B < 48) three is
+// best or level everywhere (B=16 argmax 22.2 / 21.9 / 22.8, B=32 27.6 /
+// 27.3 / 28.8); with the tile's passes split over two waves (B=64, twice
+// the waves) the argmax and the top-m take two (34.1 / 33.8 / 33.3 and
+// 39.4 / 39.0 / 38.0), the forward, whose candidate stores share the
+// waves' memory counter, four (46.1 / 46.6 / 47.3), and FP8 slabs, half the
+// bytes a chunk, three (28.4 / 27.9 / 28.3).  The by-row launch (B <= 4,
+// one row a wave, a few dozen waves) keeps four: three cost B=2 and B=4
+// 0.3 µs.  fp32 chunks are twice as large: two.
 template <typename T>
-constexpr int kGatherStages = std::is_same<T, float>::value ? 2 : 4;
+constexpr int kGatherStagesByRow = std::is_same<T, float>::value ? 2 : 4;
+template <typename T, int MODE, bool SPLIT>
+constexpr int kGatherStages = std::is_same<T, float>::value     ? 2
+                              : std::is_same<T, uint8_t>::value ? 3
+                              : !SPLIT                          ? 3
+                              : MODE == kMasked                 ? 4
+                                                                : 2;
 constexpr bool kGatherStream = true;    // non-temporal slab loads (read once per call: 21.1 -> 20.1 us at B=64)
 
 // Tile t of the tile grid: the rows that selected a cluster of the tile
@@ -1677,7 +1692,7 @@ __device__ __forceinline__ void tile_rows(const GatherArgs& a, int t, unsigned l
 // alone.  With equal tile counts per cluster the cluster follows from the
 // tile index too, so the selection words (by row: the row's top-K id) are
 // the only load before the tile's.
-template <typename T, int RB, int MODE, int NCH>
+template <typename T, int RB, int MODE, int NCH, int STG>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
   const int lane = threadIdx.x;
   // 2^split_shift waves per tile; the tile's passes of RB rows are dealt to
@@ -1793,7 +1808,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
       if (r < nrows) prow |= 1ull << rows[r];
     const uint32_t lane_off = ((lane_rows & prow) ? 0u : kBufRange) + 16u * (uint32_t)lane;
     double acc[RB];
-    dot_tile<T, RB, NCH, kGatherStages<T>, false, NoOp, kGatherStream, true>(wtb, a.d, h, rows, nrows,
+    dot_tile<T, RB, NCH, STG, false, NoOp, kGatherStream, true>(wtb, a.d, h, rows, nrows,
                                                                              acc, NoOp(), lane_off);
     pin(tok);   // keep the loads out of the branches below
     pin(sc);
@@ -2993,8 +3008,10 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   // by row a wave dots a single row: the one-row instantiation skips the
   // three unused row slots' hidden loads, widening and branches (B=1..4:
   // 0.4–0.9 µs per call on every entry point)
-#define CE_GATHER(N) \
-  (g.by_row ? go(gather_kernel<T, 1, MODE, N>) : go(gather_kernel<T, kGatherRows, MODE, N>))
+#define CE_GATHER(N)                                                                           \
+  (g.by_row            ? go(gather_kernel<T, 1, MODE, N, kGatherStagesByRow<T>>)                   \
+   : g.split_shift > 0 ? go(gather_kernel<T, kGatherRows, MODE, N, kGatherStages<T, MODE, true>>)  \
+                       : go(gather_kernel<T, kGatherRows, MODE, N, kGatherStages<T, MODE, false>>))
   CE_DISPATCH_NCH(a.d, CE_GATHER)
 #undef CE_GATHER
   return hipGetLastError();
