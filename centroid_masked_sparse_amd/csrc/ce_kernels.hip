@@ -748,7 +748,11 @@ __global__ __launch_bounds__(64) void scores_kernel(const v4u* __restrict__ CT, 
       dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, hn, lrows, nrows, acc);
     }
   } else {
-    dot_tile<T, RB, NCH>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
+    // two rows a wave (the forward from 48 rows, beside its fill waves):
+    // three stages of the centroid tile in flight (forward B=64: 46.2 ->
+    // 45.1 µs per call); one row a wave keeps two (three cost the B=64
+    // argmax 0.2 µs)
+    dot_tile<T, RB, NCH, RB >= 2 ? 3 : 2>(CT + blockIdx.x * tile_vecs, d, h, rows, nrows, acc);
   }
   if (lane < nvalid) {
 #pragma unroll
