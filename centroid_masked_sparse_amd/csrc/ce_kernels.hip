@@ -2888,17 +2888,37 @@ static int gather_split_shift(int B) { return B >= 48 ? kGatherSplitShift : 0; }
 constexpr int kRaggedSplitShift = 2;
 static int gather_split_shift_ragged(int B) { return B >= 16 ? kRaggedSplitShift : 0; }
 
-// Largest batch whose gather runs by row (equal clusters only): up to it
-// the B·K·tpc waves of the selected (row, centroid, tile) triples cost less
-// than the static grid of every tile, most of whose waves find no row
-// (sweep head, µs per call: B=1 17.3 → 15.5, B=2 19.4 → 18.0, B=4 20.1 →
-// 19.6; B=8 22.8 → 23.2 and B=16 24.2 → 25.8 the other way).
-constexpr int kGatherByRowMaxB = 4;
+// Largest batch whose float64 gather runs by row (equal clusters only):
+// the B·K·tpc waves of the selected (row, centroid, tile) triples, every
+// one with work, against the static grid of every tile, most of whose
+// waves find no row.  A tile that several rows selected is then read once
+// per row, which the batches below the split (48 rows) afford: sweep head,
+// µs per call, B=8 19.8 → 16.6, B=16 22.0 → 19.0, B=32 27.3 → 24.1 (forward
+// B=16 24.2 → 21.0, top-m B=16 26.7 → 23.0).  At B=64 the repeats cost more
+// than the idle waves (33.2 → 36.7), except for FP8 slabs, whose argmax is
+// bound by its conversions rather than its bytes and runs by row at every
+// batch (B=64 27.8 → 26.0).  (On earlier kernels the limit measured best at
+// 4 rows.)  Beyond 4 rows by row needs about one row per selected tile
+// (B K <= 2 Nc, as on the sweep head, where it is 0.5 to 1): where rows
+// share most tiles (K near Nc) every repeat is a slab read.
+constexpr int kGatherByRowMaxB = 47;
+constexpr int kGatherByRowAlways = 4;
 
-// The certified matrix-core argmax runs on the tile grid only: by row a
-// wave holds a single row, which the float64 chain serves better.
+template <typename T, int MODE>
+static bool gather_by_row(const PassArgs& a) {
+  if (a.t.tpc == 0) return false;
+  if (a.B <= kGatherByRowAlways) return true;
+  const bool fp8_argmax = std::is_same<T, uint8_t>::value && MODE == kArgmax;
+  return (long)a.B * a.K <= 2l * a.Nc && (fp8_argmax || a.B <= kGatherByRowMaxB);
+}
+// Batches of at most this many rows on equal clusters keep the float64 dot
+// by row even where the certified matrix-core argmax is on (a wave there
+// holds a single row, which the float64 chain serves better); larger ones
+// take the certified argmax's tile grid.
+constexpr int kCertByRowMaxB = 4;
+
 static bool cert_gather(const PassArgs& a) {
-  return a.cert && !(a.t.tpc > 0 && a.B <= kGatherByRowMaxB);
+  return a.cert && !(a.t.tpc > 0 && a.B <= kCertByRowMaxB);
 }
 
 // Row groups of 16 per pass of the certified gather: where the selected
@@ -2924,7 +2944,8 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.tpc = a.t.tpc;
   g.ttok = a.t.ttok;
   g.escale = a.t.escale;
-  g.split_shift = a.t.tpc > 0 ? gather_split_shift(a.B) : gather_split_shift_ragged(a.B);
+  const bool by_row = gather_by_row<T, MODE>(a);
+  g.split_shift = a.t.tpc > 0 ? (by_row ? 0 : gather_split_shift(a.B)) : gather_split_shift_ragged(a.B);
   g.best = a.best;
   g.amax = a.amax;
   g.out = a.logits;
@@ -2940,7 +2961,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
   g.topk = a.topk;
   g.ldK = a.ldK;
   g.K = a.K;
-  g.by_row = a.t.tpc > 0 && a.B <= kGatherByRowMaxB && g.split_shift == 0;
+  g.by_row = by_row;
   g.enorm = a.t.enorm;
   g.crec = reinterpret_cast<v4u*>(a.crec);
   g.crank = a.tm_rank;
