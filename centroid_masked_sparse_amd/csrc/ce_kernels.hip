@@ -1638,11 +1638,14 @@ __device__ __forceinline__ int take_rows(unsigned long long& mask, int (&rows)[R
 // the waves) the argmax and the top-m take two (34.1 / 33.8 / 33.3 and
 // 39.4 / 39.0 / 38.0), the forward, whose candidate stores share the
 // waves' memory counter, four (46.1 / 46.6 / 47.3), and FP8 slabs, half the
-// bytes a chunk, three (28.4 / 27.9 / 28.3).  The by-row launch (B <= 4,
-// one row a wave, a few dozen waves) keeps four: three cost B=2 and B=4
-// 0.3 µs.  fp32 chunks are twice as large: two.
+// bytes a chunk, three (28.4 / 27.9 / 28.3).  By row (one row a wave, up
+// to a few thousand waves) bf16 takes three, the same as four up to B=4 and
+// 0.15-0.3 µs faster from B=8 to 32 (136 VGPRs against 168; two stages, 102
+// VGPRs and four waves a SIMD, were 0.1-0.3 µs slower than three), and FP8
+// four (26.1 against 26.2 µs at B=64).  fp32 chunks are twice as large:
+// two.
 template <typename T>
-constexpr int kGatherStagesByRow = std::is_same<T, float>::value ? 2 : 4;
+constexpr int kGatherStagesByRow = std::is_same<T, float>::value ? 2 : std::is_same<T, uint8_t>::value ? 4 : 3;
 template <typename T, int MODE, bool SPLIT>
 constexpr int kGatherStages = std::is_same<T, float>::value     ? 2
                               : std::is_same<T, uint8_t>::value ? 3
