@@ -50,6 +50,7 @@ def _check_all(head, w, B, K, m=6):
     (63, 256, 16384, 256, 16, 64, False),
     (64, 512, 5000, 50, 2, 70, True),     # two passes of rows
     (65, 320, 4096, 64, 5, 5, False),     # d with no straight-line pipeline
+    (67, 128, 8192, 64, 8, 40, False),    # B*K > 2*Nc below 48 rows: masked and top-m on the unsplit tile grid
 ])
 def test_random_shapes(seed, d, V, Nc, K, B, ragged):
     w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=ragged)

@@ -1,11 +1,15 @@
 """GPU parity of the gather's two launch shapes.
 
-With equal clusters, small batches (up to 4 rows) launch one wave per
-selected (row, centroid, tile) and read the centroid from the row's top-K
-ids; larger batches launch one wave per tile of the head (two per tile from
-48 rows) and read the rows that selected it from the selection words.  Both
-must give every row the oracle's answer, including rows that select the same
-clusters (identical rows: by row, two waves then dot the same tile).
+With equal clusters the float64 gather launches one wave per selected (row,
+centroid, tile), reading the centroid from the row's top-K ids, for batches
+of up to 4 rows, and up to 47 rows while B*K <= 2*Nc (FP8 argmax: at every
+batch); otherwise one wave per tile of the head (two per tile from 48 rows),
+reading the rows that selected it from the selection words.  Both must give
+every row the oracle's answer, including rows that select the same clusters
+(identical rows: by row, two waves then dot the same tile).  The batch sizes
+below reach both shapes on each head and both sides of the B*K = 2*Nc edge
+(head 82: 42 rows by row, 43 on the tile grid; head 83: 32 by row, 40 on
+the tile grid).
 """
 
 import numpy as np
@@ -23,7 +27,7 @@ pytestmark = pytest.mark.gpu
     (82, 64, 8192, 64, 3),      # two tiles per cluster
     (83, 256, 16384, 256, 16),
 ])
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 48])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 30, 32, 40, 42, 43, 47, 48])
 def test_by_row_and_tile_grid_agree_with_oracle(seed, d, V, Nc, K, B):
     torch = torch_mod()
     w = make_random(seed, d=d, V=V, Nc=Nc, dtype="bf16", rows=64, ragged=False)
