@@ -1580,7 +1580,8 @@ struct GatherArgs {
   const uint16_t* tcl;          // [n_tiles][64]
   int split_shift;              // 2^split_shift waves per tile share its passes
   int n_tiles;
-  // by row (equal clusters, small batches): one wave per (row, selected
+  // by row (equal clusters; small batches, or mid ones whose selected
+  // tiles carry about one row each): one wave per (row, selected
   // centroid, tile of that cluster), the centroid read from the row's top-K
   const int32_t* topk;          // [B][ldK] ascending ids
   int ldK, K;
@@ -1718,8 +1719,9 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
     for (int i = 0; i < n * RB && mask; ++i) mask &= mask - 1ull;
   };
   if (a.by_row) {
-    // a tile two rows selected is dotted by two waves (rare at small
-    // batches), but no wave is launched for a tile nobody selected
+    // a tile two rows selected is dotted (and read) by two waves, but no
+    // wave is launched for a tile nobody selected, and the waves spread
+    // evenly over the CUs
     const int per_row = a.K * a.tpc;
     const int b = (int)blockIdx.x / per_row;
     const int rem = (int)blockIdx.x - b * per_row;
