@@ -55,6 +55,8 @@ __all__ = [
     "masked_logits",
     "top_tokens",
     "top_m",
+    "log_softmax_candidates",
+    "top_m_log_softmax",
     "dense_logits",
 ]
 
@@ -205,6 +207,49 @@ def top_m(h, C, E, offsets, tos, K: int, m: int, dtype: str):
         order = np.lexsort((tokens, -logits.astype(np.float64)))[:m]
         tok[b, :len(order)] = tokens[order]
         val[b, :len(order)] = logits[order]
+    return tok, val
+
+
+def log_softmax_candidates(logits) -> np.ndarray:
+    """Log-probabilities of a row's candidates under a softmax over the
+    candidate set alone: ``log p_i = l_i - log(sum_c exp(l_c))``.
+
+    This is the softmax a sampler takes over ``forward``'s masked row, whose
+    -inf entries contribute exp(-inf) = 0 (same page, class
+    ``Gemma4MTPMaskedEmbedder``, ``forward``).  The page fixes no precision:
+    in float64, with ``M`` the largest logit and ``T = sum_c exp(l_c - M)``
+    over every candidate but one that holds ``M``, ``log p_i = (l_i - M) -
+    log1p(T)``.  The shift keeps every exponential at most 1; subtracting
+    from the shifted logit (rather than adding ``M`` back first), and
+    log1p(T) rather than log(1 + T), keep the relative precision of
+    log-probabilities near 0, where the largest candidate dominates.  Each
+    result is rounded once to fp32 (nearest-even).  An empty row gives an
+    empty result.
+    """
+    x = np.asarray(logits, dtype=np.float64).ravel()
+    if x.size == 0:
+        return np.zeros(0, dtype=np.float32)
+    top = int(np.argmax(x))
+    sh = x - x[top]
+    t = np.sum(np.exp(np.delete(sh, top)))
+    return (sh - np.log1p(t)).astype(np.float32)
+
+
+def top_m_log_softmax(h, C, E, offsets, tos, K: int, m: int, dtype: str):
+    """``top_m``'s tokens with their log-probabilities under the softmax over
+    each row's candidate set (``log_softmax_candidates``) instead of their
+    logits: ``[B, m]`` token ids (ordered as in ``top_m``) and fp32
+    log-probabilities, padded with token -1 and -inf."""
+    h = np.atleast_2d(np.asarray(h))
+    B = h.shape[0]
+    tok = np.full((B, m), -1, dtype=np.int64)
+    val = np.full((B, m), -np.inf, dtype=np.float32)
+    for b in range(B):
+        logits, tokens, _ = select_and_score(h[b], C, E, offsets, tos, K, dtype)
+        lp = log_softmax_candidates(logits)
+        order = np.lexsort((tokens, -logits.astype(np.float64)))[:m]
+        tok[b, :len(order)] = tokens[order]
+        val[b, :len(order)] = lp[order]
     return tok, val
 
 
