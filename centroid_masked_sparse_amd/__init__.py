@@ -20,7 +20,8 @@ import numpy as np
 
 from . import _ffi
 from ._ffi import (CE_BF16, CE_F32, CE_MAX_TOP_M, CE_OP_DRAFT_STEP, CE_OP_MASKED_LOGITS,
-                   CE_OP_SCORE, CE_OP_TOP_M, CE_OP_TOP_TOKENS, CE_OP_TOPK, CeError, check)
+                   CE_OP_SCORE, CE_OP_TOP_M, CE_OP_TOP_M_LOG_SOFTMAX, CE_OP_TOP_TOKENS, CE_OP_TOPK,
+                   CeError, check)
 
 __all__ = ["Head", "Graph", "CeError", "load_library"]
 
@@ -248,10 +249,14 @@ class Head:
               "ce_masked_logits")
         return out
 
-    def top_m(self, h, m: int, K: int | None = None, out=None, logits_out=None, topk_out=None):
+    def top_m(self, h, m: int, K: int | None = None, out=None, logits_out=None, topk_out=None,
+              log_softmax: bool = False):
         """The m best candidates per row: ``([B, m]`` int32 token ids, ``[B, m]``
         fp32 logits), ordered by logit descending then token id ascending;
-        rows with fewer than m candidates are padded with -1 / -inf."""
+        rows with fewer than m candidates are padded with -1 / -inf.  With
+        ``log_softmax`` the second output holds each candidate's
+        log-probability under the softmax over the row's candidates
+        (``ce_top_m_log_softmax``) instead of its logit."""
         torch = _torch()
         B = self._check_h(h)
         K = self._k(K)
@@ -259,12 +264,14 @@ class Head:
             out = torch.empty((B, m), dtype=torch.int32, device=self.device)
         if logits_out is None:
             logits_out = torch.empty((B, m), dtype=torch.float32, device=self.device)
-        ws = self._workspace(B, K, CE_OP_TOP_M)
-        check(self._lib.ce_top_m(self._handle, h.data_ptr(), B, K, m, out.data_ptr(),
-                                 logits_out.data_ptr(),
-                                 0 if topk_out is None else topk_out.data_ptr(),
-                                 ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
-              "ce_top_m")
+        op = CE_OP_TOP_M_LOG_SOFTMAX if log_softmax else CE_OP_TOP_M
+        name = "ce_top_m_log_softmax" if log_softmax else "ce_top_m"
+        ws = self._workspace(B, K, op)
+        check(getattr(self._lib, name)(self._handle, h.data_ptr(), B, K, m, out.data_ptr(),
+                                       logits_out.data_ptr(),
+                                       0 if topk_out is None else topk_out.data_ptr(),
+                                       ws.data_ptr(), ws.numel(), _stream_handle(self.device)),
+              name)
         return out, logits_out
 
     def draft_step(self, x, norm_weight, eps: float, K: int | None = None, emb_table=None,
@@ -309,7 +316,8 @@ class Head:
         ``op`` is one of the ``OP_*`` codes; ``h`` is the op's input (the rows,
         the ``[B, Nc]`` scores for ``OP_TOPK``, the rows before the norm for
         ``OP_DRAFT_STEP``) and ``out`` its first output (scores, top-K ids,
-        tokens or logits).  ``OP_TOP_M`` also takes ``m`` and ``logits_out``;
+        tokens or logits).  ``OP_TOP_M`` and ``OP_TOP_M_LOG_SOFTMAX`` also take
+        ``m`` and ``logits_out``;
         ``OP_DRAFT_STEP`` takes ``norm_weight``, ``eps``, ``h_out`` and
         optionally ``emb_table``, ``normalizer`` and ``emb_out``.  Every tensor
         is read or written at the same address on every launch.  ``stream``
@@ -356,5 +364,6 @@ OP_TOPK = CE_OP_TOPK
 OP_TOP_TOKENS = CE_OP_TOP_TOKENS
 OP_MASKED_LOGITS = CE_OP_MASKED_LOGITS
 OP_TOP_M = CE_OP_TOP_M
+OP_TOP_M_LOG_SOFTMAX = CE_OP_TOP_M_LOG_SOFTMAX
 OP_DRAFT_STEP = CE_OP_DRAFT_STEP
 MAX_TOP_M = CE_MAX_TOP_M

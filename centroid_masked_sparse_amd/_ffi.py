@@ -16,6 +16,7 @@ STATUS_NAMES = {
 CE_F32, CE_BF16 = 0, 1
 CE_OP_SCORE, CE_OP_TOPK, CE_OP_TOP_TOKENS, CE_OP_MASKED_LOGITS, CE_OP_TOP_M = 0, 1, 2, 3, 4
 CE_OP_DRAFT_STEP = 5
+CE_OP_TOP_M_LOG_SOFTMAX = 6
 CE_MAX_TOP_M = 32
 CE_STATIC_SCRATCH_BYTES = 4 << 20
 CE_SLAB_NATIVE, CE_SLAB_FP8_E4M3 = 0, 1
@@ -58,6 +59,7 @@ SIGNATURES = {
     "ce_top_tokens_static": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "ce_masked_logits": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "ce_top_m": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ce_top_m_log_softmax": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ce_draft_step": (_i32, [_vp, _vp, _vp, ctypes.c_float, _i32, _i32, _vp, _vp, _vp, _i32,
                              ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
     "ce_graph_capture": (_i32, [_vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp,

@@ -105,6 +105,9 @@ bool cert_head(const ce_head* h) {
 // call, with no other benchmark row changed.
 constexpr long long kMfmaMinMacs = 1ll << 26;
 
+// The two forms of the fused top-m (logits, or log-probabilities).
+bool top_m_op(int op) { return op == CE_OP_TOP_M || op == CE_OP_TOP_M_LOG_SOFTMAX; }
+
 Layout make_layout(const ce_head* h, int B, int K, int op, bool allow_cert = true) {
   Layout L;
   const size_t nb = (size_t)std::min(B, ce::kPassRows);
@@ -137,7 +140,7 @@ Layout make_layout(const ce_head* h, int B, int K, int op, bool allow_cert = tru
       L.crec = take(nb * (size_t)h->n_tiles * 16);
     }
   }
-  if (op == CE_OP_TOP_M) {
+  if (top_m_op(op)) {
     L.tm_segcap = (int)std::max<long long>(h->tiles_top[K], 1);
     L.tm_keys = take(nb * (size_t)L.tm_segcap * ce::kTileTokens * sizeof(unsigned long long));
     L.tm_heads = take(nb * (size_t)L.tm_segcap * sizeof(unsigned long long));
@@ -267,9 +270,9 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
     st = check_draft(h, hin, B, *draft);
     if (st != CE_SUCCESS) return st;
   }
-  if (B > 0 && (!out || (op == CE_OP_TOP_M && !out2)))
+  if (B > 0 && (!out || (top_m_op(op) && !out2)))
     return fail(CE_ERR_NULL_POINTER, "output pointer is NULL");
-  if (op == CE_OP_TOP_M) {
+  if (top_m_op(op)) {
     if (m < 1 || m > ce::kMaxTopM) return fail(CE_ERR_BAD_SHAPE, "m must lie in [1, CE_MAX_TOP_M]");
     if (h->tiles_top[K] + (long long)m * ce::kTileTokens > ce::kTopMLdsWords)
       return fail(CE_ERR_UNSUPPORTED, "the K largest clusters hold too many tiles for the top-m merge");
@@ -305,8 +308,9 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
     }
     if (op == CE_OP_TOP_TOKENS || op == CE_OP_DRAFT_STEP) {
       a.tokens = static_cast<int32_t*>(out) + b0;
-    } else if (op == CE_OP_TOP_M) {
+    } else if (top_m_op(op)) {
       a.m = m;
+      a.tm_log_softmax = op == CE_OP_TOP_M_LOG_SOFTMAX;
       a.tm_cap = L.tm_segcap * ce::kTileTokens;
       a.tm_tokens = static_cast<int32_t*>(out) + (size_t)b0 * m;
       a.tm_logits = out2 + (size_t)b0 * m;
@@ -318,7 +322,7 @@ ce_status run_sparse(ce_head* h, int op, const void* hin, int B, int K, void* ou
       a.probe_start = pstart;
       a.probe_stop = pstop;
     }
-    const int mode = op == CE_OP_MASKED_LOGITS ? ce::kMasked : op == CE_OP_TOP_M ? ce::kTopM : ce::kArgmax;
+    const int mode = op == CE_OP_MASKED_LOGITS ? ce::kMasked : top_m_op(op) ? ce::kTopM : ce::kArgmax;
     void* h_out = nullptr;
     if (op == CE_OP_DRAFT_STEP) {
       // scores reads the rows before the norm and writes the normalised ones
@@ -549,7 +553,7 @@ ce_status ce_head_prepare(ce_head_t head, void* persistent, size_t bytes, hipStr
 
 ce_status ce_workspace_bytes(ce_head_t head, int32_t B, int32_t K, int32_t op, size_t* bytes) {
   if (!head || !bytes) return fail(CE_ERR_NULL_POINTER, "head or bytes is NULL");
-  if (op < CE_OP_SCORE || op > CE_OP_DRAFT_STEP) return fail(CE_ERR_UNSUPPORTED, "unknown op");
+  if (op < CE_OP_SCORE || op > CE_OP_TOP_M_LOG_SOFTMAX) return fail(CE_ERR_UNSUPPORTED, "unknown op");
   if (B < 0 || B > head->max_B) return fail(CE_ERR_BAD_SHAPE, "B must lie in [0, max_B]");
   if (op == CE_OP_TOPK) {
     *bytes = 0;
@@ -655,6 +659,13 @@ ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t 
   return run_sparse(head, CE_OP_TOP_M, h, B, K, tokens, topk_ids_or_null, ws, ws_bytes, stream, m, logits);
 }
 
+ce_status ce_top_m_log_softmax(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m,
+                               int32_t* tokens, float* logprobs, int32_t* topk_ids_or_null, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  return run_sparse(head, CE_OP_TOP_M_LOG_SOFTMAX, h, B, K, tokens, topk_ids_or_null, ws, ws_bytes,
+                    stream, m, logprobs);
+}
+
 ce_status ce_draft_step(ce_head_t head, const void* x, const void* norm_weight, float eps,
                         int32_t B, int32_t K, void* h_out, int32_t* tokens,
                         const void* emb_table, int32_t emb_dim, float normalizer,
@@ -683,6 +694,7 @@ ce_status enqueue_call(ce_head_t head, const ce_call& c, hipStream_t stream, boo
       return run_sparse(head, c.op, c.in, c.B, c.K, c.out, c.topk_ids, c.ws, c.ws_bytes, stream, 0,
                         nullptr, nullptr, dry);
     case CE_OP_TOP_M:
+    case CE_OP_TOP_M_LOG_SOFTMAX:
       return run_sparse(head, c.op, c.in, c.B, c.K, c.out, c.topk_ids, c.ws, c.ws_bytes, stream,
                         c.m, c.out_logits, nullptr, dry);
     case CE_OP_DRAFT_STEP: {
@@ -697,7 +709,7 @@ ce_status enqueue_call(ce_head_t head, const ce_call& c, hipStream_t stream, boo
 }
 
 ce_status capture(ce_head_t head, const ce_call& c, hipStream_t stream, ce_graph_t* graph) {
-  if (c.op < CE_OP_SCORE || c.op > CE_OP_DRAFT_STEP) return fail(CE_ERR_UNSUPPORTED, "unknown op");
+  if (c.op < CE_OP_SCORE || c.op > CE_OP_TOP_M_LOG_SOFTMAX) return fail(CE_ERR_UNSUPPORTED, "unknown op");
   if (!stream) return fail(CE_ERR_UNSUPPORTED, "capture needs a non-null stream");
   // check the call before capturing, so that a bad call leaves no capture
   ce_status st = enqueue_call(head, c, stream, true);

@@ -97,7 +97,8 @@ struct PassArgs {
   int16_t* tm_rank;       // equal clusters: [B][ldR] output position of each selected
   int ldR;                // centroid (top-K writes it, the gather's fixed segments read it)
   int32_t* tm_tokens;     // [B][m]
-  float* tm_logits;       // [B][m]
+  float* tm_logits;       // [B][m] logits, or log-probabilities with tm_log_softmax
+  bool tm_log_softmax;    // top-m: log-softmax over the row's candidates
   // fused draft step: h holds the rows before the final RMSNorm when norm_w
   // is set; the scores kernel writes the normalised rows to h_out (which the
   // gather then reads), and the finalize kernel writes the chosen tokens'

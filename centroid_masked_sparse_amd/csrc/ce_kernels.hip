@@ -2615,7 +2615,8 @@ struct TopmArgs {
   int cap, segcap, m;
   int fixed_segs;                   // > 0: every row has this many segments of 64 keys (zeros pad)
   int32_t* tokens;                  // [B][m]
-  float* logits;                    // [B][m]
+  float* logits;                    // [B][m] logits, or log-probabilities with log_softmax
+  int log_softmax;                  // log-probabilities under the softmax over the row's candidates
 };
 
 
@@ -2627,10 +2628,18 @@ struct TopmArgs {
 // m*64 candidates.  Each of those counts the candidates above it; a count
 // below m is its output position.  With fewer than m segments every key is
 // a candidate.
+//
+// log_softmax: every key of the row passes through the scan below, so the
+// scan also sums T = sum of exp(l - M) in float64 over all candidates but
+// the row's largest key (M its logit, the largest head), each thread in
+// its order, the waves' sums combined in wave order (the same result on
+// every run); each output is then (l - M) - log1p(T), rounded once.
 __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
   extern __shared__ unsigned long long tm_lds[];   // heads [segcap], then candidates
   __shared__ uint32_t ncand;
   __shared__ unsigned long long wred[kTopkWaves];
+  __shared__ unsigned long long wtop[kTopkWaves];
+  __shared__ double wsum[kTopkWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -2649,6 +2658,21 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
   for (int i = tid; i < segs; i += kTopkThreads) heads[i] = hsrc[i];
   if (tid == 0) ncand = 0;
   __syncthreads();
+
+  // log_softmax: the row's largest key (0: no candidate) and its logit
+  unsigned long long ktop = 0ull;
+  double mtop = 0.0;
+  if (a.log_softmax) {
+    unsigned long long hm = 0ull;
+    for (int i = tid; i < segs; i += kTopkThreads) hm = max(hm, heads[i]);
+    hm = __ockl_wfred_max_u64(hm);
+    if (lane == 0) wtop[wv] = hm;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) ktop = max(ktop, wtop[i]);
+    if (ktop) mtop = (double)key_value((uint32_t)(ktop >> 32));
+  }
+  double tsum = 0.0;
 
   unsigned long long mu = 0ull;
   if (segs >= m) {
@@ -2676,13 +2700,28 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
 #pragma unroll
     for (int u = 0; u < kScan; ++u) {
       const unsigned long long k = kk[u];
-      if (i0 + u * kTopkThreads + tid < n && k >= mu && k != 0ull) {
+      const bool in = i0 + u * kTopkThreads + tid < n && k != 0ull;
+      if (in && k >= mu) {
         const uint32_t at = atomicAdd(&ncand, 1u);
         if (at < (uint32_t)cap_c) cand[at] = k;
       }
+      if (a.log_softmax && in && k != ktop)
+        tsum += exp((double)key_value((uint32_t)(k >> 32)) - mtop);
     }
   }
+  if (a.log_softmax) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o);
+    if (lane == 0) wsum[wv] = tsum;
+  }
   __syncthreads();
+  double lg = 0.0;
+  if (a.log_softmax) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) t += wsum[i];
+    lg = log1p(t);
+  }
   const int nc = min((int)ncand, cap_c);
   int32_t* tok = a.tokens + (long)b * m;
   float* val = a.logits + (long)b * m;
@@ -2692,7 +2731,8 @@ __global__ __launch_bounds__(kTopkThreads) void topm_merge_kernel(TopmArgs a) {
     for (int j = 0; j < nc; ++j) above += cand[j] > x ? 1 : 0;
     if (above < m) {
       tok[above] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
-      val[above] = key_value((uint32_t)(x >> 32));
+      const float l = key_value((uint32_t)(x >> 32));
+      val[above] = a.log_softmax ? (float)(((double)l - mtop) - lg) : l;
     }
   }
   for (int p = min(nc, m) + tid; p < m; p += kTopkThreads) {
@@ -3075,6 +3115,7 @@ hipError_t launch_topm_merge(const PassArgs& a, hipStream_t s) {
   t.fixed_segs = a.tm_rank ? a.K * a.t.tpc : 0;
   t.tokens = a.tm_tokens;
   t.logits = a.tm_logits;
+  t.log_softmax = a.tm_log_softmax ? 1 : 0;
   const size_t lds = ((size_t)a.tm_segcap + (size_t)a.m * kTileTokens) * sizeof(unsigned long long);
   hipLaunchKernelGGL(topm_merge_kernel, dim3(a.B), dim3(kTopkThreads), lds, s, t);
   return hipGetLastError();

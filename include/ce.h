@@ -128,7 +128,8 @@ typedef enum ce_op {
   CE_OP_TOP_TOKENS = 2,     /* ce_top_tokens */
   CE_OP_MASKED_LOGITS = 3,  /* ce_masked_logits */
   CE_OP_TOP_M = 4,          /* ce_top_m */
-  CE_OP_DRAFT_STEP = 5      /* ce_draft_step */
+  CE_OP_DRAFT_STEP = 5,     /* ce_draft_step */
+  CE_OP_TOP_M_LOG_SOFTMAX = 6  /* ce_top_m_log_softmax */
 } ce_op;
 
 typedef struct ce_head* ce_head_t;
@@ -286,6 +287,26 @@ ce_status ce_top_m(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t 
                    int32_t* tokens, float* logits, int32_t* topk_ids_or_null,
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ce_top_m with each candidate's log-probability under the softmax over the
+ * row's candidate set in place of its logit: the softmax a sampler takes
+ * over the forward's masked row (vLLM compare view, gemma4_mtp.py,
+ * Gemma4MTPMaskedEmbedder.forward: -inf outside the candidates, so those
+ * tokens get probability 0), normalised over all the row's candidates, not
+ * only the m returned.  With M the row's largest canonical logit and T the
+ * sum of exp(l_c - M) over every candidate but one holding M, in float64:
+ *   logprobs[b][i] = fp32((l_i - M) - log1p(T)),
+ * rounded once to nearest-even; the summation order of T is fixed by the
+ * library, so results repeat bit for bit, and they lie within one fp32
+ * step of the same formula evaluated exactly.  Tokens and their order are
+ * exactly ce_top_m's; padding is token -1 with log-probability -inf.
+ *   logprobs  DEVICE [B][m] fp32
+ *   ws        DEVICE workspace of ce_workspace_bytes(head, B, K,
+ *             CE_OP_TOP_M_LOG_SOFTMAX) (the same as for CE_OP_TOP_M)
+ * Other arguments and errors as ce_top_m. */
+ce_status ce_top_m_log_softmax(ce_head_t head, const void* h, int32_t B, int32_t K, int32_t m,
+                               int32_t* tokens, float* logprobs, int32_t* topk_ids_or_null,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Fused draft step around the head (the step after the head that fuses its
  * neighbours).  In the page's multi-token predictor (Gemma4MultiTokenPredictor
  * forward) the head scores the output of the final RMSNorm, and the next
@@ -334,8 +355,8 @@ ce_status ce_draft_step(ce_head_t head, const void* x, const void* norm_weight, 
  *                        (topk_ids, ws unused)
  *   CE_OP_TOP_TOKENS     h -> out = tokens [B]
  *   CE_OP_MASKED_LOGITS  h -> out = logits [B][V]
- * and ce_graph_capture_call every op, CE_OP_TOP_M and CE_OP_DRAFT_STEP
- * included.  Errors: as the captured call (checked before anything is
+ * and ce_graph_capture_call every op, CE_OP_TOP_M, CE_OP_TOP_M_LOG_SOFTMAX
+ * and CE_OP_DRAFT_STEP included.  Errors: as the captured call (checked before anything is
  * enqueued, so a failed call leaves no capture behind), plus UNSUPPORTED for
  * another op or the null stream, HIP for a capture failure. */
 ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B,
@@ -347,11 +368,12 @@ ce_status ce_graph_capture(ce_head_t head, int32_t op, const void* h, int32_t B,
  * has the meaning of the same argument of the op's own entry point; fields an
  * op does not take are ignored.
  *   op          ce_op
- *   in          h (SCORE, TOP_TOKENS, MASKED_LOGITS, TOP_M), the scores (TOPK)
- *               or the rows before the norm, x (DRAFT_STEP)
+ *   in          h (SCORE, TOP_TOKENS, MASKED_LOGITS, TOP_M, TOP_M_LOG_SOFTMAX),
+ *               the scores (TOPK) or the rows before the norm, x (DRAFT_STEP)
  *   out         scores (SCORE), topk ids (TOPK), tokens (TOP_TOKENS, TOP_M,
- *               DRAFT_STEP) or logits (MASKED_LOGITS)
- *   out_logits  the [B][m] logits of TOP_M
+ *               TOP_M_LOG_SOFTMAX, DRAFT_STEP) or logits (MASKED_LOGITS)
+ *   out_logits  the [B][m] logits of TOP_M, the log-probabilities of
+ *               TOP_M_LOG_SOFTMAX
  *   topk_ids    topk_ids_or_null of the fused ops
  *   norm_weight, eps, h_out, emb_table, emb_dim, normalizer, emb_out
  *               the DRAFT_STEP operands */

@@ -150,6 +150,10 @@ def test_create_ragged_and_sizes(lib):
         # clusters touch: 2 + 2 for K=2, of one 64-token tile's keys each)
         assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_M, ctypes.byref(n)) == 0
         assert n.value >= sizes[_ffi.CE_OP_MASKED_LOGITS] + 8 * 4 * 64 * 8
+        # the log-softmax form of top-m takes the same workspace
+        n2 = ctypes.c_size_t()
+        assert lib.ce_workspace_bytes(h, 8, 2, _ffi.CE_OP_TOP_M_LOG_SOFTMAX, ctypes.byref(n2)) == 0
+        assert n2.value == n.value
     finally:
         lib.ce_head_destroy(h)
 
@@ -163,6 +167,7 @@ def test_compute_calls_before_prepare_fail_on_host(lib):
         assert lib.ce_top_tokens(h, FAKE, 1, 2, FAKE, None, FAKE, 1 << 20, None) == NP
         assert lib.ce_masked_logits(h, FAKE, 1, 2, FAKE, None, FAKE, 1 << 20, None) == NP
         assert lib.ce_top_m(h, FAKE, 1, 2, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == NP
+        assert lib.ce_top_m_log_softmax(h, FAKE, 1, 2, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == NP
         assert lib.ce_score_centroids(h, FAKE, 1, FAKE, None) == NP
         assert lib.ce_topk(h, FAKE, 1, 2, FAKE, None) == NP
         assert "prepare" in lib.ce_last_error().decode()
@@ -184,6 +189,11 @@ def test_compute_calls_before_prepare_fail_on_host(lib):
         assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE, ctypes.byref(g)) == NP
         call.op = _ffi.CE_OP_DRAFT_STEP
         assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE, ctypes.byref(g)) == NP
+        call.op = _ffi.CE_OP_TOP_M_LOG_SOFTMAX
+        assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE, ctypes.byref(g)) == NP
+        call.op = _ffi.CE_OP_TOP_M_LOG_SOFTMAX + 1
+        assert lib.ce_graph_capture_call(h, ctypes.byref(call), FAKE,
+                                         ctypes.byref(g)) == ERR["CE_ERR_UNSUPPORTED"]
         assert not g.value
         assert lib.ce_graph_launch(None, None) == ERR["CE_ERR_NULL_POINTER"]
         assert lib.ce_graph_destroy(None) == 0
