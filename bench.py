@@ -9,7 +9,8 @@ captured HIP graph (the pages' sequencing; on ROCm a graph launch costs more
 host and device time than the four launches it replaces) and the device time
 per call with eight calls captured in one graph.  The line also carries every
 batch size of the sweep, the masked full-vocabulary output (forward), the
-fused top-m, the fused draft step and FP8 slabs at B in {1, 16, 64} (eager
+fused top-m (also with log-probabilities over the row's candidates), the
+fused draft step and FP8 slabs at B in {1, 16, 64} (eager
 calls; forward also as graph replays), the skewed head (Zipf clusters,
 correlated rows) at B=64, and the wide head with its dense comparison
 path.
@@ -696,22 +697,29 @@ def main() -> int:
     # ------------------------------------------------------------ fused top-m
     top_m = []
     if not args.no_top_m:
-        from centroid_masked_sparse_amd import OP_TOP_M
+        from centroid_masked_sparse_amd import OP_TOP_M, OP_TOP_M_LOG_SOFTMAX
         m = 8
-        for B in (1, 16, 64):
-            hs = groups(B)
+
+        def top_m_us(B, hs, op, fn):
             calls = []
             for s_ in range(len(hs)):
                 for head in heads:
                     tok = torch.empty((B, m), dtype=torch.int32, device=dev)
                     val = torch.empty((B, m), dtype=torch.float32, device=dev)
-                    ws = head._workspace(B, K, OP_TOP_M)
-                    calls.append((head._lib.ce_top_m,
+                    ws = head._workspace(B, K, op)
+                    calls.append((getattr(head._lib, fn),
                                   (head._handle, hs[s_].data_ptr(), B, K, m, tok.data_ptr(),
                                    val.data_ptr(), None, ws.data_ptr(), ws.numel(), stream),
                                   tok, val))
-            us = _time_calls(torch, calls, args.steps, args.warmup)
-            row = {"B": B, "m": m, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1)}
+            return _time_calls(torch, calls, args.steps, args.warmup)
+
+        for B in (1, 16, 64):
+            hs = groups(B)
+            us = top_m_us(B, hs, OP_TOP_M, "ce_top_m")
+            # the same with log-probabilities over the row's candidates
+            us_ls = top_m_us(B, hs, OP_TOP_M_LOG_SOFTMAX, "ce_top_m_log_softmax")
+            row = {"B": B, "m": m, "us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
+                   "log_softmax_us_per_call": round(us_ls, 3)}
             top_m.append(row)
             log(f"[bench] top_m: {row}")
 
