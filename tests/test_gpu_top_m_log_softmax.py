@@ -149,3 +149,32 @@ def test_repeats_and_graph_replays_are_bit_identical():
         assert torch.equal(out, t1), i
         assert torch.equal(lpo.view(torch.int32), l1.view(torch.int32)), i
     g.close()
+
+
+def test_empty_and_single_candidate_rows():
+    """A row whose selected clusters are all empty is padding only; a row
+    with one candidate gives it log-probability exactly 0."""
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import Head
+    d = 64
+    h = np.zeros((3, d), dtype=np.float32)
+    h[0, 0] = 1.0    # picks cluster 0 (empty) at K = 1
+    h[1, 1] = 1.0    # picks cluster 1 (one token)
+    h[2, 2] = 1.0    # picks clusters 2 and 3 at K = 2
+    C = np.zeros((4, d), dtype=np.float32)
+    C[0, 0] = C[1, 1] = 5.0
+    C[2, 2], C[3, 2] = 3.0, 2.0
+    E = np.random.default_rng(3).standard_normal((128, d)).astype(np.float32)
+    off = np.array([0, 0, 1, 101, 128], dtype=np.int32)   # clusters of 0, 1, 100, 27 tokens
+    tos = np.random.default_rng(4).permutation(128).astype(np.int32)
+    head = Head(torch.from_numpy(C).cuda(), torch.from_numpy(E).cuda(), tos, off, max_B=3, max_K=4)
+    hd = torch.from_numpy(h).cuda()
+    for K, m in ((1, 4), (2, 32)):
+        tok, lp = head.top_m(hd, m, K, log_softmax=True)
+        torch.cuda.synchronize()
+        tok_o, lp_o = oracle.top_m_log_softmax(h, C, E, off, tos, K, m, "f32")
+        _compare(tok, lp, tok_o, lp_o, (K, m))
+        if K == 1:
+            assert tok_o[0].tolist() == [-1] * m
+            assert tok_o[1, 0] >= 0 and tok_o[1, 1] == -1
+            assert lp.cpu().numpy()[1, 0] == 0.0
