@@ -3018,9 +3018,7 @@ static hipError_t launch_gather_t(const PassArgs& a, hipStream_t s) {
       // (slot-major grid, n_tiles a multiple of 8 on large heads).  Ragged
       // heads' correlated rows pile onto a few tiles: from 17 rows their
       // passes take two waves (skewed head, B=64: gather 24.0 -> 17.2 µs,
-      // call 40.3 -> 32.9; four waves the same; two row groups a pass, with
-      // one or two waves a tile, 25.3-25.6 against 16.6 µs: most of the
-      // ragged head's tiles carry one or two rows)
+      // call 40.3 -> 32.9; four waves the same)
       const long rows_per_tile = (long)a.B * a.K / a.Nc;
       const int rg = cert_row_groups(a);
       g.split_shift = rg > 1 ? 0
