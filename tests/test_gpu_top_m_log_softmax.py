@@ -178,3 +178,12 @@ def test_empty_and_single_candidate_rows():
             assert tok_o[0].tolist() == [-1] * m
             assert tok_o[1, 0] >= 0 and tok_o[1, 1] == -1
             assert lp.cpu().numpy()[1, 0] == 0.0
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_matrix_core_projection(ragged):
+    """The MFMA projection with the certified top-K selects the same
+    centroids, so tokens and log-probabilities are those of the float64
+    projection."""
+    w = make_random(151, d=128, V=8192, Nc=64, dtype="bf16", rows=64, ragged=ragged)
+    _check(make_head(w, max_B=24, projection="mfma"), w, 24, 4, 8)
