@@ -2940,9 +2940,9 @@ static int gather_split_shift_ragged(int B) { return B >= 16 ? kRaggedSplitShift
 // per row, which the batches below the split (48 rows) afford: sweep head,
 // µs per call, B=8 19.8 → 16.6, B=16 22.0 → 19.0, B=32 27.3 → 24.1 (forward
 // B=16 24.2 → 21.0, top-m B=16 26.7 → 23.0).  At B=64 the repeats cost more
-// than the idle waves (33.2 → 36.7), except for FP8 slabs, whose argmax is
-// bound by its conversions rather than its bytes and runs by row at every
-// batch (B=64 27.8 → 26.0).  (On earlier kernels the limit measured best at
+// than the idle waves (33.2 → 36.7), except for FP8 slabs, whose argmax
+// runs by row at every batch (B=64 27.8 → 26.0): with half the bytes a
+// tile, the repeats cost less than the tile grid's uneven spread.  (On earlier kernels the limit measured best at
 // 4 rows.)  Beyond 4 rows by row needs about one row per selected tile
 // (B K <= 2 Nc, as on the sweep head, where it is 0.5 to 1): where rows
 // share most tiles (K near Nc) every repeat is a slab read.
