@@ -49,8 +49,8 @@ METRIC = "sparse-head draft rows/sec at B=1..64 + achieved HBM GB/s vs peak (1 M
 # write x1.00); see profiles/gather_kernel_sweep_B64.md.  Valid only for the
 # kernel source it was measured on: any other source reports null.
 TRAFFIC_RECORD = {
-    "kernels_sha256_prefix": "e1e7b69cbfc72d00",
-    "fetch_kib": 41439.9, "fetch_scale": 2.00, "write_kib": 128, "write_scale": 1.00,
+    "kernels_sha256_prefix": "0ce68a787527410b",
+    "fetch_kib": 41437.8, "fetch_scale": 2.00, "write_kib": 128, "write_scale": 1.00,
 }
 
 
