@@ -187,3 +187,32 @@ def test_matrix_core_projection(ragged):
     projection."""
     w = make_random(151, d=128, V=8192, Nc=64, dtype="bf16", rows=64, ragged=ragged)
     _check(make_head(w, max_B=24, projection="mfma"), w, 24, 4, 8)
+
+
+def test_closed_form_on_integer_logits():
+    """One-hot rows and embeddings whose first element is 0, 1, 2 or 3 give
+    exact integer logits: the row's 64 candidates hold each value 16 times,
+    so log p(l) = l - log(16 (1 + e + e^2 + e^3)), and the m best are the
+    lowest-id tokens of logit 3 (ties by token id)."""
+    import math
+    torch = torch_mod()
+    from centroid_masked_sparse_amd import Head
+    d, V = 64, 128
+    C = np.zeros((2, d), dtype=np.float32)
+    C[0, 0], C[1, 0] = 1.0, -1.0            # the row selects cluster 0 at K = 1
+    E = np.zeros((V, d), dtype=np.float32)
+    E[:64, 0] = np.arange(64) % 4           # cluster 0: logits 0, 1, 2, 3, ...
+    E[64:, 0] = 5.0
+    tos = np.random.default_rng(8).permutation(V).astype(np.int32)
+    h = np.zeros((2, d), dtype=np.float32)
+    h[:, 0] = 1.0
+    head = Head(torch.from_numpy(C).cuda(), torch.from_numpy(E).cuda(), tos, max_B=2, max_K=2)
+    m = 8
+    tok, lp = head.top_m(torch.from_numpy(h).cuda(), m, 1, log_softmax=True)
+    torch.cuda.synchronize()
+    lse = math.log(16.0 * (1.0 + math.e + math.e ** 2 + math.e ** 3))
+    want_tok = sorted(int(tos[j]) for j in range(64) if j % 4 == 3)[:m]
+    for b in range(2):
+        assert tok.cpu().numpy()[b].tolist() == want_tok
+        got = lp.cpu().numpy()[b]
+        assert np.all(_ulps(got, np.full(m, np.float32(3.0 - lse))) <= 1), got
