@@ -87,6 +87,11 @@ class Head:
     None for equal clusters.  ``max_B``/``max_K`` bound later calls.
     ``slabs="fp8"`` stores the embedding slabs as OCP E4M3 codes with a
     float32 scale per row (bf16 heads only; logits change accordingly).
+
+    Calls run on torch's current stream and share one cached workspace per
+    op, so calls of the same op issued on different streams at once would
+    overwrite each other's scratch: keep one head per stream, or pass each
+    stream's own workspace through the C ABI (``new_workspace``).
     """
 
     _PROJ = {"auto": _ffi.CE_PROJ_AUTO, "exact": _ffi.CE_PROJ_EXACT, "mfma": _ffi.CE_PROJ_MFMA}
