@@ -216,3 +216,21 @@ def test_closed_form_on_integer_logits():
         assert tok.cpu().numpy()[b].tolist() == want_tok
         got = lp.cpu().numpy()[b]
         assert np.all(_ulps(got, np.full(m, np.float32(3.0 - lse))) <= 1), got
+
+
+def test_every_token_a_candidate_is_the_dense_log_softmax():
+    """K = Nc: every token is a candidate, so the log-probabilities are the
+    full-vocabulary log-softmax of the dense logits."""
+    torch = torch_mod()
+    w = make_workload("tiny")
+    B, K, m = 3, w.Nc, 32
+    head = make_head(w, max_B=4)
+    hb = rows(w, B)
+    tok, lp = head.top_m(to_device(hb, w.dtype), m, K, log_softmax=True)
+    torch.cuda.synchronize()
+    dense = oracle.dense_logits(hb, w.E, w.tos, w.dtype)
+    tok_o, lp_o = oracle.top_m_log_softmax(hb, w.C, w.E, w.offsets, w.tos, K, m, w.dtype)
+    _compare(tok, lp, tok_o, lp_o, "K=Nc")
+    for b in range(B):
+        full = oracle.log_softmax_candidates(dense[b])
+        assert np.all(_ulps(lp.cpu().numpy()[b], full[tok_o[b]]) <= 1)
